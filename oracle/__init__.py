@@ -1,0 +1,210 @@
+"""CPU oracle for paged causal GQA attention: test infrastructure only.
+
+Only the test suite, the smoke check and the benchmark's ``cpu_baseline`` leg
+may import this package.  The product path (``paged_kv_cache_amd``) never
+does, and shares no code with it.
+
+``oracle.c`` holds the arithmetic (fp64 plain definition of attention and the
+page scatter); this module compiles it with gcc and marshals numpy arrays to
+it.  Inputs are bf16 bit patterns (numpy uint16, or bf16 torch CPU tensors,
+which are viewed, not rounded).
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_I = ctypes.c_int
+_D = ctypes.c_double
+
+
+def build(force: bool = True) -> str:
+    """Compile oracle.c into liboracle.so (portable flags: the .so may run on another host)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp"
+        subprocess.run(["gcc", "-std=c11", "-O2", "-fopenmp", "-fPIC", "-shared", "-Wall",
+                        "-Werror", _SRC, "-o", tmp, "-lm"], check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def load(lib_path: str | None = None):
+    """Load the compiled oracle (building it first if it is missing or stale)."""
+    global _lib
+    if lib_path is not None:
+        return _bind(ctypes.CDLL(lib_path))
+    if _lib is None:
+        override = os.environ.get("ORACLE_LIB")      # a planted-mistake build (mutation tests)
+        if override:
+            _lib = _bind(ctypes.CDLL(override))
+            return _lib
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build(force=True)
+        _lib = _bind(ctypes.CDLL(_LIB))
+    return _lib
+
+
+def _bind(lib):
+    lib.oracle_num_threads.restype = _I
+    lib.oracle_set_num_threads.argtypes = [_I]
+    lib.oracle_page_bytes.restype = _I64
+    lib.oracle_page_bytes.argtypes = [_I, _I]
+    lib.oracle_kv_scatter.restype = _I64
+    lib.oracle_kv_scatter.argtypes = [_P, _I64, _P, _P, _I64, _P, _P, _P, _I, _I, _I, _I, _I, _I]
+    lib.oracle_attn_prefill.restype = _I64
+    lib.oracle_attn_prefill.argtypes = [_P, _P, _I64, _P, _I, _I, _I, _I, _P, _P,
+                                        _I, _I, _I, _I, _I, _D, _I, _P, _I64, _P, _P]
+    lib.oracle_attn_decode.restype = _I64
+    lib.oracle_attn_decode.argtypes = [_P, _P, _I64, _P, _I, _I, _I, _I, _P, _P,
+                                       _I, _I, _I, _I, _D, _P, _P]
+    lib.oracle_attn_dense.restype = None
+    lib.oracle_attn_dense.argtypes = [_P, _P, _P, _I, _I, _I, _I, _I, _D, _I, _P, _I64, _P, _P]
+    return lib
+
+
+def _bits(x) -> np.ndarray:
+    """uint16 bit patterns of a bf16 torch tensor or a uint16 numpy array (contiguous)."""
+    if isinstance(x, np.ndarray):
+        assert x.dtype == np.uint16
+        return np.ascontiguousarray(x)
+    import torch
+    assert x.dtype == torch.bfloat16
+    return np.ascontiguousarray(x.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16))
+
+
+def _i32(x) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(x, dtype=np.int32))
+
+
+def _ptr(a: np.ndarray | None):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def num_threads() -> int:
+    return int(load().oracle_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    load().oracle_set_num_threads(int(n))
+
+
+def page_bytes(n_kv_heads: int, head_dim: int) -> int:
+    return int(load().oracle_page_bytes(n_kv_heads, head_dim))
+
+
+def new_pool(n_pages: int, n_kv_heads: int, head_dim: int, fill: int) -> np.ndarray:
+    """A host pool (uint8 bytes) whose every bf16 slot holds the bit pattern ``fill``."""
+    words = n_pages * page_bytes(n_kv_heads, head_dim) // 2
+    return np.full(words, fill, dtype=np.uint16).view(np.uint8)
+
+
+def kv_scatter(pool: np.ndarray, n_pages: int, k, v, slot_ids, positions, block_table,
+               layer: int, n_kv_heads: int, head_dim: int) -> int:
+    """Write token K/V rows into ``pool`` in place; returns the count of skipped tokens."""
+    kb, vb = _bits(k), _bits(v)
+    n = kb.size // (n_kv_heads * head_dim)
+    bt = _i32(block_table)
+    assert bt.ndim == 3 and pool.dtype == np.uint8 and pool.flags.c_contiguous
+    return int(load().oracle_kv_scatter(
+        _ptr(pool), n_pages, _ptr(kb), _ptr(vb), n, _ptr(_i32(slot_ids)), _ptr(_i32(positions)),
+        _ptr(bt), bt.shape[0], bt.shape[1], bt.shape[2], layer, n_kv_heads, head_dim))
+
+
+def attn_prefill(q, pool: np.ndarray, n_pages: int, block_table, layer: int, slot_ids, seq_lens,
+                 Hkv: int, scale: float, causal: bool, rows=None):
+    """Paged prefill rows. Returns (O [n_rows,Hq,d] f64, LSE [n_rows,Hq] f64, bad_lookups)."""
+    qb = _bits(q)
+    B, T, Hq, d = q.shape
+    bt = _i32(block_table)
+    rws = None if rows is None else _i32(rows).reshape(-1, 2)
+    n_rows = B * T if rws is None else rws.shape[0]
+    O = np.empty((n_rows, Hq, d), np.float64)
+    L = np.empty((n_rows, Hq), np.float64)
+    bad = load().oracle_attn_prefill(
+        _ptr(qb), _ptr(pool), n_pages, _ptr(bt), bt.shape[0], bt.shape[1], bt.shape[2], layer,
+        _ptr(None if slot_ids is None else _i32(slot_ids)), _ptr(_i32(seq_lens)),
+        B, T, Hq, Hkv, d, float(scale), int(bool(causal)), _ptr(rws), n_rows, _ptr(O), _ptr(L))
+    return O, L, int(bad)
+
+
+def attn_decode(q, pool: np.ndarray, n_pages: int, block_table, layer: int, slot_ids, ctx_lens,
+                Hkv: int, scale: float):
+    """Paged decode. Returns (O [B,Hq,d] f64, LSE [B,Hq] f64, bad_lookups)."""
+    qb = _bits(q)
+    B, Hq, d = q.shape
+    bt = _i32(block_table)
+    O = np.empty((B, Hq, d), np.float64)
+    L = np.empty((B, Hq), np.float64)
+    bad = load().oracle_attn_decode(
+        _ptr(qb), _ptr(pool), n_pages, _ptr(bt), bt.shape[0], bt.shape[1], bt.shape[2], layer,
+        _ptr(None if slot_ids is None else _i32(slot_ids)), _ptr(_i32(ctx_lens)),
+        B, Hq, Hkv, d, float(scale), _ptr(O), _ptr(L))
+    return O, L, int(bad)
+
+
+def attn_dense(q, k, v, scale: float, causal: bool, rows=None):
+    """Contiguous attention rows. Returns (O [n_rows,Hq,d] f64, LSE [n_rows,Hq] f64)."""
+    qb, kb, vb = _bits(q), _bits(k), _bits(v)
+    B, T, Hq, d = q.shape
+    Hkv = k.shape[2]
+    rws = None if rows is None else _i32(rows).reshape(-1, 2)
+    n_rows = B * T if rws is None else rws.shape[0]
+    O = np.empty((n_rows, Hq, d), np.float64)
+    L = np.empty((n_rows, Hq), np.float64)
+    load().oracle_attn_dense(_ptr(qb), _ptr(kb), _ptr(vb), B, T, Hq, Hkv, d, float(scale),
+                             int(bool(causal)), _ptr(rws), n_rows, _ptr(O), _ptr(L))
+    return O, L
+
+
+# Convenience wrappers over the seeded cases (duck-typed: any object with the
+# same attribute names works).
+
+def pool_for(case) -> np.ndarray:
+    c = case.cache
+    return new_pool(c.n_pages, c.n_kv_heads, c.head_dim, c.page_fill)
+
+
+def scatter_tokens(pool: np.ndarray, cache, tokens) -> int:
+    return kv_scatter(pool, cache.n_pages, tokens.k, tokens.v, tokens.slot_ids, tokens.positions,
+                      cache.block_table, cache.layer, cache.n_kv_heads, cache.head_dim)
+
+
+def prefill_case(case, rows=None, pool: np.ndarray | None = None):
+    """Scatter the prompt into a fresh pool, then evaluate prefill rows; returns (O, LSE, pool)."""
+    if pool is None:
+        pool = pool_for(case)
+        bad = scatter_tokens(pool, case.cache, case.tokens)
+        assert bad == 0
+    c = case.cache
+    O, L, bad = attn_prefill(case.q, pool, c.n_pages, c.block_table, c.layer, case.slot_ids,
+                             case.seq_lens, c.n_kv_heads, case.scale, case.causal, rows)
+    assert bad == 0
+    return O, L, pool
+
+
+def decode_case(case, pool: np.ndarray | None = None):
+    """Scatter context and newest tokens into a fresh pool, then decode; returns (O, LSE, pool)."""
+    if pool is None:
+        pool = pool_for(case)
+        assert scatter_tokens(pool, case.cache, case.context) == 0
+        assert scatter_tokens(pool, case.cache, case.new_tokens) == 0
+    c = case.cache
+    O, L, bad = attn_decode(case.q, pool, c.n_pages, c.block_table, c.layer, case.slot_ids,
+                            case.ctx_lens, c.n_kv_heads, case.scale)
+    assert bad == 0
+    return O, L, pool
+
+
+def dense_case(case, rows=None):
+    return attn_dense(case.q, case.k, case.v, case.scale, case.causal, rows)

@@ -1,0 +1,103 @@
+"""Planted mistakes in copies of the oracle must each fail at least one pin.
+
+Each mutant is a plausible slip in ``oracle/oracle.c`` (a dropped term, a
+wrong sign, a wrong index or stride, a transposed operand).  The copy is
+compiled on the CPU into a temporary library and the pins of
+``test_oracle.py`` run against it in a child process (a mutant may read out of
+bounds and crash, which also counts as caught).  The real oracle is never
+modified.
+"""
+
+import os
+import subprocess
+import sys
+import textwrap
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "oracle.c")
+
+MUTANTS = [
+    ("drop_scale", "scores[j] = scale * dot;", "scores[j] = dot;"),
+    ("exp_sign", "double w = exp(scores[j] - m);", "double w = exp(m - scores[j]);"),
+    ("lse_without_max", "*lse = m + log(l);", "*lse = log(l);"),
+    ("no_final_divide", "out[c] /= l;", "out[c] /= 1.0;"),
+    ("max_reversed", "if (scores[j] > m)", "if (scores[j] < m && scores[j] > -INFINITY)"),
+    ("causal_off_by_one", "(causal ? (int64_t)t + 1 : len)", "(causal ? (int64_t)t : len)"),
+    ("causal_ignored", "(causal ? (int64_t)t + 1 : len)", "(len)"),
+    ("gqa_interleaved", "int kvh = h / g;", "int kvh = h % Hkv;"),
+    ("v_offset_dropped", "vrow[j] = (const uint16_t *)(pool + off + v_offset_bytes(&s));",
+     "vrow[j] = (const uint16_t *)(pool + off);"),
+    ("k_as_v_operand", "dot += qd[c] * bf16_to_double(krow[j][c]);",
+     "dot += qd[c] * bf16_to_double(vrow[j][c]);"),
+    ("layer_stride", "(int64_t)s->layer * s->mbps", "(int64_t)s->layer * s->n_layers"),
+    ("slot_stride", "(int64_t)slot * s->n_layers * s->mbps", "(int64_t)slot * s->mbps"),
+    ("token_in_page", "(p % ORACLE_PAGE_TOKENS) * row", "(p / ORACLE_PAGE_TOKENS) * row"),
+    ("head_stride", "(int64_t)h * s->head_dim * 2;", "(int64_t)h * 2;"),
+    ("decode_drops_newest", "ctx_lens[b] > 0 ? ctx_lens[b] : 0", "ctx_lens[b] > 0 ? ctx_lens[b] - 1 : 0"),
+    ("v_offset_half", "return (int64_t)ORACLE_PAGE_TOKENS * s->n_kv_heads * s->head_dim * 2;",
+     "return (int64_t)ORACLE_PAGE_TOKENS * s->n_kv_heads * s->head_dim;"),
+    ("q_row_stride", "q + (((int64_t)b * T + t) * Hq + h) * d;", "q + (((int64_t)t * B + b) * Hq + h) * d;"),
+    ("bf16_widen", "uint32_t u = (uint32_t)bits << 16;", "uint32_t u = (uint32_t)bits << 15;"),
+]
+
+RUNNER = textwrap.dedent("""
+    import sys, traceback
+    sys.path.insert(0, {root!r}); sys.path.insert(0, {tests!r})
+    import oracle, test_oracle as T
+    import inspect
+    failed = []
+    pins = [
+        (T.test_worked_example_matches_printed_numbers, {{}}),
+        (T.test_worked_example_block_one_is_causal_row_one, {{}}),
+        (T.test_stress_tied_row_is_uniform, {{}}),
+        (T.test_zero_query_gives_causal_running_mean, {{}}),
+        (T.test_zero_query_decode_is_context_mean, {{}}),
+        (T.test_gqa_uses_consecutive_groups, {{}}),
+        (T.test_prefill_matches_brute_force, dict(Hq=32, Hkv=8, causal=True)),
+        (T.test_dense_matches_brute_force, dict(d=64, H=4, causal=True)),
+        (T.test_decode_matches_brute_force, {{}}),
+        (T.test_scatter_places_rows_at_page_addresses, dict(Hkv=8, d=64)),
+        (T.test_page_geometry_matches_printed_constants, {{}}),
+    ]
+    for fn, kw in pins:
+        try:
+            fn(oracle, **kw)
+        except Exception:
+            failed.append(fn.__name__)
+    print("FAILED_PINS", len(failed), " ".join(failed))
+""")
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_planted_mistake_is_caught(tmp_path, name, old, new):
+    src = open(SRC).read()
+    assert src.count(old) >= 1, f"mutation site for {name} not found"
+    mutant = tmp_path / "oracle_mutant.c"
+    mutant.write_text(src.replace(old, new))
+    lib = tmp_path / "liboracle_mutant.so"
+    subprocess.run(["gcc", "-std=c11", "-O1", "-fopenmp", "-fPIC", "-shared", str(mutant), "-o",
+                    str(lib), "-lm"], check=True)
+    env = dict(os.environ, ORACLE_LIB=str(lib), OMP_NUM_THREADS="2")
+    script = RUNNER.format(root=ROOT, tests=os.path.join(ROOT, "tests"))
+    r = subprocess.run([sys.executable, "-c", script], env=env, capture_output=True, text=True,
+                       timeout=300)
+    if r.returncode != 0:        # crashed on a wild read: caught
+        return
+    line = [x for x in r.stdout.splitlines() if x.startswith("FAILED_PINS")][-1]
+    assert int(line.split()[1]) > 0, f"mutant {name} passed every pin:\n{r.stdout}\n{r.stderr}"
+
+
+def test_unmutated_copy_passes_every_pin(tmp_path):
+    """Control: the same runner on an unmodified copy reports no failing pin."""
+    lib = tmp_path / "liboracle_copy.so"
+    subprocess.run(["gcc", "-std=c11", "-O1", "-fopenmp", "-fPIC", "-shared", SRC, "-o", str(lib),
+                    "-lm"], check=True)
+    env = dict(os.environ, ORACLE_LIB=str(lib), OMP_NUM_THREADS="2")
+    script = RUNNER.format(root=ROOT, tests=os.path.join(ROOT, "tests"))
+    r = subprocess.run([sys.executable, "-c", script], env=env, capture_output=True, text=True,
+                       timeout=300)
+    assert r.returncode == 0, r.stderr
+    line = [x for x in r.stdout.splitlines() if x.startswith("FAILED_PINS")][-1]
+    assert int(line.split()[1]) == 0, r.stdout
