@@ -1,0 +1,179 @@
+/*
+ * pagedattn.h -- C ABI of the MI355X (gfx950) paged causal GQA attention library
+ * (libpagedattn.so).
+ *
+ * Three calls make up the path: kv_scatter writes new K/V rows into 16-token
+ * pages, attn_prefill runs exact causal attention of a whole prompt over those
+ * pages, attn_decode runs exact attention of one new query per sequence over
+ * its cached context.  attn_prefill_dense is the same prefill over contiguous
+ * (unpaged) K/V.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - Every tensor pointer is a DEVICE pointer that the caller allocated and
+ *   owns.  The library never allocates, frees or keeps a pointer after return.
+ *   Tensor pointers must be 16-byte aligned.
+ * - bf16 is IEEE bfloat16 stored as 2 bytes; fp32 is IEEE binary32.
+ * - `stream` is a hipStream_t (NULL = the null stream).  Calls enqueue work on
+ *   it and return without waiting; outputs are ready when the stream is.
+ * - Return value: PA_OK (0) after a successful enqueue, or a negative
+ *   pa_status for an argument the host can check (NULL pointer, bad size,
+ *   unsupported head_dim/group, misalignment, small workspace, launch failure).
+ *   On a negative return nothing was enqueued.
+ * - `err` (nullable, device int32): problems only the device can see (a
+ *   block-table entry needed for a visible token that is -1 or >= n_pages, a
+ *   slot id outside [0, n_slots), a position or length beyond what the table
+ *   or the query tensor can hold) are OR-ed into *err as PA_DEVERR_* bits.
+ *   The offending token is then left out (never dereferenced), exactly as if it
+ *   were masked.  The caller clears *err beforehand.
+ *
+ * Paged KV layout (page "6. Splitting the KV cache into 16-token blocks",
+ * tiny-vllm part 6, sections "Block contents: K in front, V after V_OFFSET"
+ * and "block table")
+ * ----------------------------------------------------------------------
+ * - kv_cache is one buffer of n_pages physical pages.  A page holds 16 tokens:
+ *   K as [token 16][kv_head n_kv_heads][dim head_dim] bf16, then V in the same
+ *   order starting V_OFFSET = 16*n_kv_heads*head_dim*2 bytes into the page.
+ *   Page bytes = 2*V_OFFSET (32768 for 8 KV heads x 64).
+ * - block_table is int32 [n_slots][n_layers][max_blocks_per_seq]: the physical
+ *   page of logical block p/16 of sequence slot s in layer l sits at index
+ *   s*n_layers*max_blocks_per_seq + l*max_blocks_per_seq + p/16; -1 = none.
+ * - So K[p][h][i] of (s, l) is at byte
+ *   page*page_bytes + (p%16)*n_kv_heads*head_dim*2 + h*head_dim*2 + i*2,
+ *   and V at the same byte + V_OFFSET.
+ * - GQA: q head h reads kv head h / (Hq / Hkv) (consecutive groups; page
+ *   "3. The prefill path", section "Per-head attention scores and GQA").
+ *
+ * Results (exact attention, FlashAttention-2 explainer "Step by step (the two
+ * forward tweaks)"): O = softmax(scale * q K^T) V over the visible keys, and
+ * LSE = m + ln(l), the natural-log log-sum-exp of the scaled scores.  A query
+ * with no visible key gets O = 0 and LSE = -INFINITY.
+ */
+#ifndef PAGEDATTN_H
+#define PAGEDATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pa_status {
+    PA_OK = 0,
+    PA_ERR_NULL = -1,        /* a required pointer is NULL                          */
+    PA_ERR_SHAPE = -2,       /* a size is negative/zero or sizes disagree            */
+    PA_ERR_UNSUPPORTED = -3, /* no kernel for this head_dim / group size            */
+    PA_ERR_ALIGN = -4,       /* a tensor pointer is not 16-byte aligned              */
+    PA_ERR_WORKSPACE = -5,   /* decode workspace smaller than the size it needs      */
+    PA_ERR_RANGE = -6,       /* an index or byte offset would overflow its type      */
+    PA_ERR_LAUNCH = -7       /* the HIP runtime refused the launch                   */
+} pa_status;
+
+/* Bits OR-ed into the optional device flag `err`. */
+#define PA_DEVERR_BAD_PAGE 1 /* needed block-table entry is -1 or >= n_pages         */
+#define PA_DEVERR_BAD_SLOT 2 /* slot id outside [0, n_slots)                          */
+#define PA_DEVERR_BAD_POS 4  /* position/length outside the table (mbps*16) or T     */
+
+/* Human-readable name of a pa_status value (static string, never NULL). */
+const char *pa_status_string(int status);
+
+/* Bytes of one physical page: 2 * 16 * n_kv_heads * head_dim * 2. */
+int64_t pa_page_bytes(int n_kv_heads, int head_dim);
+
+/*
+ * kv_scatter -- write the K and V rows of n_tokens tokens into their pages
+ * (page "3. The prefill path", section "Distributing K/V into paged blocks";
+ * the decode append of page 6, section "Block contents").
+ *
+ *   k, v         [n_tokens][n_kv_heads][head_dim] bf16, read only.
+ *   slot_ids     [n_tokens] int32: block-table slot of each token.
+ *   positions    [n_tokens] int32: position of each token in its sequence.
+ *   kv_cache     pool of n_pages pages (layout above), written in place: only
+ *                the 2*n_kv_heads*head_dim*2 bytes of each token's two rows
+ *                change; every other byte is left as it was.
+ *   block_table  [n_slots][n_layers][max_blocks_per_seq] int32, read only;
+ *                `layer` selects the layer.
+ *   Pages are never allocated here: the entry for each token must already
+ *   hold its page (the caller's free-list does the allocation).
+ *   Two tokens naming the same (slot, position) race; the result is one of
+ *   the two rows.  n_tokens == 0 is a no-op.  head_dim*n_kv_heads must be a
+ *   multiple of 8.
+ */
+int kv_scatter(const void *k, const void *v, int64_t n_tokens, const int32_t *slot_ids,
+               const int32_t *positions, void *kv_cache, int64_t n_pages,
+               const int32_t *block_table, int n_slots, int n_layers, int max_blocks_per_seq,
+               int layer, int n_kv_heads, int head_dim, int32_t *err, void *stream);
+
+/*
+ * attn_prefill -- causal (or full) grouped-query attention of a batch of
+ * prompts over the paged cache (page "3. The prefill path", sections
+ * "Per-head attention scores and GQA" and "causalMask and online softmax";
+ * FlashAttention-2 explainer, sections "Step by step", "Parallelise along the
+ * sequence length" and "Work partitioning between warps").
+ *
+ *   q            [B][T][Hq][head_dim] bf16; row t of sequence b is the query
+ *                of the token at position t.
+ *   kv_cache, block_table, n_pages, n_slots, n_layers, max_blocks_per_seq,
+ *   layer        the paged cache, as for kv_scatter (read only).  The prompt's
+ *                K/V must already be in it (kv_scatter first).
+ *   slot_ids     [B] int32 block-table slot of each sequence (NULL: slot b).
+ *   seq_lens     [B] int32, 0 <= seq_lens[b] <= T: the prompt length.
+ *   causal       nonzero: query t sees keys 0..t; zero: keys 0..seq_len-1.
+ *   scale        multiplies q.k (pass 1/sqrt(head_dim) for the usual scaling).
+ *   O            [B][T][Hq][head_dim] bf16 output.
+ *   LSE          [B][Hq][T] fp32 output (natural log, scaled scores).
+ *   Rows t >= seq_lens[b] are written as O = 0, LSE = -INFINITY.
+ *   Supported: head_dim 64 or 128, Hq/Hkv in {1, 2, 4, 8}.
+ */
+int attn_prefill(const void *q, const void *kv_cache, int64_t n_pages, const int32_t *block_table,
+                 int n_slots, int n_layers, int max_blocks_per_seq, int layer,
+                 const int32_t *slot_ids, const int32_t *seq_lens, int B, int T, int Hq, int Hkv,
+                 int head_dim, float scale, int causal, void *O, float *LSE, int32_t *err,
+                 void *stream);
+
+/*
+ * attn_decode -- attention of one new query per sequence over its whole cached
+ * context, the newest token included (page 6, sections "pagedAttentionKernel"
+ * and "logical block -> physical block -> byte address").  Long contexts are
+ * split across workgroups and merged with the log-sum-exp rule of the online
+ * softmax (page 3, "causalMask and online softmax": two partial results are
+ * rescaled to the larger maximum and added).
+ *
+ *   q            [B][Hq][head_dim] bf16, the query of the token at ctx_len-1.
+ *   ctx_lens     [B] int32, tokens cached for each sequence including the
+ *                newest; 0 gives O = 0, LSE = -INFINITY.
+ *   max_ctx      host upper bound on every ctx_lens[b] (sizes the split grid);
+ *                a larger ctx_lens[b] sets PA_DEVERR_BAD_POS and is cut to max_ctx.
+ *   workspace    device scratch of at least attn_decode_workspace_size(B, Hq,
+ *                head_dim, max_ctx) bytes, 16-byte aligned; contents on entry
+ *                do not matter; two calls in flight must not share it.
+ *   O            [B][Hq][head_dim] bf16 output;  LSE [B][Hq] fp32 output.
+ *   Other arguments as for attn_prefill.  Supported: head_dim 64 or 128,
+ *   Hq/Hkv in {1, 2, 4, 8, 16}.
+ */
+int attn_decode(const void *q, const void *kv_cache, int64_t n_pages, const int32_t *block_table,
+                int n_slots, int n_layers, int max_blocks_per_seq, int layer,
+                const int32_t *slot_ids, const int32_t *ctx_lens, int B, int Hq, int Hkv,
+                int head_dim, float scale, int max_ctx, void *workspace, size_t workspace_bytes,
+                void *O, float *LSE, int32_t *err, void *stream);
+
+/* Workspace bytes attn_decode needs for this batch shape (0 on bad sizes). */
+size_t attn_decode_workspace_size(int B, int Hq, int head_dim, int max_ctx);
+
+/*
+ * attn_prefill_dense -- the prefill on contiguous K/V (FlashAttention-2
+ * explainer, section "Results": the attention-only benchmark shapes).
+ *
+ *   q            [B][T][Hq][head_dim] bf16;  k, v [B][T][Hkv][head_dim] bf16.
+ *   O            [B][T][Hq][head_dim] bf16;  LSE [B][Hq][T] fp32.
+ *   causal, scale as for attn_prefill; every sequence has length T.
+ */
+int attn_prefill_dense(const void *q, const void *k, const void *v, int B, int T, int Hq, int Hkv,
+                       int head_dim, float scale, int causal, void *O, float *LSE, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDATTN_H */

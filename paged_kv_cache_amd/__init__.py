@@ -1,0 +1,183 @@
+"""Python binding of libpagedattn.so (MI355X / gfx950 paged causal GQA attention).
+
+Argument marshalling only: every step of the path runs in the library's HIP
+kernels, launched on torch's current stream.  PyTorch supplies device memory
+and streams.  The names and argument meanings follow ``include/pagedattn.h``.
+
+The library is built in-tree by ``python -m paged_kv_cache_amd.build``; if it
+is missing, importing the functions below raises -- there is no fallback.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpagedattn.so")
+_lib = None
+
+PA_DEVERR_BAD_PAGE = 1
+PA_DEVERR_BAD_SLOT = 2
+PA_DEVERR_BAD_POS = 4
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_I64 = ctypes.c_int64
+_F = ctypes.c_float
+_SZ = ctypes.c_size_t
+
+
+class PagedAttnError(RuntimeError):
+    """A pagedattn call returned a negative status."""
+
+
+def load():
+    """Load libpagedattn.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with `python -m paged_kv_cache_amd.build`")
+        lib = ctypes.CDLL(LIB_PATH)
+        lib.pa_status_string.restype = ctypes.c_char_p
+        lib.pa_status_string.argtypes = [_I]
+        lib.pa_page_bytes.restype = _I64
+        lib.pa_page_bytes.argtypes = [_I, _I]
+        lib.kv_scatter.restype = _I
+        lib.kv_scatter.argtypes = [_P, _P, _I64, _P, _P, _P, _I64, _P, _I, _I, _I, _I, _I, _I, _P, _P]
+        lib.attn_prefill.restype = _I
+        lib.attn_prefill.argtypes = [_P, _P, _I64, _P, _I, _I, _I, _I, _P, _P, _I, _I, _I, _I, _I,
+                                     _F, _I, _P, _P, _P, _P]
+        lib.attn_decode.restype = _I
+        lib.attn_decode.argtypes = [_P, _P, _I64, _P, _I, _I, _I, _I, _P, _P, _I, _I, _I, _I, _F,
+                                    _I, _P, _SZ, _P, _P, _P, _P]
+        lib.attn_decode_workspace_size.restype = _SZ
+        lib.attn_decode_workspace_size.argtypes = [_I, _I, _I, _I]
+        lib.attn_prefill_dense.restype = _I
+        lib.attn_prefill_dense.argtypes = [_P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P, _P, _P]
+        _lib = lib
+    return _lib
+
+
+def _check(rc: int, what: str) -> None:
+    if rc != 0:
+        raise PagedAttnError(f"{what}: {load().pa_status_string(rc).decode()} (status {rc})")
+
+
+def _dev(t: torch.Tensor | None, dtype: torch.dtype | None = None, name: str = "tensor"):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def page_bytes(n_kv_heads: int, head_dim: int) -> int:
+    return int(load().pa_page_bytes(n_kv_heads, head_dim))
+
+
+def _n_pages(kv_cache: torch.Tensor, n_kv_heads: int, head_dim: int) -> int:
+    pb = page_bytes(n_kv_heads, head_dim)
+    nbytes = kv_cache.numel() * kv_cache.element_size()
+    if nbytes % pb:
+        raise ValueError("kv_cache size is not a whole number of pages")
+    return nbytes // pb
+
+
+def kv_scatter(k: torch.Tensor, v: torch.Tensor, slot_ids: torch.Tensor, positions: torch.Tensor,
+               kv_cache: torch.Tensor, block_table: torch.Tensor, layer: int,
+               err: torch.Tensor | None = None, stream=None) -> None:
+    """Write token rows k, v [N, Hkv, d] (bf16) into their pages of kv_cache."""
+    N, Hkv, d = k.shape
+    assert v.shape == k.shape and block_table.dim() == 3
+    n_slots, n_layers, mbps = block_table.shape
+    rc = load().kv_scatter(
+        _dev(k, torch.bfloat16, "k"), _dev(v, torch.bfloat16, "v"), N,
+        _dev(slot_ids, torch.int32, "slot_ids"), _dev(positions, torch.int32, "positions"),
+        _dev(kv_cache, None, "kv_cache"), _n_pages(kv_cache, Hkv, d),
+        _dev(block_table, torch.int32, "block_table"), n_slots, n_layers, mbps, layer, Hkv, d,
+        _dev(err, torch.int32, "err"), _stream(stream))
+    _check(rc, "kv_scatter")
+
+
+def attn_prefill(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tensor, layer: int,
+                 seq_lens: torch.Tensor, n_kv_heads: int, scale: float, causal: bool = True,
+                 slot_ids: torch.Tensor | None = None, out: torch.Tensor | None = None,
+                 lse: torch.Tensor | None = None, err: torch.Tensor | None = None, stream=None):
+    """Paged prefill of q [B, T, Hq, d]; returns (O [B, T, Hq, d] bf16, LSE [B, Hq, T] fp32)."""
+    B, T, Hq, d = q.shape
+    n_slots, n_layers, mbps = block_table.shape
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty(B, Hq, T, dtype=torch.float32, device=q.device)
+    rc = load().attn_prefill(
+        _dev(q, torch.bfloat16, "q"), _dev(kv_cache, None, "kv_cache"),
+        _n_pages(kv_cache, n_kv_heads, d), _dev(block_table, torch.int32, "block_table"),
+        n_slots, n_layers, mbps, layer, _dev(slot_ids, torch.int32, "slot_ids"),
+        _dev(seq_lens, torch.int32, "seq_lens"), B, T, Hq, n_kv_heads, d, float(scale),
+        int(bool(causal)), _dev(out, torch.bfloat16, "out"), _dev(lse, torch.float32, "lse"),
+        _dev(err, torch.int32, "err"), _stream(stream))
+    _check(rc, "attn_prefill")
+    return out, lse
+
+
+def decode_workspace_size(B: int, Hq: int, head_dim: int, max_ctx: int) -> int:
+    return int(load().attn_decode_workspace_size(B, Hq, head_dim, max_ctx))
+
+
+def attn_decode(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tensor, layer: int,
+                ctx_lens: torch.Tensor, n_kv_heads: int, scale: float, max_ctx: int,
+                slot_ids: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                out: torch.Tensor | None = None, lse: torch.Tensor | None = None,
+                err: torch.Tensor | None = None, stream=None):
+    """Paged decode of q [B, Hq, d]; returns (O [B, Hq, d] bf16, LSE [B, Hq] fp32)."""
+    B, Hq, d = q.shape
+    n_slots, n_layers, mbps = block_table.shape
+    ws_bytes = decode_workspace_size(B, Hq, d, max_ctx)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty(B, Hq, dtype=torch.float32, device=q.device)
+    rc = load().attn_decode(
+        _dev(q, torch.bfloat16, "q"), _dev(kv_cache, None, "kv_cache"),
+        _n_pages(kv_cache, n_kv_heads, d), _dev(block_table, torch.int32, "block_table"),
+        n_slots, n_layers, mbps, layer, _dev(slot_ids, torch.int32, "slot_ids"),
+        _dev(ctx_lens, torch.int32, "ctx_lens"), B, Hq, n_kv_heads, d, float(scale), int(max_ctx),
+        _dev(workspace, None, "workspace"), workspace.numel() * workspace.element_size(),
+        _dev(out, torch.bfloat16, "out"), _dev(lse, torch.float32, "lse"),
+        _dev(err, torch.int32, "err"), _stream(stream))
+    _check(rc, "attn_decode")
+    return out, lse
+
+
+def attn_prefill_dense(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: float,
+                       causal: bool = True, out: torch.Tensor | None = None,
+                       lse: torch.Tensor | None = None, stream=None):
+    """Unpaged prefill: q [B, T, Hq, d], k, v [B, T, Hkv, d]; returns (O, LSE [B, Hq, T])."""
+    B, T, Hq, d = q.shape
+    Hkv = k.shape[2]
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty(B, Hq, T, dtype=torch.float32, device=q.device)
+    rc = load().attn_prefill_dense(
+        _dev(q, torch.bfloat16, "q"), _dev(k, torch.bfloat16, "k"), _dev(v, torch.bfloat16, "v"),
+        B, T, Hq, Hkv, d, float(scale), int(bool(causal)), _dev(out, torch.bfloat16, "out"),
+        _dev(lse, torch.float32, "lse"), _stream(stream))
+    _check(rc, "attn_prefill_dense")
+    return out, lse

@@ -1,0 +1,134 @@
+// api.hip -- the extern "C" entry points declared in include/pagedattn.h.
+// Host-side argument checks, then one or two kernel launches on the caller's
+// stream.  Nothing here allocates or synchronises.
+
+#include <hip/hip_runtime.h>
+
+#include "kernels.h"
+#include "pagedattn.h"
+
+namespace {
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool supported_head_dim(int d) { return d == 64 || d == 128; }
+
+// Common checks of the paged-cache description.
+int check_cache(const void *kv_cache, int64_t n_pages, const int32_t *block_table, int n_slots,
+                int n_layers, int mbps, int layer, int n_kv_heads, int head_dim) {
+  if (!kv_cache || !block_table) return PA_ERR_NULL;
+  if (n_pages <= 0 || n_slots <= 0 || n_layers <= 0 || mbps <= 0 || n_kv_heads <= 0 ||
+      head_dim <= 0)
+    return PA_ERR_SHAPE;
+  if (layer < 0 || layer >= n_layers) return PA_ERR_SHAPE;
+  if (!aligned16(kv_cache)) return PA_ERR_ALIGN;
+  const int64_t page = pa_page_bytes(n_kv_heads, head_dim);
+  if (n_pages > INT64_MAX / page) return PA_ERR_RANGE;
+  if (n_pages > 0x7fffffffLL) return PA_ERR_RANGE;                      // int32 page ids
+  if ((int64_t)n_slots * n_layers * mbps > 0x7fffffffLL) return PA_ERR_RANGE;
+  if ((int64_t)mbps * 16 > 0x7fffffffLL) return PA_ERR_RANGE;
+  return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *pa_status_string(int status) {
+  switch (status) {
+    case PA_OK: return "ok";
+    case PA_ERR_NULL: return "required pointer is NULL";
+    case PA_ERR_SHAPE: return "invalid or inconsistent size";
+    case PA_ERR_UNSUPPORTED: return "unsupported head_dim or group size";
+    case PA_ERR_ALIGN: return "tensor pointer not 16-byte aligned";
+    case PA_ERR_WORKSPACE: return "workspace too small";
+    case PA_ERR_RANGE: return "index or byte offset overflow";
+    case PA_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+int64_t pa_page_bytes(int n_kv_heads, int head_dim) {
+  if (n_kv_heads <= 0 || head_dim <= 0) return 0;
+  return 2LL * 16 * n_kv_heads * head_dim * 2;
+}
+
+int kv_scatter(const void *k, const void *v, int64_t n_tokens, const int32_t *slot_ids,
+               const int32_t *positions, void *kv_cache, int64_t n_pages,
+               const int32_t *block_table, int n_slots, int n_layers, int max_blocks_per_seq,
+               int layer, int n_kv_heads, int head_dim, int32_t *err, void *stream) {
+  if (n_tokens < 0) return PA_ERR_SHAPE;
+  int rc = check_cache(kv_cache, n_pages, block_table, n_slots, n_layers, max_blocks_per_seq, layer,
+                       n_kv_heads, head_dim);
+  if (rc != PA_OK) return rc;
+  if (((int64_t)n_kv_heads * head_dim) % 8 != 0) return PA_ERR_UNSUPPORTED;
+  if (n_tokens == 0) return PA_OK;
+  if (!k || !v || !slot_ids || !positions) return PA_ERR_NULL;
+  if (!aligned16(k) || !aligned16(v)) return PA_ERR_ALIGN;
+  return pa::launch_kv_scatter(k, v, n_tokens, slot_ids, positions, kv_cache, n_pages, block_table,
+                               n_slots, n_layers, max_blocks_per_seq, layer, n_kv_heads, head_dim,
+                               err, static_cast<hipStream_t>(stream));
+}
+
+int attn_prefill(const void *q, const void *kv_cache, int64_t n_pages, const int32_t *block_table,
+                 int n_slots, int n_layers, int max_blocks_per_seq, int layer,
+                 const int32_t *slot_ids, const int32_t *seq_lens, int B, int T, int Hq, int Hkv,
+                 int head_dim, float scale, int causal, void *O, float *LSE, int32_t *err,
+                 void *stream) {
+  if (B < 0 || T < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0) return PA_ERR_SHAPE;
+  if (!supported_head_dim(head_dim)) return PA_ERR_UNSUPPORTED;
+  int rc = check_cache(kv_cache, n_pages, block_table, n_slots, n_layers, max_blocks_per_seq, layer,
+                       Hkv, head_dim);
+  if (rc != PA_OK) return rc;
+  if (B == 0 || T == 0) return PA_OK;
+  if (!q || !seq_lens || !O || !LSE) return PA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(O)) return PA_ERR_ALIGN;
+  if ((int64_t)B * T * Hq > 0x7fffffffLL) return PA_ERR_RANGE;
+  return pa::launch_prefill_paged(q, kv_cache, n_pages, block_table, n_slots, n_layers,
+                                  max_blocks_per_seq, layer, slot_ids, seq_lens, B, T, Hq, Hkv,
+                                  head_dim, scale, causal, O, LSE, err,
+                                  static_cast<hipStream_t>(stream));
+}
+
+size_t attn_decode_workspace_size(int B, int Hq, int head_dim, int max_ctx) {
+  if (B <= 0 || Hq <= 0 || head_dim <= 0 || max_ctx < 0) return 0;
+  return pa::decode_workspace_bytes(B, Hq, head_dim, max_ctx);
+}
+
+int attn_decode(const void *q, const void *kv_cache, int64_t n_pages, const int32_t *block_table,
+                int n_slots, int n_layers, int max_blocks_per_seq, int layer,
+                const int32_t *slot_ids, const int32_t *ctx_lens, int B, int Hq, int Hkv,
+                int head_dim, float scale, int max_ctx, void *workspace, size_t workspace_bytes,
+                void *O, float *LSE, int32_t *err, void *stream) {
+  if (B < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || max_ctx < 0) return PA_ERR_SHAPE;
+  if (!supported_head_dim(head_dim)) return PA_ERR_UNSUPPORTED;
+  const int G = Hq / Hkv;
+  if (G != 1 && G != 2 && G != 4 && G != 8 && G != 16) return PA_ERR_UNSUPPORTED;
+  int rc = check_cache(kv_cache, n_pages, block_table, n_slots, n_layers, max_blocks_per_seq, layer,
+                       Hkv, head_dim);
+  if (rc != PA_OK) return rc;
+  if (B == 0) return PA_OK;
+  if (!q || !ctx_lens || !O || !LSE || !workspace) return PA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(O) || !aligned16(workspace)) return PA_ERR_ALIGN;
+  if (workspace_bytes < pa::decode_workspace_bytes(B, Hq, head_dim, max_ctx)) return PA_ERR_WORKSPACE;
+  return pa::launch_decode(q, kv_cache, n_pages, block_table, n_slots, n_layers,
+                           max_blocks_per_seq, layer, slot_ids, ctx_lens, B, Hq, Hkv, head_dim,
+                           scale, max_ctx, workspace, O, LSE, err,
+                           static_cast<hipStream_t>(stream));
+}
+
+int attn_prefill_dense(const void *q, const void *k, const void *v, int B, int T, int Hq, int Hkv,
+                       int head_dim, float scale, int causal, void *O, float *LSE, void *stream) {
+  if (B < 0 || T < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0) return PA_ERR_SHAPE;
+  if (!supported_head_dim(head_dim)) return PA_ERR_UNSUPPORTED;
+  const int G = Hq / Hkv;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return PA_ERR_UNSUPPORTED;
+  if (B == 0 || T == 0) return PA_OK;
+  if (!q || !k || !v || !O || !LSE) return PA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(O)) return PA_ERR_ALIGN;
+  if ((int64_t)B * T * Hq > 0x7fffffffLL) return PA_ERR_RANGE;
+  return pa::launch_prefill_dense(q, k, v, B, T, Hq, Hkv, head_dim, scale, causal, O, LSE,
+                                  static_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,32 @@
+// kernels.h -- host-side launchers of the gfx950 kernels (internal to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pa {
+
+int launch_kv_scatter(const void *k, const void *v, int64_t n_tokens, const int32_t *slot_ids,
+                      const int32_t *positions, void *kv_cache, int64_t n_pages,
+                      const int32_t *block_table, int n_slots, int n_layers, int mbps, int layer,
+                      int n_kv_heads, int head_dim, int32_t *err, hipStream_t stream);
+
+int launch_prefill_paged(const void *q, const void *kv_cache, int64_t n_pages,
+                         const int32_t *block_table, int n_slots, int n_layers, int mbps, int layer,
+                         const int32_t *slot_ids, const int32_t *seq_lens, int B, int T, int Hq,
+                         int Hkv, int D, float scale, int causal, void *O, float *LSE, int32_t *err,
+                         hipStream_t stream);
+
+int launch_prefill_dense(const void *q, const void *k, const void *v, int B, int T, int Hq, int Hkv,
+                         int D, float scale, int causal, void *O, float *LSE, hipStream_t stream);
+
+int decode_split_tokens(int B, int max_ctx);
+size_t decode_workspace_bytes(int B, int Hq, int D, int max_ctx);
+
+int launch_decode(const void *q, const void *kv_cache, int64_t n_pages, const int32_t *block_table,
+                  int n_slots, int n_layers, int mbps, int layer, const int32_t *slot_ids,
+                  const int32_t *ctx_lens, int B, int Hq, int Hkv, int D, float scale, int max_ctx,
+                  void *workspace, void *O, float *LSE, int32_t *err, hipStream_t stream);
+
+}  // namespace pa

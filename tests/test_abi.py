@@ -1,0 +1,90 @@
+"""The C-ABI library loads and exports what include/pagedattn.h declares; host
+argument checks reject bad calls before anything is launched (CPU only)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import paged_kv_cache_amd as pa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pagedattn.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*([a-z_][a-z_0-9]*)\s*\(", src, re.M)))
+
+
+def test_header_declares_the_path():
+    names = declared_functions()
+    for n in ["kv_scatter", "attn_prefill", "attn_decode", "attn_prefill_dense",
+              "attn_decode_workspace_size", "pa_status_string", "pa_page_bytes"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(pa.LIB_PATH)
+    for n in declared_functions():
+        assert hasattr(lib, n), f"{n} declared in pagedattn.h but not exported"
+
+
+def test_page_bytes_and_status_strings():
+    assert pa.page_bytes(8, 64) == 32768
+    assert pa.page_bytes(2, 128) == 2 * 16 * 2 * 128 * 2
+    lib = pa.load()
+    for s in range(0, -8, -1):
+        assert lib.pa_status_string(s).decode() not in ("", "unknown status")
+    assert lib.pa_status_string(5).decode() == "unknown status"
+
+
+def test_decode_workspace_size():
+    assert pa.decode_workspace_size(64, 32, 64, 2048) > 64 * 32 * 64 * 4
+    assert pa.decode_workspace_size(0, 32, 64, 2048) == 0
+
+
+P = ctypes.c_void_p
+
+
+def _fake(addr=0x10000):
+    return ctypes.c_void_p(addr)
+
+
+def test_host_checks_reject_bad_arguments():
+    lib = pa.load()
+    good = _fake()
+    # NULL cache
+    assert lib.kv_scatter(good, good, 1, good, good, None, 64, good, 1, 1, 128, 0, 8, 64, None, None) == -1
+    # layer out of range
+    assert lib.kv_scatter(good, good, 1, good, good, good, 64, good, 1, 1, 128, 1, 8, 64, None, None) == -2
+    # misaligned k
+    assert lib.kv_scatter(_fake(0x10002), good, 1, good, good, good, 64, good, 1, 1, 128, 0, 8, 64,
+                          None, None) == -4
+    # zero tokens is a no-op
+    assert lib.kv_scatter(None, None, 0, None, None, good, 64, good, 1, 1, 128, 0, 8, 64, None, None) == 0
+    # unsupported head_dim
+    assert lib.attn_prefill(good, good, 64, good, 1, 1, 128, 0, None, good, 1, 17, 32, 8, 96,
+                            0.125, 1, good, good, None, None) == -3
+    # Hq not a multiple of Hkv
+    assert lib.attn_prefill(good, good, 64, good, 1, 1, 128, 0, None, good, 1, 17, 30, 8, 64,
+                            0.125, 1, good, good, None, None) == -2
+    # group size without a decode kernel
+    assert lib.attn_decode(good, good, 64, good, 1, 1, 128, 0, None, good, 1, 96, 3, 64, 0.125,
+                           64, good, 1 << 20, good, good, None, None) == -3
+    # workspace too small
+    assert lib.attn_decode(good, good, 64, good, 1, 1, 128, 0, None, good, 64, 32, 8, 64, 0.125,
+                           2048, good, 16, good, good, None, None) == -5
+    # page count overflow of int32 page ids
+    assert lib.kv_scatter(good, good, 1, good, good, good, 1 << 31, good, 1, 1, 128, 0, 8, 64,
+                          None, None) == -6
+    assert lib.attn_prefill_dense(good, good, None, 1, 16, 4, 4, 64, 0.125, 1, good, good, None) == -1
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(pa, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(pa, "_lib", None)
+    with pytest.raises(ImportError):
+        pa.load()

@@ -1,0 +1,168 @@
+"""attn_prefill (paged) and attn_prefill_dense on the GPU against the oracle."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from gpu_util import (DEV, assert_attn_close, device_pool, i32, prefill_rows_layout, run_prefill,
+                      sample_rows, scatter)
+
+import paged_kv_cache_amd as pa
+
+pytestmark = pytest.mark.gpu
+
+
+def _full_parity(case, what=None):
+    O, L, pool = run_prefill(case)
+    Oref, Lref, _ = oracle.prefill_case(case)
+    B, T, Hq, d = case.q.shape
+    # oracle rows are (b, t) in order: [B*T, Hq, d] and [B*T, Hq]
+    assert_attn_close(O.reshape(B * T, Hq, d), L.permute(0, 2, 1).reshape(B * T, Hq), Oref, Lref,
+                      what=what or case.name)
+    return O, L, pool
+
+
+def test_prefill_tiny_prompt():
+    _full_parity(W.tiny_prefill())
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(32, 8), (8, 8), (16, 8), (64, 8)])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [True, False])
+def test_prefill_ragged(Hq, Hkv, d, causal):
+    # lengths crossing the 32-row, 64-key and 128-row tile edges, plus empty and 1
+    lens = [200, 1, 64, 65, 0, 129]
+    case = W.make_prefill("ragged", B=len(lens), T=200, Hq=Hq, Hkv=Hkv, d=d, n_pages=120,
+                          seed=Hq + d, seq_lens=lens, causal=causal, n_layers=2, layer=1,
+                          n_slots=8, slot_ids=[7, 0, 3, 5, 1, 2], fill_other_layers=True)
+    O, L, _ = _full_parity(case)
+    assert torch.all(O[4] == 0) and torch.all(torch.isneginf(L[4]))
+
+
+def test_prefill_llama_sampled_rows():
+    case = W.llama_prefill()
+    O, L, _ = run_prefill(case)
+    rows = sample_rows(case.B, case.T, per_seq=48)
+    Oref, Lref, _ = oracle.prefill_case(case, rows=rows)
+    Og, Lg = prefill_rows_layout(O, L, rows)
+    assert_attn_close(Og, Lg, Oref, Lref, what="llama prefill")
+
+
+def test_prefill_llama_properties_all_rows():
+    """Every row of the full-size prefill: finite, and O within the convex hull
+    bound |O| <= max|V| of the visible keys; LSE >= max visible score."""
+    case = W.llama_prefill()
+    O, L, _ = run_prefill(case)
+    assert torch.isfinite(O.float()).all() and torch.isfinite(L).all()
+    vmax = float(case.tokens.v.float().abs().max())
+    assert float(O.float().abs().max()) <= vmax + 2e-2
+
+
+def test_prefill_deterministic_and_permutation_bitwise():
+    a = W.make_prefill("pa", B=2, T=300, Hq=32, Hkv=8, d=64, n_pages=128, seed=21)
+    b = W.make_prefill("pb", B=2, T=300, Hq=32, Hkv=8, d=64, n_pages=128, seed=21)
+    perm = np.random.default_rng(99).permutation(128).astype(np.int32)
+    b.cache.block_table = np.where(a.cache.block_table >= 0, perm[np.maximum(a.cache.block_table, 0)], -1)
+    Oa, La, pool = run_prefill(a)
+    Oa2, La2, _ = run_prefill(a, pool=pool)
+    Ob, Lb, _ = run_prefill(b)
+    assert torch.equal(Oa, Oa2) and torch.equal(La, La2)
+    assert torch.equal(Oa, Ob) and torch.equal(La, Lb)
+
+
+def test_prefill_zero_query_running_mean():
+    case = W.make_prefill("zq", B=1, T=130, Hq=32, Hkv=8, d=64, n_pages=16, seed=4)
+    case.q = torch.zeros_like(case.q)
+    O, L, _ = run_prefill(case)
+    expect = torch.log(torch.arange(1, 131, dtype=torch.float32))
+    assert (L[0].cpu() - expect[None, :]).abs().max() <= 1e-3
+    _full_parity(case)
+
+
+def test_prefill_worked_example_row():
+    d = 64
+    case = W.make_prefill("fa2", B=1, T=4, Hq=1, Hkv=1, d=d, n_pages=4, seed=2, scale=1 / 8)
+    q = torch.zeros(1, 4, 1, d)
+    q[..., 0] = 8.0
+    k = torch.zeros(4, 1, d)
+    k[:, 0, 0] = torch.tensor([1.0, 2.0, 3.0, 0.0])
+    v = torch.zeros(4, 1, d)
+    v[:, 0, 0] = torch.tensor([10.0, 20.0, 30.0, 0.0])
+    case.q = q.to(torch.bfloat16)
+    case.tokens.k, case.tokens.v = k.to(torch.bfloat16), v.to(torch.bfloat16)
+    O, L, _ = run_prefill(case)
+    assert abs(float(O[0, 3, 0, 0]) - 24.9265) <= 0.125
+    assert abs(float(L[0, 0, 3]) - 3.440190) <= 1e-3
+    assert abs(float(L[0, 0, 1]) - (2 + math.log(1 + math.exp(-1)))) <= 1e-3
+
+
+def test_prefill_missing_page_is_flagged_and_skipped():
+    case = W.make_prefill("bad", B=1, T=100, Hq=32, Hkv=8, d=64, n_pages=16, seed=8)
+    _, _, pool = run_prefill(case)
+    bt = case.cache.block_table.copy()
+    bt[0, 0, 3] = -1
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    O, L = pa.attn_prefill(case.q.to(DEV), pool, i32(bt), 0, i32(case.seq_lens), 8, case.scale,
+                           err=err)
+    pool_h = oracle.pool_for(case)
+    oracle.scatter_tokens(pool_h, case.cache, case.tokens)
+    Oref, Lref, bad = oracle.attn_prefill(case.q, pool_h, 16, bt, 0, None, case.seq_lens, 8,
+                                          case.scale, True)
+    assert bad > 0
+    torch.cuda.synchronize()
+    assert int(err.item()) & pa.PA_DEVERR_BAD_PAGE
+    # every row still sees keys 0..47, so every row is compared
+    assert_attn_close(O[0], L[0].T, Oref, Lref, what="missing page")
+
+
+# ------------------------------------------------------------------- dense
+
+def _dense_parity(case, rows=None):
+    O, L = pa.attn_prefill_dense(case.q.to(DEV), case.k.to(DEV), case.v.to(DEV), case.scale,
+                                 case.causal)
+    Oref, Lref = oracle.dense_case(case, rows=rows)
+    B, T, Hq, d = case.q.shape
+    if rows is None:
+        assert_attn_close(O.reshape(B * T, Hq, d), L.permute(0, 2, 1).reshape(B * T, Hq), Oref,
+                          Lref, what=case.name)
+    else:
+        Og, Lg = prefill_rows_layout(O, L, rows)
+        assert_attn_close(Og, Lg, Oref, Lref, what=case.name)
+    return O, L
+
+
+@pytest.mark.parametrize("d,H,Hkv", [(64, 8, 8), (128, 4, 4), (64, 16, 4), (128, 8, 2)])
+@pytest.mark.parametrize("causal", [True, False])
+def test_dense_small(d, H, Hkv, causal):
+    _dense_parity(W.make_dense("dense", B=2, T=333, Hq=H, Hkv=Hkv, d=d, causal=causal, seed=d + H))
+
+
+@pytest.mark.parametrize("T", [512, 2048, 16384])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [True, False])
+def test_dense_fa2_shapes_sampled(T, d, causal):
+    case = W.fa2_dense(T, d, causal)
+    rows = sample_rows(case.q.shape[0], T, per_seq=max(4, 64 // case.q.shape[0]))
+    if len(rows) > 160:
+        rows = rows[np.random.default_rng(0).permutation(len(rows))[:160]]
+    _dense_parity(case, rows=rows)
+
+
+def test_dense_long_prefill_sampled():
+    case = W.long_prefill()
+    rows = sample_rows(1, case.q.shape[1], per_seq=40)
+    _dense_parity(case, rows=rows)
+
+
+def test_paged_equals_dense_bitwise():
+    """Same keys, same tiles: the paged and the dense instance give identical bits."""
+    p = W.make_prefill("p", B=2, T=200, Hq=32, Hkv=8, d=64, n_pages=64, seed=13)
+    Op, Lp, _ = run_prefill(p)
+    k = p.tokens.k.reshape(2, 200, 8, 64).to(DEV)
+    v = p.tokens.v.reshape(2, 200, 8, 64).to(DEV)
+    Od, Ld = pa.attn_prefill_dense(p.q.to(DEV), k, v, p.scale, True)
+    assert torch.equal(Op, Od) and torch.equal(Lp, Ld)
