@@ -73,19 +73,31 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
   constexpr int RW = kWaves / HW;                  // 32-row blocks per workgroup
   constexpr int BM = 32 * RW;                      // query rows per workgroup
   constexpr int KROW = D + 8;                      // K row in LDS (bf16), padded
-  constexpr int VROW = kBN + 2;                    // V^T row in LDS (bf16), padded
   constexpr int CH = D / 8;                        // 16-byte chunks per K/V row
   constexpr int NLD = kBN * CH / kThreads;         // 16-byte loads per thread per tile (K, and V)
+  constexpr int KTILE = kBN * KROW;                // bf16 elements of one K tile in LDS
+  constexpr int VTILE = kBN * D;                   // bf16 elements of one V tile in LDS
   static_assert(NLD >= 1 && kBN * CH % kThreads == 0, "tile/thread mismatch");
+  static_assert(kPageTokens % (64 / CH) == 0, "a wave load step must stay inside one page");
+  // A running max is only raised when a row's tile max exceeds it by more
+  // than this (log2 units), so most tiles skip the rescale; p stays <= 2^8.
+  constexpr float kRescaleSlack = 8.f;
+  constexpr float kMaxFloor = -1e30f;              // finite start of the running max
 
-  __shared__ __attribute__((aligned(16))) uint16_t ks[kBN * KROW];
-  __shared__ __attribute__((aligned(16))) uint16_t vt[D * VROW];
+  // Two K and two V tiles: tile t+1 is written while tile t is read.
+  // V is row-major [key][d] with its 16-byte chunks XOR-swizzled per key so
+  // that the transposing reads of the PV operands hit 64 distinct banks.
+  __shared__ __attribute__((aligned(16))) uint16_t ks[2 * KTILE];
+  __shared__ __attribute__((aligned(16))) uint16_t vs[2 * VTILE];
+  auto vswz = [](int key) { return 4 * ((key / (128 / D)) % (CH / 4)); };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int lr = lane & 31;      // query row within the wave's 32 rows
   const int lh = lane >> 5;      // lane half
+  const int l16 = lane & 15;     // lane within its 16-lane group
+  const int g16 = lane >> 4;     // 16-lane group
 
   // ---- workgroup -> (sequence, head group, query tile)
   const int n_pairs = a.B * a.n_hgroups;
@@ -110,7 +122,10 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
   const int T = a.T;
 
   int len = T;
-  PageTable pt{};
+  // paged source of this sequence: table row and page geometry
+  const int32_t *trow = nullptr;
+  const int64_t page_bytes = 2LL * kPageTokens * a.Hkv * D * 2;
+  const int64_t v_offset = page_bytes / 2;
   if constexpr (PAGED) {
     len = a.seq_lens[b];
     if (len < 0 || len > T) {
@@ -126,20 +141,17 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
       if (tid == 0 && hg == 0 && rb == 0) raise_err(a.err, PA_DEVERR_BAD_POS);
       len = a.mbps * kPageTokens;
     }
-    pt.pool = a.pool;
-    pt.row = a.block_table + ((int64_t)(len > 0 ? slot : 0) * a.n_layers + a.layer) * a.mbps;
-    pt.n_pages = a.n_pages;
-    pt.page_bytes = 2LL * kPageTokens * a.Hkv * D * 2;
-    pt.v_offset = pt.page_bytes / 2;
-    pt.mbps = a.mbps;
+    trow = a.block_table + ((int64_t)(len > 0 ? slot : 0) * a.n_layers + a.layer) * a.mbps;
   }
 
   const int row = row0 + lr;
   const int wg_row_end = min(rb * BM + BM, len);
   const int kv_end = a.causal ? wg_row_end : len;
   const int n_tiles = (kv_end > 0 && rb * BM < len) ? (kv_end + kBN - 1) / kBN : 0;
+  // last key this lane's row may see (-1: padding row, sees nothing)
+  const int lim = row < len ? (a.causal ? row : len - 1) : -1;
 
-  // ---- Q^T as B operands: lane holds row `row`, d = lh*(D/2) + ks*8 + i
+  // ---- Q^T as B operands: lane holds row `row`, d = lh*(D/2) + k*8 + i
   bf16x8 qf[D / 16];
   {
     const bool ok = row < len;
@@ -155,144 +167,182 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
   for (int i = 0; i < D / 32; ++i)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[i][r] = 0.f;
-  float m_run = -INFINITY;
-  float l_lane = 0.f;
+  float m_run = kMaxFloor;   // reference max of the row (log2 units)
+  float l_lane = 0.f;        // this lane's half of the row's exp-sum
+  const float c = a.scale_log2;
 
-  // ---- K/V tile loader: thread covers (key tid/CH + c*(256/CH), chunk tid%CH)
+  // ---- physical page of logical block blk, -1 when missing.  Every lane of
+  // a wave asks for the same block, so this is a scalar load.
+  auto page_of = [&](int blk) -> int64_t {
+    if (blk * kPageTokens >= kv_end || blk >= a.mbps) return -1;
+    const int32_t v = trow[blk];
+    return (v < 0 || (int64_t)v >= a.n_pages) ? -1 : (int64_t)v;
+  };
+  // In one load step the 64 lanes of a wave cover 64/CH consecutive keys of a
+  // single page, so the page index is uniform per (step, wave).
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+
+  // ---- K/V tile loader: thread covers (key idx/CH, chunk idx%CH), idx = c*256 + tid
   uint4 kr[NLD], vr[NLD];
   auto load_tile = [&](int kv0) {
 #pragma unroll
-    for (int c = 0; c < NLD; ++c) {
-      const int idx = c * kThreads + tid;
+    for (int cc = 0; cc < NLD; ++cc) {
+      const int idx = cc * kThreads + tid;
       const int key = idx / CH;
       const int ch = idx % CH;
       const int j = kv0 + key;
-      kr[c] = uint4{0u, 0u, 0u, 0u};
-      vr[c] = uint4{0u, 0u, 0u, 0u};
-      if (j < kv_end) {
-        if constexpr (PAGED) {
-          const int64_t page = pt.page(j / kPageTokens);
-          if (page >= 0) {
-            const uint8_t *p = pt.pool + page * pt.page_bytes +
+      kr[cc] = uint4{0u, 0u, 0u, 0u};
+      vr[cc] = uint4{0u, 0u, 0u, 0u};
+      if constexpr (PAGED) {
+        const int64_t page = page_of(kv0 / kPageTokens + ((cc * kThreads + 64 * wv) / CH) / kPageTokens);
+        if (j < kv_end && page >= 0) {
+          const uint8_t *src = a.pool + page * page_bytes +
                                (int64_t)(j % kPageTokens) * a.Hkv * D * 2 + (int64_t)kvh * D * 2 + ch * 16;
-            kr[c] = *reinterpret_cast<const uint4 *>(p);
-            vr[c] = *reinterpret_cast<const uint4 *>(p + pt.v_offset);
-          }
-        } else {
+          kr[cc] = *reinterpret_cast<const uint4 *>(src);
+          vr[cc] = *reinterpret_cast<const uint4 *>(src + v_offset);
+        }
+      } else {
+        if (j < kv_end) {
           const int64_t off = (((int64_t)b * T + j) * a.Hkv + kvh) * D + ch * 8;
-          kr[c] = *reinterpret_cast<const uint4 *>(a.k + off);
-          vr[c] = *reinterpret_cast<const uint4 *>(a.v + off);
+          kr[cc] = *reinterpret_cast<const uint4 *>(a.k + off);
+          vr[cc] = *reinterpret_cast<const uint4 *>(a.v + off);
         }
       }
     }
   };
-  auto store_tile = [&]() {
+  auto store_tile = [&](int buf) {
 #pragma unroll
-    for (int c = 0; c < NLD; ++c) {
-      const int idx = c * kThreads + tid;
+    for (int cc = 0; cc < NLD; ++cc) {
+      const int idx = cc * kThreads + tid;
       const int key = idx / CH;
       const int ch = idx % CH;
-      *reinterpret_cast<uint4 *>(&ks[key * KROW + ch * 8]) = kr[c];
-      const uint32_t w[4] = {vr[c].x, vr[c].y, vr[c].z, vr[c].w};
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        vt[(ch * 8 + i) * VROW + key] = (uint16_t)(w[i / 2] >> (16 * (i % 2)));
+      *reinterpret_cast<uint4 *>(&ks[buf * KTILE + key * KROW + ch * 8]) = kr[cc];
+      *reinterpret_cast<uint4 *>(&vs[buf * VTILE + key * D + ((ch ^ vswz(key)) * 8)]) = vr[cc];
     }
   };
 
-  if (n_tiles > 0) load_tile(0);
+  if (n_tiles > 0) {
+    load_tile(0);
+    store_tile(0);
+    if (n_tiles > 1) load_tile(kBN);
+    __syncthreads();
+  }
 
   for (int t = 0; t < n_tiles; ++t) {
     const int kv0 = t * kBN;
-    __syncthreads();
-    store_tile();
-    __syncthreads();
-    if (t + 1 < n_tiles) load_tile(kv0 + kBN);
-
-    // pages of this tile that are needed but missing from the table: their
-    // keys are left out (the same four table entries in every lane)
-    uint32_t bad_pages = 0;
+    const int buf = t & 1;
+    uint32_t bad_pages = 0;    // needed pages of this tile missing from the table
     if constexpr (PAGED) {
 #pragma unroll
       for (int p = 0; p < kBN / kPageTokens; ++p) {
         const int blk = kv0 / kPageTokens + p;
-        if (blk * kPageTokens < kv_end && pt.page(blk) < 0) bad_pages |= 1u << p;
+        if (blk * kPageTokens < kv_end && page_of(blk) < 0) bad_pages |= 1u << p;
       }
       if (bad_pages && tid == 0) raise_err(a.err, PA_DEVERR_BAD_PAGE);
     }
 
     // a wave whose rows all precede this tile sees none of it (causal)
-    if (a.causal && kv0 > row0 + 31) continue;
-    const bool need_mask = (a.causal && kv0 + kBN - 1 > row0) || (kv0 + kBN > len) || bad_pages;
+    if (!(a.causal && kv0 > row0 + 31)) {
+      const uint16_t *kt = &ks[buf * KTILE];
+      const uint16_t *vtile = &vs[buf * VTILE];
+      // S^T = K Q^T: two 32-key halves
+      f32x16 s[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[h][r] = 0.f;
+#pragma unroll
+        for (int k = 0; k < D / 16; ++k) {
+          const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(&kt[(h * 32 + lr) * KROW + lh * (D / 2) + k * 8]);
+          s[h] = mfma32(kf, qf[k], s[h]);
+        }
+      }
 
-    // S^T = K Q^T: two 32-key halves
-    f32x16 s[2];
+      // mask: only tiles that cross the diagonal, the sequence end or a missing
+      // page.  The lane holds keys kv0 + h*32 + 8*(r/4) + 4*lh + r%4.
+      const bool need_mask = (kv0 + kBN - 1 > row0 && a.causal) | (kv0 + kBN > len) | (bad_pages != 0);
+      if (need_mask) {
+        const int rel = lim - (kv0 + 4 * lh);      // visible iff key offset <= rel
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
+        for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s[h][r] = 0.f;
+          for (int r = 0; r < 16; ++r) {
+            const int off = h * 32 + 8 * (r / 4) + (r % 4);
+            s[h][r] = off <= rel ? s[h][r] : -INFINITY;
+          }
+        if (bad_pages) {
 #pragma unroll
-      for (int k = 0; k < D / 16; ++k) {
-        const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(&ks[(h * 32 + lr) * KROW + lh * (D / 2) + k * 8]);
-        s[h] = mfma32(kf, qf[k], s[h]);
+          for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int pidx = (h * 32 + 8 * (r / 4) + 4 * lh) / kPageTokens;
+              s[h][r] = ((bad_pages >> pidx) & 1u) ? -INFINITY : s[h][r];
+            }
+        }
+      }
+
+      // tile row max of the raw scores (scale >= 0 keeps the order)
+      float rmax = -INFINITY;
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) rmax = fmaxf(rmax, s[h][r]);
+      rmax = fmaxf(rmax, __shfl_xor(rmax, 32));
+      const float mt = rmax * c;
+      if (__any(mt > m_run + kRescaleSlack)) {
+        const float m_new = fmaxf(m_run, mt);
+        const float corr = fast_exp2(m_run - m_new);
+        m_run = m_new;
+        l_lane *= corr;
+#pragma unroll
+        for (int i = 0; i < D / 32; ++i)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[i][r] *= corr;
+      }
+
+      // P = 2^(s*c - m) (bf16) as B operands of the PV product: 16 keys each
+      bf16x8 pb[4];
+      float psum = 0.f;
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float p = fast_exp2(__builtin_fmaf(s[h][r], c, -m_run));
+          psum += p;
+          pb[h * 2 + r / 8][r % 8] = (__bf16)p;
+        }
+      l_lane += psum;
+
+      // O^T += V^T P^T.  Operand kk covers keys 16kk..16kk+15; contraction slot
+      // (lh*8 + i) is key 16kk + 8*(i/4) + 4*lh + i%4.  Each half of the A
+      // operand is one transposing LDS read: in 16-lane group g, lane L points
+      // at V[key0 + L/4][d0 + 4*(L%4)] and receives V[key0..key0+3][d0 + L].
+#pragma unroll
+      for (int mb = 0; mb < D / 32; ++mb) {
+        const int dcol = mb * 32 + 16 * (g16 & 1) + 4 * (l16 & 3);   // this lane's 4 d values
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+          uint2 part[2];
+#pragma unroll
+          for (int half = 0; half < 2; ++half) {
+            const int key = 16 * kk + 8 * half + 4 * (g16 >> 1) + (l16 >> 2);
+            const int ch = dcol / 8;
+            const uint16_t *src = &vtile[key * D + ((ch ^ vswz(key)) * 8) + (dcol % 8)];
+            part[half] = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                                       (__attribute__((address_space(3))) i16x4 *)(src)));
+          }
+          const bf16x8 va = __builtin_bit_cast(bf16x8, uint4{part[0].x, part[0].y, part[1].x, part[1].y});
+          acc[mb] = mfma32(va, pb[kk], acc[mb]);
+        }
       }
     }
 
-    // scale, mask, row max (lane holds keys h*32 + 8*(r/4) + 4*lh + r%4)
-    float cmax = -INFINITY;
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float x = s[h][r] * a.scale_log2;
-        if (need_mask) {
-          const int j = kv0 + h * 32 + 8 * (r / 4) + 4 * lh + (r % 4);
-          const bool vis = j < len && (!a.causal || j <= row) &&
-                           !((bad_pages >> ((j - kv0) / kPageTokens)) & 1u);
-          x = vis ? x : -INFINITY;
-        }
-        s[h][r] = x;
-        cmax = fmaxf(cmax, x);
-      }
-    cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
-    const float m_new = fmaxf(m_run, cmax);
-    const bool live = m_new != -INFINITY;
-    const float corr = live ? fast_exp2(m_run - m_new) : 1.f;
-    m_run = m_new;
-
-    // P (bf16) as B operands of the PV product: 16 keys per operand
-    bf16x8 pb[4];
-    float psum = 0.f;
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = live ? fast_exp2(s[h][r] - m_new) : 0.f;
-        psum += p;
-        pb[h * 2 + r / 8][r % 8] = (__bf16)p;
-      }
-    l_lane = l_lane * corr + psum;
-#pragma unroll
-    for (int i = 0; i < D / 32; ++i)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][r] *= corr;
-
-    // O^T += V^T P^T; operand kk covers keys 16kk..16kk+15, slot (lh*8 + i)
-    // is key 16kk + 8*(i/4) + 4*lh + i%4
-#pragma unroll
-    for (int mb = 0; mb < D / 32; ++mb) {
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const uint16_t *vrow = &vt[(mb * 32 + lr) * VROW + 16 * kk + 4 * lh];
-        bf16x8 va;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          va[i] = __builtin_bit_cast(__bf16, vrow[i]);
-          va[4 + i] = __builtin_bit_cast(__bf16, vrow[8 + i]);
-        }
-        acc[mb] = mfma32(va, pb[kk], acc[mb]);
-      }
+    // stage tile t+1 into the other buffer, then prefetch tile t+2
+    if (t + 1 < n_tiles) {
+      store_tile(buf ^ 1);
+      if (t + 2 < n_tiles) load_tile(kv0 + 2 * kBN);
     }
+    __syncthreads();
   }
 
   // ---- epilogue: one divide per row, LSE in natural-log units
