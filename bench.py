@@ -145,8 +145,7 @@ def bench_decode(steps: int, warmup: int, replicas: int = 8):
     lens = i32(case.ctx_lens)
     sid = i32(case.slot_ids)
     max_ctx = case.max_ctx
-    ws = torch.empty(pa.decode_workspace_size(case.B, case.Hq, case.d, max_ctx), dtype=torch.uint8,
-                     device=DEV)
+    ws = pa.decode_workspace(case.B, case.Hq, c.n_kv_heads, case.d, max_ctx, DEV)
     O = torch.empty_like(q)
     L = torch.empty(case.B, case.Hq, dtype=torch.float32, device=DEV)
 

@@ -145,9 +145,12 @@ int attn_prefill(const void *q, const void *kv_cache, int64_t n_pages, const int
  *                newest; 0 gives O = 0, LSE = -INFINITY.
  *   max_ctx      host upper bound on every ctx_lens[b] (sizes the split grid);
  *                a larger ctx_lens[b] sets PA_DEVERR_BAD_POS and is cut to max_ctx.
- *   workspace    device scratch of at least attn_decode_workspace_size(B, Hq,
- *                head_dim, max_ctx) bytes, 16-byte aligned; contents on entry
- *                do not matter; two calls in flight must not share it.
+ *   workspace    device scratch of attn_decode_workspace_size(B, Hq, Hkv,
+ *                head_dim, max_ctx) bytes, 16-byte aligned, for the partial
+ *                results when contexts are split across workgroups (few long
+ *                sequences); the size is 0 (workspace may be NULL) when they
+ *                are not.  Contents on entry do not matter; two calls in
+ *                flight must not share it.
  *   O            [B][Hq][head_dim] bf16 output;  LSE [B][Hq] fp32 output.
  *   Other arguments as for attn_prefill.  Supported: head_dim 64 or 128,
  *   Hq/Hkv in {1, 2, 4, 8, 16}.
@@ -159,7 +162,7 @@ int attn_decode(const void *q, const void *kv_cache, int64_t n_pages, const int3
                 void *O, float *LSE, int32_t *err, void *stream);
 
 /* Workspace bytes attn_decode needs for this batch shape (0 on bad sizes). */
-size_t attn_decode_workspace_size(int B, int Hq, int head_dim, int max_ctx);
+size_t attn_decode_workspace_size(int B, int Hq, int Hkv, int head_dim, int max_ctx);
 
 /*
  * attn_prefill_dense -- the prefill on contiguous K/V (FlashAttention-2

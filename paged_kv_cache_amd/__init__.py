@@ -54,7 +54,7 @@ def load():
         lib.attn_decode.argtypes = [_P, _P, _I64, _P, _I, _I, _I, _I, _P, _P, _I, _I, _I, _I, _F,
                                     _I, _P, _SZ, _P, _P, _P, _P]
         lib.attn_decode_workspace_size.restype = _SZ
-        lib.attn_decode_workspace_size.argtypes = [_I, _I, _I, _I]
+        lib.attn_decode_workspace_size.argtypes = [_I, _I, _I, _I, _I]
         lib.attn_prefill_dense.restype = _I
         lib.attn_prefill_dense.argtypes = [_P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P, _P, _P]
         _lib = lib
@@ -134,8 +134,15 @@ def attn_prefill(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Ten
     return out, lse
 
 
-def decode_workspace_size(B: int, Hq: int, head_dim: int, max_ctx: int) -> int:
-    return int(load().attn_decode_workspace_size(B, Hq, head_dim, max_ctx))
+def decode_workspace_size(B: int, Hq: int, Hkv: int, head_dim: int, max_ctx: int) -> int:
+    return int(load().attn_decode_workspace_size(B, Hq, Hkv, head_dim, max_ctx))
+
+
+def decode_workspace(B: int, Hq: int, Hkv: int, head_dim: int, max_ctx: int,
+                     device=None) -> torch.Tensor:
+    """A decode workspace of the size attn_decode needs for this shape (may be 16 B)."""
+    n = max(decode_workspace_size(B, Hq, Hkv, head_dim, max_ctx), 16)
+    return torch.empty(n, dtype=torch.uint8, device=device or torch.device("cuda"))
 
 
 def attn_decode(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tensor, layer: int,
@@ -146,9 +153,8 @@ def attn_decode(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tens
     """Paged decode of q [B, Hq, d]; returns (O [B, Hq, d] bf16, LSE [B, Hq] fp32)."""
     B, Hq, d = q.shape
     n_slots, n_layers, mbps = block_table.shape
-    ws_bytes = decode_workspace_size(B, Hq, d, max_ctx)
     if workspace is None:
-        workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=q.device)
+        workspace = decode_workspace(B, Hq, n_kv_heads, d, max_ctx, q.device)
     if out is None:
         out = torch.empty_like(q)
     if lse is None:

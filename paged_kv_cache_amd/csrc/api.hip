@@ -90,9 +90,9 @@ int attn_prefill(const void *q, const void *kv_cache, int64_t n_pages, const int
                                   static_cast<hipStream_t>(stream));
 }
 
-size_t attn_decode_workspace_size(int B, int Hq, int head_dim, int max_ctx) {
-  if (B <= 0 || Hq <= 0 || head_dim <= 0 || max_ctx < 0) return 0;
-  return pa::decode_workspace_bytes(B, Hq, head_dim, max_ctx);
+size_t attn_decode_workspace_size(int B, int Hq, int Hkv, int head_dim, int max_ctx) {
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || head_dim <= 0 || max_ctx < 0) return 0;
+  return pa::decode_workspace_bytes(B, Hq, Hkv, head_dim, max_ctx);
 }
 
 int attn_decode(const void *q, const void *kv_cache, int64_t n_pages, const int32_t *block_table,
@@ -108,9 +108,12 @@ int attn_decode(const void *q, const void *kv_cache, int64_t n_pages, const int3
                        Hkv, head_dim);
   if (rc != PA_OK) return rc;
   if (B == 0) return PA_OK;
-  if (!q || !ctx_lens || !O || !LSE || !workspace) return PA_ERR_NULL;
-  if (!aligned16(q) || !aligned16(O) || !aligned16(workspace)) return PA_ERR_ALIGN;
-  if (workspace_bytes < pa::decode_workspace_bytes(B, Hq, head_dim, max_ctx)) return PA_ERR_WORKSPACE;
+  if (!q || !ctx_lens || !O || !LSE) return PA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(O)) return PA_ERR_ALIGN;
+  const size_t ws_need = pa::decode_workspace_bytes(B, Hq, Hkv, head_dim, max_ctx);
+  if (ws_need > 0 && !workspace) return PA_ERR_NULL;
+  if (ws_need > 0 && !aligned16(workspace)) return PA_ERR_ALIGN;
+  if (workspace_bytes < ws_need) return PA_ERR_WORKSPACE;
   return pa::launch_decode(q, kv_cache, n_pages, block_table, n_slots, n_layers,
                            max_blocks_per_seq, layer, slot_ids, ctx_lens, B, Hq, Hkv, head_dim,
                            scale, max_ctx, workspace, O, LSE, err,

@@ -1,32 +1,38 @@
 // decode.hip -- attn_decode: one query token per sequence against its whole
 // paged context (tiny-vllm part 6, "pagedAttentionKernel" and "logical block
-// -> physical block -> byte address"), with the context split across
-// wavefronts and merged by the log-sum-exp rule (tiny-vllm part 3, "causalMask
+// -> physical block -> byte address"), the context split across wavefronts
+// and the splits merged by the log-sum-exp rule (tiny-vllm part 3, "causalMask
 // and online softmax": partial results are rescaled to the larger maximum and
 // added).
 //
-// Work split.  One wavefront owns (sequence b, kv head, split of S tokens).
-// The reference launches one 64-thread block per (sequence, q head), reads
-// each kv head once per q head of its group, and reduces every single
-// q.k over shuffles and two barriers.  Here the G = Hq/Hkv query heads of a
-// group ride in the columns of one MFMA, so each K/V byte is read from HBM
-// exactly once, and the tokens ride in its rows:
+// Work split.  A workgroup of kWaves wavefronts owns (sequence b, kv head,
+// cross-split of the context); its wavefronts take interleaved 32-token chunks
+// and merge their partial results through LDS at the end.  Only when the
+// batch is too small to fill the GPU (few long sequences) is a context also
+// split across workgroups, whose partials a small second kernel merges.
 //
-//   S^T[16 tok][16 col] = K[16 tok][32 d] x Q^T[32 d][16 col]   (v_mfma_f32_16x16x32_bf16)
+// The reference launches one 64-thread block per (sequence, q head), reads
+// each kv head once per q head of its group, and reduces every single q.k over
+// shuffles and two barriers.  Here the G = Hq/Hkv query heads of a group ride
+// in the columns of one MFMA, so each K/V byte is read from HBM exactly once,
+// and the tokens ride in its rows (v_mfma_f32_16x16x32_bf16):
+//
+//   S^T[16 tok][16 col] = K[16 tok][32 d] x Q^T[32 d][16 col]
 //   O^T[16 d][16 col]  += V^T[16 d][32 tok] x P^T[32 tok][16 col]
 //
-// Column c carries q head (c mod G) of the group, so columns repeat when
-// G < 16.  K rows are loaded straight from the page into the A operand with
-// 16-byte loads: lane l takes token l%16 and 16-byte pieces of its head row,
-// so four lanes cover one 128-byte row.  P^T needs no data movement: the
-// 8 probabilities a lane holds after the first MFMA are exactly its B operand
-// of the second one, once the contraction slots are assigned to the tokens
-// that lane already holds.  V^T needs the tokens along the contraction, so the
-// V chunk is staged through LDS (written as loaded, read back column-wise).
+// Column c carries q head (c mod G) of the group (columns repeat when G < 16).
+// K rows go straight from the page into the A operand with 16-byte loads:
+// lane l takes token l%16 and 16-byte pieces of its head row, four lanes per
+// 128-byte row.  P^T needs no data movement: the 8 probabilities a lane holds
+// after the first product are its B operand of the second one.  V^T needs the
+// tokens along the contraction, so V is staged row-major in LDS (16-byte
+// chunks XOR-swizzled per token against bank conflicts) and read back with
+// the gfx950 transposing LDS read, 4 tokens of one d column per read.
 //
-// Each chunk is 32 tokens (two pages).  Loads of chunk c+1 are issued before
-// chunk c is computed, so every wave keeps 8 KB (K+V of two pages for one kv
-// head) in flight while it works.
+// Pipeline.  The loads of a wavefront's next chunk are in flight while its
+// current chunk is computed (two register sets used in turn).  A missing page
+// is never dereferenced: its lanes read page 0 instead and its tokens are
+// masked.
 
 #include "device.h"
 #include "kernels.h"
@@ -35,73 +41,114 @@ namespace pa {
 
 namespace {
 
-constexpr int kChunk = 32;
+constexpr int kChunk = 32;             // tokens per wavefront step (two pages)
+constexpr int kWaves = 8;              // wavefronts per workgroup
+constexpr float kRescaleSlack = 8.f;   // see prefill.hip: lazy max, p <= 2^8
+constexpr float kMaxFloor = -1e30f;
+
+struct DecodeArgs {
+  const uint16_t *q;            // [B][Hq][D]
+  const uint8_t *pool;
+  int64_t n_pages;
+  const int32_t *block_table;
+  const int32_t *slot_ids;
+  const int32_t *ctx_lens;
+  int n_slots, n_layers, mbps, layer;
+  int Hkv;
+  float scale_log2;
+  int max_ctx;
+  int xsplit_tokens;            // tokens per workgroup split of a context
+  int n_xsplits;                // workgroup splits per (sequence, kv head)
+  float *ws_o;                  // [B][Hq][n_xsplits][D] normalised partials (n_xsplits > 1)
+  float *ws_lse;                // [B][Hq][n_xsplits] partial LSE, natural log
+  uint16_t *out;                // [B][Hq][D]
+  float *lse;                   // [B][Hq]
+  int32_t *err;
+};
+
+// max / sum over the four 16-lane rows of a wave (lanes l, l^16, l^32, l^48)
+__device__ __forceinline__ float rows_max(float x) {
+  auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+  auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(q[0]), __uint_as_float(q[1]));
+}
+__device__ __forceinline__ float rows_sum(float x) {
+  auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+  auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(q[0]) + __uint_as_float(q[1]);
+}
 
 template <int D>
-struct ChunkRegs {
-  // [half][piece]: D/32 16-byte pieces per token row per lane
-  uint4 k[2][D / 32];
+struct Chunk {
+  uint4 k[2][D / 32];   // [16-token half][16-byte piece]
   uint4 v[2][D / 32];
+  bool ok[2];           // the half's page exists
 };
+
+// Context length actually used for sequence b (bad lengths and slots are
+// reported once and clamped); the same in both kernels.
+__device__ __forceinline__ int clamped_ctx(const DecodeArgs &a, int b, bool report, int *slot_out) {
+  int ctx = a.ctx_lens[b];
+  const int slot = a.slot_ids ? a.slot_ids[b] : b;
+  const bool slot_ok = slot >= 0 && slot < a.n_slots;
+  if (!slot_ok) {
+    if (report) raise_err(a.err, PA_DEVERR_BAD_SLOT);
+    ctx = 0;
+  }
+  if (ctx < 0 || ctx > a.max_ctx || ctx > a.mbps * kPageTokens) {
+    if (report) raise_err(a.err, PA_DEVERR_BAD_POS);
+    ctx = ctx < 0 ? 0 : min(min(ctx, a.max_ctx), a.mbps * kPageTokens);
+  }
+  *slot_out = slot_ok ? slot : 0;
+  return ctx;
+}
 
 }  // namespace
 
 template <int D, int G>
-__global__ __launch_bounds__(64) void decode_partial_kernel(
-    const uint16_t *__restrict__ q, const uint8_t *__restrict__ pool, int64_t n_pages,
-    const int32_t *__restrict__ block_table, int n_slots, int n_layers, int mbps, int layer,
-    const int32_t *__restrict__ slot_ids, const int32_t *__restrict__ ctx_lens, int Hkv,
-    float scale_log2, int max_ctx, int split_tokens, int n_splits, float *__restrict__ ws_o,
-    float *__restrict__ ws_lse, int32_t *__restrict__ ws_nsplit, uint16_t *__restrict__ out,
-    float *__restrict__ lse_out, int32_t *err) {
+__global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
   static_assert(D % 32 == 0 && 16 % G == 0, "unsupported shape");
   constexpr int P = D / 32;          // 16-byte pieces per lane per token row
-  constexpr int ROW = D + 8;         // LDS row (bf16 elements), padded against bank conflicts
-  __shared__ __attribute__((aligned(16))) uint16_t vlds[kChunk * ROW];
+  constexpr int CH = D / 8;          // 16-byte chunks per V row
+  __shared__ __attribute__((aligned(16))) uint16_t vl[kWaves][kChunk * D];
+  __shared__ float red_o[kWaves][G][D];
+  __shared__ float red_m[kWaves][G];
+  __shared__ float red_l[kWaves][G];
+  // chunk swizzle: the 8 token rows read together by a half-wave land on
+  // 8 distinct 32-byte bank groups
+  auto swz = [](int tok) { return 2 * ((tok / (128 / D)) % (CH / 2)); };
 
-  const int lane = threadIdx.x;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lrow = lane & 15;        // MFMA row/column lane index
   const int lgrp = lane >> 4;        // MFMA k-group / output row group
-  const int split = blockIdx.x % n_splits;
-  const int rest = blockIdx.x / n_splits;
-  const int kvh = rest % Hkv;
-  const int b = rest / Hkv;
-  const int Hq = Hkv * G;
+  const int xs = blockIdx.x % a.n_xsplits;
+  const int rest = blockIdx.x / a.n_xsplits;
+  const int kvh = rest % a.Hkv;
+  const int b = rest / a.Hkv;
+  const int Hq = a.Hkv * G;
 
-  int ctx = ctx_lens[b];
-  const int slot = slot_ids ? slot_ids[b] : b;
-  if (slot < 0 || slot >= n_slots) {
-    if (split == 0 && kvh == 0 && lane == 0) raise_err(err, PA_DEVERR_BAD_SLOT);
-    ctx = 0;
-  }
-  if (ctx < 0 || ctx > max_ctx || ctx > mbps * kPageTokens) {
-    if (split == 0 && kvh == 0 && lane == 0) raise_err(err, PA_DEVERR_BAD_POS);
-    ctx = ctx < 0 ? 0 : min(min(ctx, max_ctx), mbps * kPageTokens);
-  }
-  const int my_splits = ctx == 0 ? 1 : (ctx + split_tokens - 1) / split_tokens;
-  if (split >= my_splits) return;
-  if (split == 0 && kvh == 0 && lane == 0) ws_nsplit[b] = my_splits;
+  int slot;
+  const int ctx = clamped_ctx(a, b, xs == 0 && kvh == 0 && tid == 0, &slot);
+  const int t_begin = xs * a.xsplit_tokens;
+  const int t_end = min(ctx, t_begin + a.xsplit_tokens);
 
-  const int t_begin = split * split_tokens;
-  const int t_end = min(ctx, t_begin + split_tokens);
-
-  PageTable pt;
-  pt.pool = pool;
-  pt.row = block_table + ((int64_t)(slot < 0 || slot >= n_slots ? 0 : slot) * n_layers + layer) * mbps;
-  pt.n_pages = n_pages;
-  pt.page_bytes = 2LL * kPageTokens * Hkv * D * 2;
-  pt.v_offset = pt.page_bytes / 2;
-  pt.mbps = mbps;
-  const int64_t row_bytes = (int64_t)Hkv * D * 2;
-  // byte offset of this lane's pieces inside a page (token lrow, kv head, d-range)
+  const int32_t *trow = a.block_table + ((int64_t)slot * a.n_layers + a.layer) * a.mbps;
+  const int64_t row_bytes = (int64_t)a.Hkv * D * 2;
+  const int64_t page_bytes = row_bytes * 2 * kPageTokens;
+  const int64_t v_offset = page_bytes / 2;
+  // this lane's pieces inside a page: token lrow, kv head, d = lgrp*(D/4) ..
   const int64_t lane_off = (int64_t)lrow * row_bytes + (int64_t)kvh * D * 2 + (int64_t)lgrp * (D / 4) * 2;
 
-  // Q^T as the B operand: column lrow -> q head kvh*G + lrow%G; the lane's
-  // contraction slots hold d = lgrp*(D/4) + piece*8 + i.
+  // Q^T as the B operand: column lrow -> q head kvh*G + lrow%G; contraction
+  // slots hold d = lgrp*(D/4) + piece*8 + i
   bf16x8 qb[P];
   {
     const int hq = kvh * G + (lrow % G);
-    const uint4 *qp = reinterpret_cast<const uint4 *>(q + ((int64_t)b * Hq + hq) * D + lgrp * (D / 4));
+    const uint4 *qp = reinterpret_cast<const uint4 *>(a.q + ((int64_t)b * Hq + hq) * D + lgrp * (D / 4));
 #pragma unroll
     for (int p = 0; p < P; ++p) qb[p] = __builtin_bit_cast(bf16x8, qp[p]);
   }
@@ -109,47 +156,45 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(
   f32x4 acc[D / 16];
 #pragma unroll
   for (int i = 0; i < D / 16; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY;   // running max (log2 units) of this lane's column
+  float m_run = kMaxFloor;   // reference max (log2 units) of this lane's column
   float l_lane = 0.f;        // this lane's share of the column's exp-sum
+  const float c = a.scale_log2;
+  uint16_t *vw = vl[w];
 
-  auto load_chunk = [&](int c0, ChunkRegs<D> &r, bool ok[2]) {
+  auto load = [&](Chunk<D> &r, int c0) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int first = c0 + 16 * h;
       int64_t page = -1;
-      if (first < t_end) {
-        page = pt.page(first / kPageTokens);
-        if (page < 0 && lane == 0) raise_err(err, PA_DEVERR_BAD_PAGE);
+      if (first < t_end) {               // uniform: the same entry for every lane
+        const int32_t e = trow[first / kPageTokens];
+        page = (e < 0 || (int64_t)e >= a.n_pages) ? -1 : (int64_t)e;
+        if (page < 0 && lane == 0) raise_err(a.err, PA_DEVERR_BAD_PAGE);
       }
-      ok[h] = page >= 0;
-      const bool tok_ok = ok[h] && (first + lrow) < t_end;
-      const uint8_t *base = pool + (page < 0 ? 0 : page) * pt.page_bytes + lane_off;
+      r.ok[h] = page >= 0;
+      const uint8_t *base = a.pool + (page < 0 ? 0 : page) * page_bytes + lane_off;
 #pragma unroll
       for (int p = 0; p < P; ++p) {
-        if (tok_ok) {
-          r.k[h][p] = *reinterpret_cast<const uint4 *>(base + p * 16);
-          r.v[h][p] = *reinterpret_cast<const uint4 *>(base + pt.v_offset + p * 16);
-        } else {
-          r.k[h][p] = uint4{0u, 0u, 0u, 0u};
-          r.v[h][p] = uint4{0u, 0u, 0u, 0u};
-        }
+        r.k[h][p] = *reinterpret_cast<const uint4 *>(base + p * 16);
+        r.v[h][p] = *reinterpret_cast<const uint4 *>(base + v_offset + p * 16);
       }
     }
   };
 
-  ChunkRegs<D> cur, nxt;
-  bool ok_cur[2], ok_nxt[2];
-  if (t_begin < t_end) load_chunk(t_begin, cur, ok_cur);
-
-  for (int c0 = t_begin; c0 < t_end; c0 += kChunk) {
-    if (c0 + kChunk < t_end) load_chunk(c0 + kChunk, nxt, ok_nxt);
-
-    // stage V rows in LDS: token (16h + lrow), d = lgrp*(D/4) + p*8 .. +8
+  auto process = [&](const Chunk<D> &r, int c0) {
+    const bool tail = (c0 + kChunk > t_end) | !r.ok[0] | !r.ok[1];
+    // stage V (token 16h + lrow, chunk lgrp*P + p), zero rows that must not count
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
+    for (int h = 0; h < 2; ++h) {
+      const int tok = 16 * h + lrow;
+      const bool keep = !tail || (r.ok[h] && c0 + tok < t_end);
 #pragma unroll
-      for (int p = 0; p < P; ++p)
-        *reinterpret_cast<uint4 *>(&vlds[(16 * h + lrow) * ROW + lgrp * (D / 4) + p * 8]) = cur.v[h][p];
+      for (int p = 0; p < P; ++p) {
+        const int ch = lgrp * P + p;
+        *reinterpret_cast<uint4 *>(&vw[tok * D + (ch ^ swz(tok)) * 8]) =
+            keep ? r.v[h][p] : uint4{0u, 0u, 0u, 0u};
+      }
+    }
 
     // S^T = K Q^T for the two 16-token halves
     f32x4 s[2];
@@ -157,174 +202,190 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(
     for (int h = 0; h < 2; ++h) {
       s[h] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int p = 0; p < P; ++p) s[h] = mfma16(__builtin_bit_cast(bf16x8, cur.k[h][p]), qb[p], s[h]);
+      for (int p = 0; p < P; ++p) s[h] = mfma16(__builtin_bit_cast(bf16x8, r.k[h][p]), qb[p], s[h]);
     }
-
-    // online softmax over the chunk (log2 domain); the lane holds tokens
-    // 16h + 4*lgrp + r of column lrow
-    float x[8];
-    float cmax = -INFINITY;
+    // the lane holds tokens c0 + 16h + 4*lgrp + i of its column
+    if (tail) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const bool vis = r.ok[h] && (c0 + 16 * h + 4 * lgrp + i) < t_end;
+          s[h][i] = vis ? s[h][i] : -INFINITY;
+        }
+    }
+    float cmax = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
+                       fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
+    cmax = rows_max(cmax);
+    const float mt = cmax * c;
+    if (__any(mt > m_run + kRescaleSlack)) {
+      const float m_new = fmaxf(m_run, mt);
+      const float corr = fast_exp2(m_run - m_new);
+      m_run = m_new;
+      l_lane *= corr;
+#pragma unroll
+      for (int mb = 0; mb < D / 16; ++mb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[mb][i] *= corr;
+    }
+    bf16x8 pb;
+    float psum = 0.f;
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int t = c0 + 16 * h + 4 * lgrp + r;
-        const bool valid = ok_cur[h] && t < t_end;
-        const float v = valid ? s[h][r] * scale_log2 : -INFINITY;
-        x[4 * h + r] = v;
-        cmax = fmaxf(cmax, v);
+      for (int i = 0; i < 4; ++i) {
+        const float p = fast_exp2(__builtin_fmaf(s[h][i], c, -m_run));
+        psum += p;
+        pb[4 * h + i] = (__bf16)p;
       }
-    cmax = fmaxf(cmax, __shfl_xor(cmax, 16));
-    cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
-    const float m_new = fmaxf(m_run, cmax);
-    const bool live = m_new != -INFINITY;
-    const float corr = live ? fast_exp2(m_run - m_new) : 1.f;
-    m_run = m_new;
-    float psum = 0.f;
-    bf16x8 pb;
+    l_lane += psum;
+
+    // O^T += V^T P^T.  Contraction slot lgrp*8 + 4*half + k is token
+    // 16*half + 4*lgrp + k; one transposing read per half: lane lrow points at
+    // V[16*half + 4*lgrp + lrow/4][16*mb + 4*(lrow%4)] and receives
+    // V[16*half + 4*lgrp + k][16*mb + lrow], k = 0..3.
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float p = live ? fast_exp2(x[i] - m_new) : 0.f;
-      psum += p;
-      pb[i] = (__bf16)p;
+    for (int mb = 0; mb < D / 16; ++mb) {
+      uint2 part[2];
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const int tok = 16 * half + 4 * lgrp + (lrow >> 2);
+        const int d = 16 * mb + 4 * (lrow & 3);
+        const uint16_t *src = &vw[tok * D + ((d / 8) ^ swz(tok)) * 8 + (d % 8)];
+        part[half] = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                                   (__attribute__((address_space(3))) i16x4 *)(src)));
+      }
+      const bf16x8 va = __builtin_bit_cast(bf16x8, uint4{part[0].x, part[0].y, part[1].x, part[1].y});
+      acc[mb] = mfma16(va, pb, acc[mb]);
     }
-    l_lane = l_lane * corr + psum;
+  };
+
+  // this wavefront's chunks: t_begin + (w + kWaves*i) * kChunk
+  const int stride = kWaves * kChunk;
+  Chunk<D> ca, cb;
+  int c0 = t_begin + w * kChunk;
+  if (c0 < t_end) load(ca, c0);
+  for (; c0 < t_end; c0 += 2 * stride) {
+    if (c0 + stride < t_end) load(cb, c0 + stride);
+    process(ca, c0);
+    if (c0 + stride >= t_end) break;
+    if (c0 + 2 * stride < t_end) load(ca, c0 + 2 * stride);
+    process(cb, c0 + stride);
+  }
+
+  // ---- merge the wavefronts: unnormalised outputs, maxima and sums via LDS
+  const float l_tot = rows_sum(l_lane);
+  if (lrow < G) {
 #pragma unroll
     for (int mb = 0; mb < D / 16; ++mb)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) acc[mb][r] *= corr;
-
-    __syncthreads();
-    // O^T += V^T P^T; contraction slot (lgrp*8 + i) is token 16*(i/4) + 4*lgrp + i%4
-#pragma unroll
-    for (int mb = 0; mb < D / 16; ++mb) {
-      bf16x8 va;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int t = 16 * (i / 4) + 4 * lgrp + (i % 4);
-        va[i] = __builtin_bit_cast(__bf16, vlds[t * ROW + mb * 16 + lrow]);
-      }
-      acc[mb] = mfma16(va, pb, acc[mb]);
-    }
-    __syncthreads();
-
-    if (c0 + kChunk < t_end) {
-      cur = nxt;
-      ok_cur[0] = ok_nxt[0];
-      ok_cur[1] = ok_nxt[1];
+      for (int i = 0; i < 4; ++i) red_o[w][lrow][mb * 16 + 4 * lgrp + i] = acc[mb][i];
+    if (lgrp == 0) {
+      red_m[w][lrow] = m_run;
+      red_l[w][lrow] = l_tot;
     }
   }
-
-  // column totals: the four lane groups hold disjoint tokens of the column
-  float l_tot = l_lane + __shfl_xor(l_lane, 16);
-  l_tot += __shfl_xor(l_tot, 32);
-  const bool empty = !(l_tot > 0.f);
-  const float inv_l = empty ? 0.f : 1.f / l_tot;
-  const float lse = empty ? -INFINITY : (m_run + fast_log2(l_tot)) * kLn2;
-
-  if (lrow < G) {
-    const int hq = kvh * G + lrow;
-    const int64_t bh = (int64_t)b * Hq + hq;
-    if (my_splits == 1) {
+  __syncthreads();
+  for (int idx = tid; idx < G * D; idx += 64 * kWaves) {
+    const int j = idx / D;
+    const int d = idx % D;
+    float M = kMaxFloor;
 #pragma unroll
-      for (int mb = 0; mb < D / 16; ++mb) {
-        uint2 w;
-        w.x = pack_bf16x2(acc[mb][0] * inv_l, acc[mb][1] * inv_l);
-        w.y = pack_bf16x2(acc[mb][2] * inv_l, acc[mb][3] * inv_l);
-        *reinterpret_cast<uint2 *>(out + bh * D + mb * 16 + 4 * lgrp) = w;
-      }
-      if (lgrp == 0) lse_out[bh] = lse;
+    for (int v = 0; v < kWaves; ++v) M = fmaxf(M, red_m[v][j]);
+    float o = 0.f, L = 0.f;
+#pragma unroll
+    for (int v = 0; v < kWaves; ++v) {
+      const float sc = fast_exp2(red_m[v][j] - M);
+      o += sc * red_o[v][j][d];
+      L += sc * red_l[v][j];
+    }
+    const bool empty = !(L > 0.f);
+    const float val = empty ? 0.f : o / L;
+    const float lse_v = empty ? -INFINITY : (M + fast_log2(L)) * kLn2;
+    const int64_t bh = (int64_t)b * Hq + kvh * G + j;
+    if (a.n_xsplits == 1) {
+      a.out[bh * D + d] = f32_to_bf16(val);
+      if (d == 0) a.lse[bh] = lse_v;
     } else {
-      float *dst = ws_o + (bh * n_splits + split) * D;
-#pragma unroll
-      for (int mb = 0; mb < D / 16; ++mb)
-        *reinterpret_cast<float4 *>(dst + mb * 16 + 4 * lgrp) =
-            float4{acc[mb][0] * inv_l, acc[mb][1] * inv_l, acc[mb][2] * inv_l, acc[mb][3] * inv_l};
-      if (lgrp == 0) ws_lse[bh * n_splits + split] = lse;
+      a.ws_o[(bh * a.n_xsplits + xs) * D + d] = val;
+      if (d == 0) a.ws_lse[bh * a.n_xsplits + xs] = lse_v;
     }
   }
 }
 
-// Merge the split partials of one (sequence, q head): O = sum_i w_i O_i / sum_i w_i,
-// w_i = exp(LSE_i - max LSE), LSE = max + ln(sum_i w_i).
+// Merge the workgroup splits of one (sequence, q head): O = sum_i w_i O_i /
+// sum_i w_i with w_i = exp(LSE_i - max LSE), LSE = max + ln(sum_i w_i).
+// Splits past the end of a context hold LSE = -inf and weigh nothing.
 template <int D>
-__global__ __launch_bounds__(64) void decode_combine_kernel(
-    const float *__restrict__ ws_o, const float *__restrict__ ws_lse,
-    const int32_t *__restrict__ ws_nsplit, int Hq, int n_splits, uint16_t *__restrict__ out,
-    float *__restrict__ lse_out) {
+__global__ __launch_bounds__(64) void decode_combine_kernel(DecodeArgs a, int Hq) {
   const int64_t bh = blockIdx.x;
-  const int b = (int)(bh / Hq);
-  const int n = ws_nsplit[b];
-  if (n <= 1) return;
   const int lane = threadIdx.x;
-  const float *lp = ws_lse + bh * n_splits;
+  const float *lp = a.ws_lse + bh * a.n_xsplits;
   float M = -INFINITY;
-  for (int i = 0; i < n; ++i) M = fmaxf(M, lp[i]);
+  for (int i = 0; i < a.n_xsplits; ++i) M = fmaxf(M, lp[i]);
   constexpr int E = D / 64;
   float o[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) o[e] = 0.f;
   float L = 0.f;
   if (M != -INFINITY) {
-    for (int i = 0; i < n; ++i) {
-      const float w = fast_exp2((lp[i] - M) * kLog2e);
-      L += w;
-      const float *op = ws_o + (bh * n_splits + i) * D;
+    for (int i = 0; i < a.n_xsplits; ++i) {
+      const float wgt = fast_exp2((lp[i] - M) * kLog2e);
+      L += wgt;
+      const float *op = a.ws_o + (bh * a.n_xsplits + i) * D;
 #pragma unroll
-      for (int e = 0; e < E; ++e) o[e] += w * op[lane + 64 * e];
+      for (int e = 0; e < E; ++e) o[e] += wgt * op[lane + 64 * e];
     }
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
 #pragma unroll
-  for (int e = 0; e < E; ++e) out[bh * D + lane + 64 * e] = f32_to_bf16(o[e] * inv);
-  if (lane == 0) lse_out[bh] = L > 0.f ? M + fast_log2(L) * kLn2 : -INFINITY;
+  for (int e = 0; e < E; ++e) a.out[bh * D + lane + 64 * e] = f32_to_bf16(o[e] * inv);
+  if (lane == 0) a.lse[bh] = L > 0.f ? M + fast_log2(L) * kLn2 : -INFINITY;
 }
 
-int decode_split_tokens(int B, int max_ctx) {
-  // Aim for a few thousand wavefronts over the batch; 32-token multiples.
-  int64_t s = ((int64_t)B * max_ctx) / 512;
-  s = (s + kChunk - 1) / kChunk * kChunk;
-  if (s < 64) s = 64;
-  if (s > 512) s = 512;
-  return (int)s;
-}
-
-size_t decode_workspace_bytes(int B, int Hq, int D, int max_ctx) {
-  const int split = decode_split_tokens(B, max_ctx);
-  const int64_t n_splits = max_ctx <= 0 ? 1 : (max_ctx + split - 1) / split;
-  const int64_t o = (int64_t)B * Hq * n_splits * D * 4;
-  const int64_t l = (int64_t)B * Hq * n_splits * 4;
-  const int64_t n = (int64_t)B * 4;
+namespace {
+struct Split {
+  int tokens, n;                // tokens per workgroup split, splits per context
+  int64_t o_bytes, lse_bytes;   // workspace parts (zero when n == 1)
+};
+Split split_policy(int B, int Hq, int Hkv, int D, int max_ctx) {
+  // Aim for about 4096 wavefronts in flight: split a context across
+  // workgroups only when B * Hkv workgroups of kWaves waves fall short, and
+  // never below 2 chunks per wavefront.
   auto up = [](int64_t x) { return (x + 255) / 256 * 256; };
-  return (size_t)(up(o) + up(l) + up(n));
+  Split s{};
+  const int64_t groups = (int64_t)B * Hkv;
+  int64_t n = (4096 + groups * kWaves - 1) / (groups * kWaves);
+  const int64_t min_tokens = 2LL * kWaves * kChunk;
+  const int64_t n_max = max_ctx <= 0 ? 1 : (max_ctx + min_tokens - 1) / min_tokens;
+  if (n > n_max) n = n_max;
+  if (n < 1) n = 1;
+  int64_t t = max_ctx <= 0 ? kChunk : (max_ctx + n - 1) / n;
+  t = (t + kChunk - 1) / kChunk * kChunk;
+  s.tokens = (int)t;
+  s.n = max_ctx <= 0 ? 1 : (int)((max_ctx + t - 1) / t);
+  if (s.n > 1) {
+    s.o_bytes = up((int64_t)B * Hq * s.n * D * 4);
+    s.lse_bytes = up((int64_t)B * Hq * s.n * 4);
+  }
+  return s;
+}
+}  // namespace
+
+size_t decode_workspace_bytes(int B, int Hq, int Hkv, int D, int max_ctx) {
+  const Split s = split_policy(B, Hq, Hkv, D, max_ctx);
+  return (size_t)(s.o_bytes + s.lse_bytes);
 }
 
 template <int D, int G>
-static int launch_decode_t(const void *q, const void *kv_cache, int64_t n_pages,
-                           const int32_t *block_table, int n_slots, int n_layers, int mbps,
-                           int layer, const int32_t *slot_ids, const int32_t *ctx_lens, int B,
-                           int Hkv, float scale, int max_ctx, void *workspace, void *O, float *LSE,
-                           int32_t *err, hipStream_t stream) {
-  const int Hq = Hkv * G;
-  const int split = decode_split_tokens(B, max_ctx);
-  const int n_splits = max_ctx <= 0 ? 1 : (max_ctx + split - 1) / split;
-  auto up = [](int64_t x) { return (x + 255) / 256 * 256; };
-  uint8_t *ws = static_cast<uint8_t *>(workspace);
-  float *ws_o = reinterpret_cast<float *>(ws);
-  float *ws_lse = reinterpret_cast<float *>(ws + up((int64_t)B * Hq * n_splits * D * 4));
-  int32_t *ws_n = reinterpret_cast<int32_t *>(ws + up((int64_t)B * Hq * n_splits * D * 4) +
-                                              up((int64_t)B * Hq * n_splits * 4));
-  const int64_t grid = (int64_t)B * Hkv * n_splits;
+static int launch_decode_t(DecodeArgs a, int B, hipStream_t stream) {
+  const int64_t grid = (int64_t)B * a.Hkv * a.n_xsplits;
   if (grid > 0x7fffffff) return PA_ERR_RANGE;
-  hipLaunchKernelGGL((decode_partial_kernel<D, G>), dim3((unsigned)grid), dim3(64), 0, stream,
-                     static_cast<const uint16_t *>(q), static_cast<const uint8_t *>(kv_cache),
-                     n_pages, block_table, n_slots, n_layers, mbps, layer, slot_ids, ctx_lens, Hkv,
-                     scale * kLog2e, max_ctx, split, n_splits, ws_o, ws_lse, ws_n,
-                     static_cast<uint16_t *>(O), LSE, err);
+  hipLaunchKernelGGL((decode_kernel<D, G>), dim3((unsigned)grid), dim3(64 * kWaves), 0, stream, a);
   if (hipGetLastError() != hipSuccess) return PA_ERR_LAUNCH;
-  if (n_splits > 1) {
-    hipLaunchKernelGGL((decode_combine_kernel<D>), dim3((unsigned)(B * Hq)), dim3(64), 0, stream,
-                       ws_o, ws_lse, ws_n, Hq, n_splits, static_cast<uint16_t *>(O), LSE);
+  if (a.n_xsplits > 1) {
+    hipLaunchKernelGGL((decode_combine_kernel<D>), dim3((unsigned)(B * a.Hkv * G)), dim3(64), 0,
+                       stream, a, a.Hkv * G);
     if (hipGetLastError() != hipSuccess) return PA_ERR_LAUNCH;
   }
   return PA_OK;
@@ -334,12 +395,32 @@ int launch_decode(const void *q, const void *kv_cache, int64_t n_pages, const in
                   int n_slots, int n_layers, int mbps, int layer, const int32_t *slot_ids,
                   const int32_t *ctx_lens, int B, int Hq, int Hkv, int D, float scale, int max_ctx,
                   void *workspace, void *O, float *LSE, int32_t *err, hipStream_t stream) {
+  const Split s = split_policy(B, Hq, Hkv, D, max_ctx);
+  uint8_t *ws = static_cast<uint8_t *>(workspace);
+  DecodeArgs a{};
+  a.q = static_cast<const uint16_t *>(q);
+  a.pool = static_cast<const uint8_t *>(kv_cache);
+  a.n_pages = n_pages;
+  a.block_table = block_table;
+  a.slot_ids = slot_ids;
+  a.ctx_lens = ctx_lens;
+  a.n_slots = n_slots;
+  a.n_layers = n_layers;
+  a.mbps = mbps;
+  a.layer = layer;
+  a.Hkv = Hkv;
+  a.scale_log2 = scale * kLog2e;
+  a.max_ctx = max_ctx;
+  a.xsplit_tokens = s.tokens;
+  a.n_xsplits = s.n;
+  a.ws_o = s.n > 1 ? reinterpret_cast<float *>(ws) : nullptr;
+  a.ws_lse = s.n > 1 ? reinterpret_cast<float *>(ws + s.o_bytes) : nullptr;
+  a.out = static_cast<uint16_t *>(O);
+  a.lse = LSE;
+  a.err = err;
   const int G = Hq / Hkv;
-#define PA_DECODE_CASE(DD, GG)                                                                  \
-  if (D == DD && G == GG)                                                                       \
-    return launch_decode_t<DD, GG>(q, kv_cache, n_pages, block_table, n_slots, n_layers, mbps,  \
-                                   layer, slot_ids, ctx_lens, B, Hkv, scale, max_ctx, workspace, \
-                                   O, LSE, err, stream);
+#define PA_DECODE_CASE(DD, GG) \
+  if (D == DD && G == GG) return launch_decode_t<DD, GG>(a, B, stream);
   PA_DECODE_CASE(64, 1)
   PA_DECODE_CASE(64, 2)
   PA_DECODE_CASE(64, 4)

@@ -21,8 +21,7 @@ int launch_prefill_paged(const void *q, const void *kv_cache, int64_t n_pages,
 int launch_prefill_dense(const void *q, const void *k, const void *v, int B, int T, int Hq, int Hkv,
                          int D, float scale, int causal, void *O, float *LSE, hipStream_t stream);
 
-int decode_split_tokens(int B, int max_ctx);
-size_t decode_workspace_bytes(int B, int Hq, int D, int max_ctx);
+size_t decode_workspace_bytes(int B, int Hq, int Hkv, int D, int max_ctx);
 
 int launch_decode(const void *q, const void *kv_cache, int64_t n_pages, const int32_t *block_table,
                   int n_slots, int n_layers, int mbps, int layer, const int32_t *slot_ids,

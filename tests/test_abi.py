@@ -42,8 +42,11 @@ def test_page_bytes_and_status_strings():
 
 
 def test_decode_workspace_size():
-    assert pa.decode_workspace_size(64, 32, 64, 2048) > 64 * 32 * 64 * 4
-    assert pa.decode_workspace_size(0, 32, 64, 2048) == 0
+    # a batch that fills the GPU needs no cross-workgroup partials
+    assert pa.decode_workspace_size(64, 32, 8, 64, 2048) == 0
+    # a few long contexts are split across workgroups: O and LSE partials
+    assert pa.decode_workspace_size(4, 32, 8, 64, 16384) >= 4 * 32 * 2 * (64 + 1) * 4
+    assert pa.decode_workspace_size(0, 32, 8, 64, 2048) == 0
 
 
 P = ctypes.c_void_p
@@ -74,9 +77,11 @@ def test_host_checks_reject_bad_arguments():
     # group size without a decode kernel
     assert lib.attn_decode(good, good, 64, good, 1, 1, 128, 0, None, good, 1, 96, 3, 64, 0.125,
                            64, good, 1 << 20, good, good, None, None) == -3
-    # workspace too small
-    assert lib.attn_decode(good, good, 64, good, 1, 1, 128, 0, None, good, 64, 32, 8, 64, 0.125,
-                           2048, good, 16, good, good, None, None) == -5
+    # workspace too small (4 long contexts are split across workgroups)
+    assert lib.attn_decode(good, good, 64, good, 4, 1, 1024, 0, None, good, 4, 32, 8, 64, 0.125,
+                           16384, good, 16, good, good, None, None) == -5
+    assert lib.attn_decode(good, good, 64, good, 4, 1, 1024, 0, None, good, 4, 32, 8, 64, 0.125,
+                           16384, None, 0, good, good, None, None) == -1
     # page count overflow of int32 page ids
     assert lib.kv_scatter(good, good, 1, good, good, good, 1 << 31, good, 1, 1, 128, 0, 8, 64,
                           None, None) == -6
