@@ -37,13 +37,15 @@ def compile_flags() -> list[str]:
             "-Wall", "-Wno-unused-function", f"-I{INCLUDE}", f"-I{CSRC}"]
 
 
-def build(verbose: bool = False, jobs: int = 4) -> str:
-    os.makedirs(BUILD, exist_ok=True)
+def build(verbose: bool = False, jobs: int = 4, out: str = LIB, defines=(), build_dir: str = BUILD) -> str:
+    """Compile every source and link `out`; `defines` are extra -D tunables."""
+    os.makedirs(build_dir, exist_ok=True)
     cc = hipcc()
+    extra = [f"-D{d}" for d in defines]
 
     def one(src: str) -> str:
-        obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-        cmd = [cc, *compile_flags(), "-c", os.path.join(CSRC, src), "-o", obj]
+        obj = os.path.join(build_dir, os.path.splitext(src)[0] + ".o")
+        cmd = [cc, *compile_flags(), *extra, "-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         r = subprocess.run(cmd, capture_output=True, text=True)
@@ -53,13 +55,13 @@ def build(verbose: bool = False, jobs: int = 4) -> str:
 
     with ThreadPoolExecutor(max_workers=jobs) as ex:
         objs = list(ex.map(one, SOURCES))
-    tmp = LIB + ".tmp"
+    tmp = out + ".tmp"
     cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

@@ -42,7 +42,13 @@ namespace pa {
 namespace {
 
 constexpr int kChunk = 32;             // tokens per wavefront step (two pages)
-constexpr int kWaves = 8;              // wavefronts per workgroup
+#ifndef PA_DECODE_WAVES
+#define PA_DECODE_WAVES 8
+#endif
+#ifndef PA_DECODE_MIN_WAVES_PER_SIMD
+#define PA_DECODE_MIN_WAVES_PER_SIMD 2
+#endif
+constexpr int kWaves = PA_DECODE_WAVES;  // wavefronts per workgroup
 constexpr float kRescaleSlack = 8.f;   // see prefill.hip: lazy max, p <= 2^8
 constexpr float kMaxFloor = -1e30f;
 
@@ -87,28 +93,28 @@ struct Chunk {
   bool ok[2];           // the half's page exists
 };
 
-// Context length actually used for sequence b (bad lengths and slots are
-// reported once and clamped); the same in both kernels.
-__device__ __forceinline__ int clamped_ctx(const DecodeArgs &a, int b, bool report, int *slot_out) {
+// Context length actually used for sequence b: bad lengths and slots are
+// clamped and their error bits returned through *err_bits.
+__device__ __forceinline__ int clamped_ctx(const DecodeArgs &a, int b, int *slot_out, int *err_bits) {
   int ctx = a.ctx_lens[b];
   const int slot = a.slot_ids ? a.slot_ids[b] : b;
   const bool slot_ok = slot >= 0 && slot < a.n_slots;
   if (!slot_ok) {
-    if (report) raise_err(a.err, PA_DEVERR_BAD_SLOT);
+    *err_bits |= PA_DEVERR_BAD_SLOT;
     ctx = 0;
   }
   if (ctx < 0 || ctx > a.max_ctx || ctx > a.mbps * kPageTokens) {
-    if (report) raise_err(a.err, PA_DEVERR_BAD_POS);
+    *err_bits |= PA_DEVERR_BAD_POS;
     ctx = ctx < 0 ? 0 : min(min(ctx, a.max_ctx), a.mbps * kPageTokens);
   }
-  *slot_out = slot_ok ? slot : 0;
-  return ctx;
+  *slot_out = uniform(slot_ok ? slot : 0);
+  return uniform(ctx);
 }
 
 }  // namespace
 
 template <int D, int G>
-__global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(64 * kWaves, PA_DECODE_MIN_WAVES_PER_SIMD) void decode_kernel(DecodeArgs a) {
   static_assert(D % 32 == 0 && 16 % G == 0, "unsupported shape");
   constexpr int P = D / 32;          // 16-byte pieces per lane per token row
   constexpr int CH = D / 8;          // 16-byte chunks per V row
@@ -131,8 +137,13 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
   const int b = rest / a.Hkv;
   const int Hq = a.Hkv * G;
 
+  // Errors are collected here and reported once at the end: a global atomic
+  // before the chunk loop would make the compiler treat the block table as
+  // possibly clobbered and keep its (uniform) reads off the scalar unit.
+  int err_bits = 0;
   int slot;
-  const int ctx = clamped_ctx(a, b, xs == 0 && kvh == 0 && tid == 0, &slot);
+  const int ctx = clamped_ctx(a, b, &slot, &err_bits);
+  if (xs != 0 || kvh != 0) err_bits = 0;     // one workgroup per sequence reports these
   const int t_begin = xs * a.xsplit_tokens;
   const int t_end = min(ctx, t_begin + a.xsplit_tokens);
 
@@ -167,9 +178,9 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
       const int first = c0 + 16 * h;
       int64_t page = -1;
       if (first < t_end) {               // uniform: the same entry for every lane
-        const int32_t e = trow[first / kPageTokens];
+        const int32_t e = trow[uniform(first / kPageTokens)];
         page = (e < 0 || (int64_t)e >= a.n_pages) ? -1 : (int64_t)e;
-        if (page < 0 && lane == 0) raise_err(a.err, PA_DEVERR_BAD_PAGE);
+        if (page < 0) err_bits |= PA_DEVERR_BAD_PAGE;
       }
       r.ok[h] = page >= 0;
       const uint8_t *base = a.pool + (page < 0 ? 0 : page) * page_bytes + lane_off;
@@ -272,6 +283,8 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
     if (c0 + 2 * stride < t_end) load(ca, c0 + 2 * stride);
     process(cb, c0 + stride);
   }
+
+  if (err_bits && lane == 0) raise_err(a.err, err_bits);
 
   // ---- merge the wavefronts: unnormalised outputs, maxima and sums via LDS
   const float l_tot = rows_sum(l_lane);

@@ -122,26 +122,32 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
   const int T = a.T;
 
   int len = T;
+  // Errors are collected here and reported once at the end: a global atomic
+  // before the key loop would make the compiler treat the block table as
+  // possibly clobbered and keep its (uniform) reads off the scalar unit.
+  int err_bits = 0;
   // paged source of this sequence: table row and page geometry
   const int32_t *trow = nullptr;
   const int64_t page_bytes = 2LL * kPageTokens * a.Hkv * D * 2;
   const int64_t v_offset = page_bytes / 2;
   if constexpr (PAGED) {
+    const bool reporter = hg == 0 && rb == 0;   // one workgroup per sequence reports
     len = a.seq_lens[b];
     if (len < 0 || len > T) {
-      if (tid == 0 && hg == 0 && rb == 0) raise_err(a.err, PA_DEVERR_BAD_POS);
+      if (reporter) err_bits |= PA_DEVERR_BAD_POS;
       len = len < 0 ? 0 : T;
     }
     const int slot = a.slot_ids ? a.slot_ids[b] : b;
     if (slot < 0 || slot >= a.n_slots) {
-      if (tid == 0 && hg == 0 && rb == 0) raise_err(a.err, PA_DEVERR_BAD_SLOT);
+      if (reporter) err_bits |= PA_DEVERR_BAD_SLOT;
       len = 0;
     }
     if (len > a.mbps * kPageTokens) {
-      if (tid == 0 && hg == 0 && rb == 0) raise_err(a.err, PA_DEVERR_BAD_POS);
+      if (reporter) err_bits |= PA_DEVERR_BAD_POS;
       len = a.mbps * kPageTokens;
     }
-    trow = a.block_table + ((int64_t)(len > 0 ? slot : 0) * a.n_layers + a.layer) * a.mbps;
+    len = uniform(len);
+    trow = a.block_table + ((int64_t)uniform(len > 0 ? slot : 0) * a.n_layers + a.layer) * a.mbps;
   }
 
   const int row = row0 + lr;
@@ -174,6 +180,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
   // ---- physical page of logical block blk, -1 when missing.  Every lane of
   // a wave asks for the same block, so this is a scalar load.
   auto page_of = [&](int blk) -> int64_t {
+    blk = uniform(blk);
     if (blk * kPageTokens >= kv_end || blk >= a.mbps) return -1;
     const int32_t v = trow[blk];
     return (v < 0 || (int64_t)v >= a.n_pages) ? -1 : (int64_t)v;
@@ -238,7 +245,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
         const int blk = kv0 / kPageTokens + p;
         if (blk * kPageTokens < kv_end && page_of(blk) < 0) bad_pages |= 1u << p;
       }
-      if (bad_pages && tid == 0) raise_err(a.err, PA_DEVERR_BAD_PAGE);
+      if (bad_pages) err_bits |= PA_DEVERR_BAD_PAGE;
     }
 
     // a wave whose rows all precede this tile sees none of it (causal)
@@ -344,6 +351,8 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
     }
     __syncthreads();
   }
+
+  if (err_bits && tid == 0) raise_err(a.err, err_bits);
 
   // ---- epilogue: one divide per row, LSE in natural-log units
   float l_row = l_lane + __shfl_xor(l_lane, 32);
