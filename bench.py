@@ -23,6 +23,7 @@ workload on the host cores.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -56,27 +57,75 @@ def prefill_flops(B: int, T: int, Hq: int, d: int, causal: bool) -> float:
     return f / 2 if causal else f
 
 
-def time_launches(fn, n: int) -> float:
-    """Mean device time (s) of one fn() call, from an event pair around each call."""
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
-    for s, e in ev:
-        s.record()
-        fn()
-        e.record()
+def capture(fn, reps: int = 1) -> torch.cuda.CUDAGraph:
+    """A HIP graph holding `reps` back-to-back calls of fn (its kernels only)."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()                                   # warm the path once outside the graph
+    torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
-    return float(np.mean([s.elapsed_time(e) for s, e in ev])) / 1e3
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(reps):
+            fn()
+    torch.cuda.synchronize()
+    return g
 
 
-def timed_steps(step, steps: int, warmup: int) -> float:
-    """Wall time (s) of `steps` steps after `warmup`, bracketed by device syncs."""
+def kernel_time(fn, reps: int = 20, trials: int = 5) -> float:
+    """Mean device time (s) of one call of fn: a graph of `reps` back-to-back
+    calls is replayed between two HIP events on the launching stream; the
+    best of `trials` replays is kept."""
+    g = capture(fn, reps)
+    best = float("inf")
+    for _ in range(trials):
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        g.replay()
+        e.record()
+        torch.cuda.synchronize()
+        best = min(best, s.elapsed_time(e) / 1e3 / reps)
+    return best
+
+
+def timed_steps(graphs, steps: int, warmup: int) -> float:
+    """Wall time (s) of `steps` graph-replayed steps after `warmup`, bracketed
+    by device syncs; step i replays graphs[i % len(graphs)]."""
     for i in range(warmup):
-        step(i)
+        graphs[i % len(graphs)].replay()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
-        step(i)
+        graphs[i % len(graphs)].replay()
     torch.cuda.synchronize()
     return time.perf_counter() - t0
+
+
+def source_digest(*names: str) -> str:
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "paged_kv_cache_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+# HBM traffic per launch measured with rocprofv3 --pmc FETCH_SIZE and
+# WRITE_SIZE (separate runs), scaled by the factor a plain copy kernel of
+# known size reads on the same counters; valid only for the kernel source it
+# was taken on (digest of the .hip files), null otherwise.
+TRAFFIC = {
+    # kernel: (source digest, fetched bytes, written bytes)
+    "prefill": ("d26f8685317684ef", 25323131, 17301504),
+    "decode": ("64158c1b145b3a25", 152454348, 278528),
+}
+
+
+def traffic_of(kernel: str, digest: str):
+    t = TRAFFIC.get(kernel)
+    if not t or t[0] != digest:
+        return None
+    return t[1] + t[2]
 
 
 # ----------------------------------------------------------------- prefill
@@ -103,15 +152,21 @@ def bench_prefill(steps: int, warmup: int):
         pa.attn_prefill(q, pool, bt, c.layer, lens, c.n_kv_heads, case.scale, True, slot_ids=sid,
                         out=O, lse=L)
 
-    def step(_):
+    def step():
         scatter()
         prefill()
 
-    wall = timed_steps(step, steps, warmup)
+    # eager reference result, then the graph of one step must reproduce it
+    step()
+    torch.cuda.synchronize()
+    O_ref, L_ref = O.clone(), L.clone()
+    g = capture(step)
+    wall = timed_steps([g], steps, warmup)
+    assert torch.equal(O, O_ref) and torch.equal(L, L_ref), "graph replay differs from eager"
     flops = prefill_flops(case.B, case.T, case.Hq, case.d, True)
-    t_kernel = time_launches(prefill, max(steps, 20))
-    t_scatter = time_launches(scatter, max(steps, 20))
-    return dict(case=case, wall=wall, flops=flops, t_kernel=t_kernel, t_scatter=t_scatter)
+    alg_bytes = (q.numel() + O.numel()) * 2 + L.numel() * 4 + 2 * k.numel() * 2
+    return dict(case=case, wall=wall, flops=flops, t_kernel=kernel_time(prefill),
+                t_scatter=kernel_time(scatter), alg_bytes=alg_bytes)
 
 
 # ------------------------------------------------------------------ decode
@@ -150,22 +205,27 @@ def bench_decode(steps: int, warmup: int, replicas: int = 8):
     L = torch.empty(case.B, case.Hq, dtype=torch.float32, device=DEV)
 
     def scatter(r):
-        pa.kv_scatter(new_k, new_v, new_s, new_p, pool, tables[r % replicas], c.layer)
+        pa.kv_scatter(new_k, new_v, new_s, new_p, pool, tables[r], c.layer)
 
     def decode(r):
-        pa.attn_decode(q, pool, tables[r % replicas], c.layer, lens, c.n_kv_heads, case.scale,
+        pa.attn_decode(q, pool, tables[r], c.layer, lens, c.n_kv_heads, case.scale,
                        max_ctx, slot_ids=sid, workspace=ws, out=O, lse=L)
 
-    def step(i):
-        scatter(i)
-        decode(i)
+    def step(r):
+        scatter(r)
+        decode(r)
 
-    wall = timed_steps(step, steps, warmup)
+    step(0)
+    torch.cuda.synchronize()
+    O_ref, L_ref = O.clone(), L.clone()
+    graphs = [capture(lambda r=r: step(r)) for r in range(replicas)]
+    wall = timed_steps(graphs, steps, warmup)
+    assert torch.equal(O, O_ref) and torch.equal(L, L_ref), "graph replay differs from eager"
     n_ctx = int(case.ctx_lens.sum())
     kv_bytes = n_ctx * c.n_kv_heads * case.d * 2 * 2
     io_bytes = q.numel() * 2 + O.numel() * 2 + L.numel() * 4 + int(np.ceil(case.ctx_lens / 16).sum()) * 4
-    counter = iter(range(10**9))
-    t_kernel = time_launches(lambda: decode(next(counter)), max(steps, 40))
+    # one launch per replica in turn: the KV of a launch is never the previous one's
+    t_kernel = kernel_time(lambda: [decode(r) for r in range(replicas)], reps=4) / replicas
     return dict(case=case, wall=wall, kv_bytes=kv_bytes, io_bytes=io_bytes, t_kernel=t_kernel,
                 replicas=replicas, n_ctx=n_ctx)
 
@@ -176,13 +236,16 @@ def cpu_prefill_baseline(case):
     import oracle
     pool = oracle.pool_for(case)
     oracle.scatter_tokens(pool, case.cache, case.tokens)
+    reps = 0
     t0 = time.perf_counter()
-    oracle.prefill_case(case, pool=pool)
-    dt = time.perf_counter() - t0
+    while reps < 1 or time.perf_counter() - t0 < 10.0:   # the whole workload, >= 10 s in all
+        oracle.prefill_case(case, pool=pool)
+        reps += 1
+    dt = (time.perf_counter() - t0) / reps
     flops = prefill_flops(case.B, case.T, case.Hq, case.d, True)
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.num_threads(),
             "kind": "oracle",
-            "sample": f"the whole workload (2 x 2048 rows x 32 heads, fp64, {dt:.2f} s)"}
+            "sample": f"the whole workload (2 x 2048 rows x 32 heads, fp64), {reps} repeats of {dt:.2f} s"}
 
 
 def cpu_decode_baseline(case):
@@ -195,12 +258,52 @@ def cpu_decode_baseline(case):
     while True:
         oracle.decode_case(case, pool=pool)
         reps += 1
-        if time.perf_counter() - t0 > 2.0:
+        if time.perf_counter() - t0 > 5.0:
             break
     dt = (time.perf_counter() - t0) / reps
     kv = int(case.ctx_lens.sum()) * case.cache.n_kv_heads * case.d * 4
     return {"value": round(kv / dt / 1e9, 4), "unit": "GB/s", "cores": oracle.num_threads(),
             "kind": "oracle", "sample": f"the whole decode step, {reps} repeats ({dt:.3f} s each)"}
+
+
+COPY_BYTES = 256 << 20
+
+
+def kernels_only(n: int) -> None:
+    """For hardware-counter runs: launch a plain copy of COPY_BYTES (the
+    FETCH_SIZE / WRITE_SIZE calibration), then the Llama prefill, scatter and
+    decode kernels n times each, eagerly, one dispatch per call."""
+    src = torch.ones(COPY_BYTES // 2, dtype=torch.bfloat16, device=DEV)
+    dst = torch.empty_like(src)
+    for _ in range(n):
+        dst.copy_(src)
+    case = W.llama_prefill()
+    c = case.cache
+    pool = device_pool(c)
+    bt = i32(c.block_table)
+    k, v = case.tokens.k.to(DEV), case.tokens.v.to(DEV)
+    slots, pos = i32(case.tokens.slot_ids), i32(case.tokens.positions)
+    q, lens, sid = case.q.to(DEV), i32(case.seq_lens), i32(case.slot_ids)
+    for _ in range(n):
+        pa.kv_scatter(k, v, slots, pos, pool, bt, c.layer)
+    for _ in range(n):
+        pa.attn_prefill(q, pool, bt, c.layer, lens, c.n_kv_heads, case.scale, True, slot_ids=sid)
+    del pool
+    d = W.llama_decode()
+    c = d.cache
+    pool = device_pool(c)
+    tables = [i32(t) for t in decode_replicas(d, 8)]
+    for bt in tables:
+        for tok in (d.context, d.new_tokens):
+            pa.kv_scatter(tok.k.to(DEV), tok.v.to(DEV), i32(tok.slot_ids), i32(tok.positions), pool,
+                          bt, c.layer)
+    q, lens, sid = d.q.to(DEV), i32(d.ctx_lens), i32(d.slot_ids)
+    ws = pa.decode_workspace(d.B, d.Hq, c.n_kv_heads, d.d, d.max_ctx, DEV)
+    for i in range(n):
+        pa.attn_decode(q, pool, tables[i % 8], c.layer, lens, c.n_kv_heads, d.scale, d.max_ctx,
+                       slot_ids=sid, workspace=ws)
+    torch.cuda.synchronize()
+    print(f"kernels-only: {n} launches each", flush=True)
 
 
 def main() -> int:
@@ -209,6 +312,8 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--kernels-only", type=int, default=0, metavar="N",
+                    help="launch each dominant kernel N times for a counter run; no JSON")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -216,10 +321,15 @@ def main() -> int:
         return 2
     torch.cuda.set_device(0)
     pa.load()
+    if args.kernels_only:
+        kernels_only(args.kernels_only)
+        return 0
 
     p = bench_prefill(args.steps, args.warmup)
     d = bench_decode(args.steps, args.warmup)
 
+    prefill_digest = source_digest("device.h", "prefill.hip")
+    decode_digest = source_digest("device.h", "decode.hip")
     case = p["case"]
     ms = p["wall"] / args.steps * 1e3
     value = p["flops"] / (p["wall"] / args.steps) / 1e12
@@ -249,8 +359,10 @@ def main() -> int:
                    "flops_per_step": p["flops"], "pct_of_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2)},
         "roofline": {"kernel": "prefill_kernel<64,4,paged>", "bound": "mfma",
                      "achieved": round(kern_tflops, 3), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(kern_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
-                     "avg_us": round(p["t_kernel"] * 1e6, 3)},
+                     "frac": round(kern_tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic_of("prefill", prefill_digest),
+                     "avg_us": round(p["t_kernel"] * 1e6, 3), "alg_bytes": p["alg_bytes"],
+                     "source_digest": prefill_digest},
         "scatter_us": round(p["t_scatter"] * 1e6, 3),
         "decode": {
             "metric": "decode KV-read GB/s", "unit": "GB/s",
@@ -260,10 +372,12 @@ def main() -> int:
             "config": {"workload": "paged decode step, 64 sequences, ctx ~ U[1, 2048]",
                        "batch": dcase.B, "ctx_tokens": d["n_ctx"], "kv_bytes": d["kv_bytes"],
                        "replicas": d["replicas"], "step": "kv_scatter(64 tokens) + attn_decode"},
-            "roofline": {"kernel": "attn_decode (partial + combine)", "bound": "hbm",
+            "roofline": {"kernel": "decode_kernel<64,4>", "bound": "hbm",
                          "achieved": round(d_kern, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                         "frac": round(d_kern / PEAK_HBM_GBS, 4), "traffic": None,
-                         "avg_us": round(d["t_kernel"] * 1e6, 3), "alg_bytes": d_alg},
+                         "frac": round(d_kern / PEAK_HBM_GBS, 4),
+                         "traffic": traffic_of("decode", decode_digest),
+                         "avg_us": round(d["t_kernel"] * 1e6, 3), "alg_bytes": d_alg,
+                         "source_digest": decode_digest},
         },
     }
     if not args.no_cpu:
