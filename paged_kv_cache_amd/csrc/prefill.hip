@@ -25,14 +25,20 @@
 // Lane l owns query row l%32 throughout, so the row max, the exponentials and
 // the row sum of P stay in-lane (one cross-half exchange per tile), and the
 // probabilities a lane produces are already its B operand of the PV product.
-// K is kept row-major in LDS (a 16-byte read gives an A operand); V is
-// transposed when it is written to LDS so that the keys of a PV operand are
-// contiguous.
+//
+// K/V staging: tiles go from HBM straight into LDS (global_load_lds, 16 bytes
+// per lane, no staging registers) into a ring of NS stages, fetched NS-1
+// tiles ahead.  Each wave fetches one 16-token page of every tile (one scalar
+// block-table read per tile).  Rows are stored [key][16-byte chunk] with XOR
+// swizzles chosen so that both the K operand reads and the transposing V
+// reads are free of bank conflicts.
 //
 // Workgroup order: consecutive workgroup ids go to different XCDs, so the id
 // is remapped to keep every tile of one (sequence, head group) on one XCD
 // (its K/V then stays in that XCD's L2), and causal query tiles are issued
 // longest first.
+
+#include <type_traits>
 
 #include "device.h"
 #include "kernels.h"
@@ -67,33 +73,61 @@ struct PrefillArgs {
 
 }  // namespace
 
-template <int D, int G, bool PAGED>
-__global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
+// LDS placement of the 16-byte chunks of a K or V row (XOR swizzles).
+template <int D>
+struct Swz {
+  // K: chunk c of key j sits at c ^ k(j).  The QK operand reads (lanes 0..31
+  // = 32 consecutive keys, same chunk) then hit distinct banks in every group
+  // of 8 or 16 lanes.
+  __device__ static int k(int key) { return D == 64 ? ((key & 7) ^ ((key >> 3) & 1)) : (key & 15); }
+  // V: chunk c of key j sits at c ^ v(j); the transposing PV reads (4 keys x
+  // 4 columns per 16-lane group) then hit 64 distinct banks.
+  __device__ static int v(int key) { return 4 * ((key / (128 / D)) % (D / 32)); }
+};
+
+template <int D, int G, bool PAGED, int NS, int OCC>
+__global__ __launch_bounds__(kThreads, OCC) void prefill_kernel(PrefillArgs a) {
   constexpr int HW = G < kWaves ? G : kWaves;      // heads per workgroup
   constexpr int RW = kWaves / HW;                  // 32-row blocks per workgroup
   constexpr int BM = 32 * RW;                      // query rows per workgroup
-  constexpr int KROW = D + 8;                      // K row in LDS (bf16), padded
   constexpr int CH = D / 8;                        // 16-byte chunks per K/V row
-  constexpr int NLD = kBN * CH / kThreads;         // 16-byte loads per thread per tile (K, and V)
-  constexpr int KTILE = kBN * KROW;                // bf16 elements of one K tile in LDS
-  constexpr int VTILE = kBN * D;                   // bf16 elements of one V tile in LDS
-  static_assert(NLD >= 1 && kBN * CH % kThreads == 0, "tile/thread mismatch");
-  static_assert(kPageTokens % (64 / CH) == 0, "a wave load step must stay inside one page");
+  constexpr int ROWB = D * 2;                      // bytes of one K/V row (one head)
+  constexpr int TILEB = kBN * ROWB;                // bytes of one K (or V) tile
+  constexpr int KPI = 64 / CH;                     // keys per 1-KB wave transfer
+  constexpr int NDMA = TILEB / (kWaves * 1024);    // transfers per wave per tile, for K and for V
+  static_assert(NDMA * KPI == kPageTokens, "each wave fetches exactly one page of every key tile");
+  static_assert(NS >= 2 && NS <= 4, "LDS ring depth");
   // A running max is only raised when a row's tile max exceeds it by more
   // than this (log2 units), so most tiles skip the rescale; p stays <= 2^8.
   constexpr float kRescaleSlack = 8.f;
   constexpr float kMaxFloor = -1e30f;              // finite start of the running max
 
-  // Two K and two V tiles: tile t+1 is written while tile t is read.
-  // V is row-major [key][d] with its 16-byte chunks XOR-swizzled per key so
-  // that the transposing reads of the PV operands hit 64 distinct banks.
-  __shared__ __attribute__((aligned(16))) uint16_t ks[2 * KTILE];
-  __shared__ __attribute__((aligned(16))) uint16_t vs[2 * VTILE];
-  auto vswz = [](int key) { return 4 * ((key / (128 / D)) % (CH / 4)); };
+  // Ring of NS stages, each a K tile and a V tile ([key][chunk], swizzled).
+  // Tile u lives in stage u % NS; it is fetched NS-1 tiles ahead of use.
+  // Every tile buffer is a variable of its own: the compiler can then tell
+  // a transfer into one stage from a read of another and does not drain the
+  // transfers in flight before each LDS read.
+  __shared__ __attribute__((aligned(1024))) uint8_t lk0[TILEB], lv0[TILEB], lk1[TILEB], lv1[TILEB];
+  __shared__ __attribute__((aligned(1024))) uint8_t lk2[NS > 2 ? TILEB : 16], lv2[NS > 2 ? TILEB : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t lk3[NS > 3 ? TILEB : 16], lv3[NS > 3 ? TILEB : 16];
+  auto kbuf = [&](auto S_) -> uint8_t * {
+    constexpr int S = decltype(S_)::value;
+    if constexpr (S == 0) return lk0;
+    else if constexpr (S == 1) return lk1;
+    else if constexpr (S == 2) return lk2;
+    else return lk3;
+  };
+  auto vbuf = [&](auto S_) -> uint8_t * {
+    constexpr int S = decltype(S_)::value;
+    if constexpr (S == 0) return lv0;
+    else if constexpr (S == 1) return lv1;
+    else if constexpr (S == 2) return lv2;
+    else return lv3;
+  };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (scalar branches)
   const int lr = lane & 31;      // query row within the wave's 32 rows
   const int lh = lane >> 5;      // lane half
   const int l16 = lane & 15;     // lane within its 16-lane group
@@ -122,14 +156,12 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
   const int T = a.T;
 
   int len = T;
-  // Errors are collected here and reported once at the end: a global atomic
-  // before the key loop would make the compiler treat the block table as
-  // possibly clobbered and keep its (uniform) reads off the scalar unit.
+  // Errors are collected here and reported once at the end.
   int err_bits = 0;
-  // paged source of this sequence: table row and page geometry
-  const int32_t *trow = nullptr;
-  const int64_t page_bytes = 2LL * kPageTokens * a.Hkv * D * 2;
-  const int64_t v_offset = page_bytes / 2;
+  const int64_t page_bytes = 2LL * kPageTokens * a.Hkv * ROWB;
+  const uint32_t v_offset = (uint32_t)(page_bytes / 2);
+  const int32_t *trow_v = nullptr;   // block-table row (vector reads)
+  const_i32_ptr trow = nullptr;      // the same row (scalar reads)
   if constexpr (PAGED) {
     const bool reporter = hg == 0 && rb == 0;   // one workgroup per sequence reports
     len = a.seq_lens[b];
@@ -147,25 +179,161 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
       len = a.mbps * kPageTokens;
     }
     len = uniform(len);
-    trow = a.block_table + ((int64_t)uniform(len > 0 ? slot : 0) * a.n_layers + a.layer) * a.mbps;
+    trow_v = a.block_table + ((int64_t)uniform(len > 0 ? slot : 0) * a.n_layers + a.layer) * a.mbps;
+    trow = as_const(trow_v);
   }
 
   const int row = row0 + lr;
   const int wg_row_end = min(rb * BM + BM, len);
-  const int kv_end = a.causal ? wg_row_end : len;
+  const int kv_end = a.causal ? wg_row_end : len;   // keys past this are never visible here
   const int n_tiles = (kv_end > 0 && rb * BM < len) ? (kv_end + kBN - 1) / kBN : 0;
+  const int nblk = (kv_end + kPageTokens - 1) / kPageTokens;   // blocks read (paged)
   // last key this lane's row may see (-1: padding row, sees nothing)
   const int lim = row < len ? (a.causal ? row : len - 1) : -1;
+
+  // ---- pages: validated once for the whole workgroup.  A key that must not
+  // count (past kv_end, or on a missing page) is fetched from a safe token
+  // instead (token 0 of the first valid block, or of pool page 0 if there is
+  // none) so that every tile moves the same bytes and its V rows stay finite;
+  // its score is masked.
+  bool any_bad = false;
+  int64_t safe_page = 0;
+  if constexpr (PAGED) {
+    bool found = false;
+    for (int b0 = 0; b0 < nblk; b0 += 64) {
+      const int blk = b0 + lane;
+      const bool in = blk < nblk;
+      const int p = in ? trow_v[blk] : 0;
+      const bool bad = in && (p < 0 || (int64_t)p >= a.n_pages);
+      const uint64_t badm = __ballot(bad);
+      const uint64_t goodm = __ballot(in && !bad);
+      if (badm) any_bad = true;
+      if (!found && goodm) {
+        safe_page = __builtin_amdgcn_readlane(p, (int)__builtin_ctzll(goodm));
+        found = true;
+      }
+    }
+    if (any_bad) err_bits |= PA_DEVERR_BAD_PAGE;
+  }
+  auto page_ok = [&](int blk) -> bool {   // only for blk < nblk
+    const int32_t v = trow[blk];
+    return v >= 0 && (int64_t)v < a.n_pages;
+  };
 
   // ---- Q^T as B operands: lane holds row `row`, d = lh*(D/2) + k*8 + i
   bf16x8 qf[D / 16];
   {
     const bool ok = row < len;
-    const uint4 *qp = reinterpret_cast<const uint4 *>(
+    const u32x4 *qp = reinterpret_cast<const u32x4 *>(
         a.q + (((int64_t)b * T + (ok ? row : 0)) * Hq + head) * D + lh * (D / 2));
 #pragma unroll
     for (int k = 0; k < D / 16; ++k)
-      qf[k] = __builtin_bit_cast(bf16x8, ok ? qp[k] : uint4{0u, 0u, 0u, 0u});
+      qf[k] = __builtin_bit_cast(bf16x8, ok ? qp[k] : u32x4{0u, 0u, 0u, 0u});
+  }
+  // Let Q land before the first K/V transfer is issued: otherwise the
+  // compiler's wait bookkeeping counts Q as in flight at the top of every
+  // tile.  (An empty asm that takes the Q registers forces the wait.)
+#pragma unroll
+  for (int k = 0; k < D / 16; ++k) asm("" : "+v"(qf[k]));
+
+  // ---- per-lane transfer offsets, the same for every tile.  Transfer i of
+  // this wave carries tile keys kt = (wave*NDMA + i)*KPI + lane/CH, which all
+  // lie on page `wave` of the tile, at key kt % 16 of that page.
+  const int64_t tok_bytes = (int64_t)a.Hkv * ROWB;   // one token, all KV heads
+  // ksafe/vsafe: the same chunks of the safe token.  All of these stay in
+  // registers for the whole kernel, so a transfer never waits on a register.
+  uint32_t koff[NDMA], voff[NDMA], ksafe[NDMA], vsafe[NDMA];
+#pragma unroll
+  for (int i = 0; i < NDMA; ++i) {
+    const int kt = (wave * NDMA + i) * KPI + lane / CH;
+    const int pos = lane % CH;
+    const uint32_t kc = (uint32_t)(pos ^ Swz<D>::k(kt)) * 16;
+    const uint32_t vc = (uint32_t)(pos ^ Swz<D>::v(kt)) * 16;
+    if constexpr (PAGED) {
+      const uint32_t h = (uint32_t)(kvh * ROWB);
+      const uint32_t r = (uint32_t)((i * KPI + lane / CH) * tok_bytes);
+      koff[i] = r + h + kc;
+      voff[i] = v_offset + r + h + vc;
+      ksafe[i] = h + kc;
+      vsafe[i] = v_offset + h + vc;
+    } else {
+      koff[i] = (uint32_t)(kt * tok_bytes) + kc;
+      voff[i] = (uint32_t)(kt * tok_bytes) + vc;
+      ksafe[i] = kc;
+      vsafe[i] = vc;
+    }
+  }
+
+  // ---- fetch tile u into stage S: 2*NDMA transfers per wave, always
+  auto fetch = [&](int u, auto S_) {
+    uint8_t *kdst = kbuf(S_) + wave * NDMA * 1024;
+    uint8_t *vdst = vbuf(S_) + wave * NDMA * 1024;
+    const int key0 = u * kBN + wave * kPageTokens;   // first key of this wave's page
+    const uint8_t *kb, *vb, *sk, *sv;                // normal and safe bases
+    bool page_good = true;
+    if constexpr (PAGED) {
+      const int blk = u * (kBN / kPageTokens) + wave;
+      int64_t page = safe_page;
+      if (blk < nblk) {
+        const int32_t v = trow[blk];
+        page_good = v >= 0 && (int64_t)v < a.n_pages;
+        if (page_good) page = v;
+      } else {
+        page_good = false;
+      }
+      kb = a.pool + page * page_bytes;
+      vb = kb;
+      sk = a.pool + safe_page * page_bytes;
+      sv = sk;
+    } else {
+      const int64_t base = (((int64_t)b * T + u * kBN) * a.Hkv + kvh) * ROWB;
+      const int64_t safe = ((int64_t)b * T * a.Hkv + kvh) * ROWB;
+      kb = reinterpret_cast<const uint8_t *>(a.k) + base;
+      vb = reinterpret_cast<const uint8_t *>(a.v) + base;
+      sk = reinterpret_cast<const uint8_t *>(a.k) + safe;
+      sv = reinterpret_cast<const uint8_t *>(a.v) + safe;
+    }
+    if (page_good && key0 + kPageTokens <= kv_end) {
+#pragma unroll
+      for (int i = 0; i < NDMA; ++i) dma16(kb, koff[i], kdst + i * 1024);
+#pragma unroll
+      for (int i = 0; i < NDMA; ++i) dma16(vb, voff[i], vdst + i * 1024);
+    } else {
+      // some keys of this page must not count: those lanes fetch the safe
+      // token instead (two masked transfers; at least one per chunk runs).
+      // (The safe ones carry the non-temporal hint: they are few bytes, read
+      // again and again.)
+#pragma unroll
+      for (int i = 0; i < NDMA; ++i) {
+        const bool ok = page_good && key0 + i * KPI + lane / CH < kv_end;
+        if (ok) {
+          dma16(kb, koff[i], kdst + i * 1024);
+          dma16(vb, voff[i], vdst + i * 1024);
+        } else {
+          dma16<1>(sk, ksafe[i], kdst + i * 1024);
+          dma16<1>(sv, vsafe[i], vdst + i * 1024);
+        }
+      }
+    }
+  };
+
+  // ---- per-lane LDS read offsets (the stage and tile position are immediates)
+  // QK: lane reads key h*32 + lr, chunk lh*(CH/2) + k; the swizzle of key
+  // h*32 + lr depends on lr only.
+  uint32_t kaddr[CH / 2];
+#pragma unroll
+  for (int k = 0; k < CH / 2; ++k)
+    kaddr[k] = lr * ROWB + (uint32_t)(((lh * (CH / 2) + k) ^ Swz<D>::k(lr)) * 16);
+  // PV: operand kk covers keys 16kk..16kk+15; contraction slot (lh*8 + i) is
+  // key 16kk + 8*(i/4) + 4*lh + i%4.  Each half of the A operand is one
+  // transposing LDS read: in 16-lane group g, lane L points at
+  // V[key0 + L/4][d0 + 4*(L%4)] and receives V[key0..key0+3][d0 + L].
+  uint32_t vaddr[D / 32];
+#pragma unroll
+  for (int mb = 0; mb < D / 32; ++mb) {
+    const int key = 4 * (g16 >> 1) + (l16 >> 2);   // + 16kk + 8half (swizzle unchanged)
+    const int dcol = mb * 32 + 16 * (g16 & 1) + 4 * (l16 & 3);
+    vaddr[mb] = key * ROWB + (uint32_t)((((dcol / 8) ^ Swz<D>::v(key)) * 16) + (dcol % 8) * 2);
   }
 
   f32x16 acc[D / 32];
@@ -177,185 +345,150 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
   float l_lane = 0.f;        // this lane's half of the row's exp-sum
   const float c = a.scale_log2;
 
-  // ---- physical page of logical block blk, -1 when missing.  Every lane of
-  // a wave asks for the same block, so this is a scalar load.
-  auto page_of = [&](int blk) -> int64_t {
-    blk = uniform(blk);
-    if (blk * kPageTokens >= kv_end || blk >= a.mbps) return -1;
-    const int32_t v = trow[blk];
-    return (v < 0 || (int64_t)v >= a.n_pages) ? -1 : (int64_t)v;
-  };
-  // In one load step the 64 lanes of a wave cover 64/CH consecutive keys of a
-  // single page, so the page index is uniform per (step, wave).
-  const int wv = __builtin_amdgcn_readfirstlane(wave);
-
-  // ---- K/V tile loader: thread covers (key idx/CH, chunk idx%CH), idx = c*256 + tid
-  uint4 kr[NLD], vr[NLD];
-  auto load_tile = [&](int kv0) {
-#pragma unroll
-    for (int cc = 0; cc < NLD; ++cc) {
-      const int idx = cc * kThreads + tid;
-      const int key = idx / CH;
-      const int ch = idx % CH;
-      const int j = kv0 + key;
-      kr[cc] = uint4{0u, 0u, 0u, 0u};
-      vr[cc] = uint4{0u, 0u, 0u, 0u};
-      if constexpr (PAGED) {
-        const int64_t page = page_of(kv0 / kPageTokens + ((cc * kThreads + 64 * wv) / CH) / kPageTokens);
-        if (j < kv_end && page >= 0) {
-          const uint8_t *src = a.pool + page * page_bytes +
-                               (int64_t)(j % kPageTokens) * a.Hkv * D * 2 + (int64_t)kvh * D * 2 + ch * 16;
-          kr[cc] = *reinterpret_cast<const uint4 *>(src);
-          vr[cc] = *reinterpret_cast<const uint4 *>(src + v_offset);
-        }
-      } else {
-        if (j < kv_end) {
-          const int64_t off = (((int64_t)b * T + j) * a.Hkv + kvh) * D + ch * 8;
-          kr[cc] = *reinterpret_cast<const uint4 *>(a.k + off);
-          vr[cc] = *reinterpret_cast<const uint4 *>(a.v + off);
-        }
-      }
-    }
-  };
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int cc = 0; cc < NLD; ++cc) {
-      const int idx = cc * kThreads + tid;
-      const int key = idx / CH;
-      const int ch = idx % CH;
-      *reinterpret_cast<uint4 *>(&ks[buf * KTILE + key * KROW + ch * 8]) = kr[cc];
-      *reinterpret_cast<uint4 *>(&vs[buf * VTILE + key * D + ((ch ^ vswz(key)) * 8)]) = vr[cc];
-    }
-  };
-
-  if (n_tiles > 0) {
-    load_tile(0);
-    store_tile(0);
-    if (n_tiles > 1) load_tile(kBN);
-    __syncthreads();
-  }
-
-  for (int t = 0; t < n_tiles; ++t) {
+  // ---- one key tile: S = K Q^T, online softmax, O^T += V^T P^T
+  auto compute = [&](int t, auto S_) {
+    const uint8_t *kt = kbuf(S_);
+    const uint8_t *vt = vbuf(S_);
     const int kv0 = t * kBN;
-    const int buf = t & 1;
-    uint32_t bad_pages = 0;    // needed pages of this tile missing from the table
-    if constexpr (PAGED) {
+
+    f32x16 s[2];
 #pragma unroll
-      for (int p = 0; p < kBN / kPageTokens; ++p) {
-        const int blk = kv0 / kPageTokens + p;
-        if (blk * kPageTokens < kv_end && page_of(blk) < 0) bad_pages |= 1u << p;
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[h][r] = 0.f;
+#pragma unroll
+      for (int k = 0; k < CH / 2; ++k) {
+        const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(kt + kaddr[k] + h * 32 * ROWB);
+        s[h] = mfma32(kf, qf[k], s[h]);
       }
-      if (bad_pages) err_bits |= PA_DEVERR_BAD_PAGE;
     }
 
-    // a wave whose rows all precede this tile sees none of it (causal)
-    if (!(a.causal && kv0 > row0 + 31)) {
-      const uint16_t *kt = &ks[buf * KTILE];
-      const uint16_t *vtile = &vs[buf * VTILE];
-      // S^T = K Q^T: two 32-key halves
-      f32x16 s[2];
+    // mask: only tiles that cross the diagonal, kv_end or a missing page.
+    // The lane holds keys kv0 + h*32 + 8*(r/4) + 4*lh + r%4.
+    uint32_t bad_pages = 0;
+    if constexpr (PAGED) {
+      if (any_bad) {
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s[h][r] = 0.f;
-#pragma unroll
-        for (int k = 0; k < D / 16; ++k) {
-          const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(&kt[(h * 32 + lr) * KROW + lh * (D / 2) + k * 8]);
-          s[h] = mfma32(kf, qf[k], s[h]);
+        for (int p = 0; p < kBN / kPageTokens; ++p) {
+          const int blk = t * (kBN / kPageTokens) + p;
+          if (blk < nblk && !page_ok(blk)) bad_pages |= 1u << p;
         }
       }
-
-      // mask: only tiles that cross the diagonal, the sequence end or a missing
-      // page.  The lane holds keys kv0 + h*32 + 8*(r/4) + 4*lh + r%4.
-      const bool need_mask = (kv0 + kBN - 1 > row0 && a.causal) | (kv0 + kBN > len) | (bad_pages != 0);
-      if (need_mask) {
-        const int rel = lim - (kv0 + 4 * lh);      // visible iff key offset <= rel
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int off = h * 32 + 8 * (r / 4) + (r % 4);
-            s[h][r] = off <= rel ? s[h][r] : -INFINITY;
-          }
-        if (bad_pages) {
-#pragma unroll
-          for (int h = 0; h < 2; ++h)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int pidx = (h * 32 + 8 * (r / 4) + 4 * lh) / kPageTokens;
-              s[h][r] = ((bad_pages >> pidx) & 1u) ? -INFINITY : s[h][r];
-            }
-        }
-      }
-
-      // tile row max of the raw scores (scale >= 0 keeps the order)
-      float rmax = -INFINITY;
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) rmax = fmaxf(rmax, s[h][r]);
-      rmax = fmaxf(rmax, __shfl_xor(rmax, 32));
-      const float mt = rmax * c;
-      if (__any(mt > m_run + kRescaleSlack)) {
-        const float m_new = fmaxf(m_run, mt);
-        const float corr = fast_exp2(m_run - m_new);
-        m_run = m_new;
-        l_lane *= corr;
-#pragma unroll
-        for (int i = 0; i < D / 32; ++i)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) acc[i][r] *= corr;
-      }
-
-      // P = 2^(s*c - m) (bf16) as B operands of the PV product: 16 keys each
-      bf16x8 pb[4];
-      float psum = 0.f;
+    }
+    const bool need_mask = (a.causal && kv0 + kBN - 1 > row0) | (kv0 + kBN > kv_end) | (bad_pages != 0);
+    if (need_mask) {
+      const int rel = lim - (kv0 + 4 * lh);      // visible iff key offset <= rel
 #pragma unroll
       for (int h = 0; h < 2; ++h)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float p = fast_exp2(__builtin_fmaf(s[h][r], c, -m_run));
-          psum += p;
-          pb[h * 2 + r / 8][r % 8] = (__bf16)p;
+          const int off = h * 32 + 8 * (r / 4) + (r % 4);
+          s[h][r] = off <= rel ? s[h][r] : -INFINITY;
         }
-      l_lane += psum;
-
-      // O^T += V^T P^T.  Operand kk covers keys 16kk..16kk+15; contraction slot
-      // (lh*8 + i) is key 16kk + 8*(i/4) + 4*lh + i%4.  Each half of the A
-      // operand is one transposing LDS read: in 16-lane group g, lane L points
-      // at V[key0 + L/4][d0 + 4*(L%4)] and receives V[key0..key0+3][d0 + L].
+      if (bad_pages) {
 #pragma unroll
-      for (int mb = 0; mb < D / 32; ++mb) {
-        const int dcol = mb * 32 + 16 * (g16 & 1) + 4 * (l16 & 3);   // this lane's 4 d values
+        for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-          uint2 part[2];
-#pragma unroll
-          for (int half = 0; half < 2; ++half) {
-            const int key = 16 * kk + 8 * half + 4 * (g16 >> 1) + (l16 >> 2);
-            const int ch = dcol / 8;
-            const uint16_t *src = &vtile[key * D + ((ch ^ vswz(key)) * 8) + (dcol % 8)];
-            part[half] = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                                                       (__attribute__((address_space(3))) i16x4 *)(src)));
+          for (int r = 0; r < 16; ++r) {
+            const int pidx = (h * 32 + 8 * (r / 4) + 4 * lh) / kPageTokens;
+            s[h][r] = ((bad_pages >> pidx) & 1u) ? -INFINITY : s[h][r];
           }
-          const bf16x8 va = __builtin_bit_cast(bf16x8, uint4{part[0].x, part[0].y, part[1].x, part[1].y});
-          acc[mb] = mfma32(va, pb[kk], acc[mb]);
-        }
       }
     }
 
-    // stage tile t+1 into the other buffer, then prefetch tile t+2
-    if (t + 1 < n_tiles) {
-      store_tile(buf ^ 1);
-      if (t + 2 < n_tiles) load_tile(kv0 + 2 * kBN);
+    // tile row max of the raw scores (scale >= 0 keeps the order)
+    float rmax = -INFINITY;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) rmax = fmaxf(rmax, s[h][r]);
+    auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(rmax), __float_as_uint(rmax), false, false);
+    rmax = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+    const float mt = rmax * c;
+    if (__any(mt > m_run + kRescaleSlack)) {
+      const float m_new = fmaxf(m_run, mt);
+      const float corr = fast_exp2(m_run - m_new);
+      m_run = m_new;
+      l_lane *= corr;
+#pragma unroll
+      for (int i = 0; i < D / 32; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][r] *= corr;
     }
-    __syncthreads();
+
+    // P = 2^(s*c - m) (bf16) as B operands of the PV product: 16 keys each
+    bf16x8 pb[4];
+    float psum = 0.f;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = fast_exp2(__builtin_fmaf(s[h][r], c, -m_run));
+        psum += p;
+        pb[h * 2 + r / 8][r % 8] = (__bf16)p;
+      }
+    l_lane += psum;
+
+#pragma unroll
+    for (int mb = 0; mb < D / 32; ++mb) {
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        uint2 part[2];
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          const uint8_t *src = vt + vaddr[mb] + (16 * kk + 8 * half) * ROWB;
+          part[half] = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                                     (__attribute__((address_space(3))) i16x4 *)(src)));
+        }
+        const bf16x8 va = __builtin_bit_cast(bf16x8, u32x4{part[0].x, part[0].y, part[1].x, part[1].y});
+        acc[mb] = mfma32(va, pb[kk], acc[mb]);
+      }
+    }
+  };
+
+  // ---- the ring.  Step t: wait for this wave's transfers of tile t, barrier
+  // (now every wave's transfers of tile t have landed and every wave is done
+  // with tile t-1), fetch tile t+NS-1 into the stage tile t-1 used, compute t.
+  // Every step issues its transfers, also for tiles past the end (they carry
+  // the safe token), so the number in flight is the same on every path and
+  // one constant wait is exact; the compiler's own bookkeeping then agrees
+  // and adds no drain of its own.
+  auto skip = [&](int t) { return a.causal && t * kBN > row0 + 31; };   // rows all precede the tile
+  auto step = [&](int t, auto S_) {
+    constexpr int S = decltype(S_)::value;
+    wait_vm_lgkm0<(NS - 2) * 2 * NDMA>();
+    __builtin_amdgcn_s_barrier();
+    fetch(t + NS - 1, std::integral_constant<int, (S + NS - 1) % NS>{});
+    if (!skip(t)) compute(t, S_);
+  };
+
+  if (n_tiles > 0) {
+    fetch(0, std::integral_constant<int, 0>{});
+    if constexpr (NS > 2) fetch(1, std::integral_constant<int, 1>{});
+    if constexpr (NS > 3) fetch(2, std::integral_constant<int, 2>{});
+    for (int t = 0;;) {
+      step(t, std::integral_constant<int, 0>{});
+      if (++t >= n_tiles) break;
+      step(t, std::integral_constant<int, 1 % NS>{});
+      if (++t >= n_tiles) break;
+      if constexpr (NS > 2) {
+        step(t, std::integral_constant<int, 2 % NS>{});
+        if (++t >= n_tiles) break;
+      }
+      if constexpr (NS > 3) {
+        step(t, std::integral_constant<int, 3 % NS>{});
+        if (++t >= n_tiles) break;
+      }
+    }
+    // no transfer may still be writing LDS when the workgroup ends
+    wait_vm_lgkm0<0>();
   }
 
   if (err_bits && tid == 0) raise_err(a.err, err_bits);
 
   // ---- epilogue: one divide per row, LSE in natural-log units
-  float l_row = l_lane + __shfl_xor(l_lane, 32);
+  auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_lane), __float_as_uint(l_lane), false, false);
+  const float l_row = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
   const bool has = row < len && l_row > 0.f;
   const float inv_l = has ? 1.f / l_row : 0.f;
   if (row < T) {
@@ -374,6 +507,20 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
   }
 }
 
+#ifndef PA_PREFILL_NS64
+#define PA_PREFILL_NS64 3
+#endif
+#ifndef PA_PREFILL_OCC64
+#define PA_PREFILL_OCC64 3
+#endif
+// ring depth and target waves per SIMD: d=64 keeps 3 tiles in flight (48 KB
+// of LDS, 3 workgroups per CU); d=128 two (64 KB, 2 per CU)
+template <int D>
+struct PrefillCfg {
+  static constexpr int NS = D == 64 ? PA_PREFILL_NS64 : 2;
+  static constexpr int OCC = D == 64 ? PA_PREFILL_OCC64 : 2;
+};
+
 template <int D, int G, bool PAGED>
 static int launch_prefill_t(PrefillArgs a, hipStream_t stream) {
   constexpr int HW = G < kWaves ? G : kWaves;
@@ -385,7 +532,8 @@ static int launch_prefill_t(PrefillArgs a, hipStream_t stream) {
   const int64_t grid = (int64_t)a.B * a.n_hgroups * a.n_rowblocks;
   if (grid == 0) return PA_OK;
   if (grid > 0x7fffffff) return PA_ERR_RANGE;
-  hipLaunchKernelGGL((prefill_kernel<D, G, PAGED>), dim3((unsigned)grid), dim3(kThreads), 0, stream, a);
+  hipLaunchKernelGGL((prefill_kernel<D, G, PAGED, PrefillCfg<D>::NS, PrefillCfg<D>::OCC>), dim3((unsigned)grid),
+                     dim3(kThreads), 0, stream, a);
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
 
