@@ -7,17 +7,23 @@
 // unnormalised output, rescale both when m grows, divide by l once at the end
 // and store LSE = m + ln l.  The exponentials are taken base 2 on scores
 // pre-multiplied by scale*log2(e) (same values; v_exp_f32 is a base-2 unit).
+// m need not be the exact running max: any reference value works as long as
+// the exponentials neither overflow nor lose the row, so m is moved (and O, l
+// rescaled) only on a row's first tile or when some p of a tile would reach
+// 2^64; the others take p = 2^(s*c - m) against the old m, with no tile max.
 // Causal tiles wholly above the diagonal are never visited and the mask is
 // evaluated only on tiles that cross the diagonal or the sequence end
 // (explainer, "causal mask" paragraph).
 //
 // Work split (explainer, "Parallelise along the sequence length" and "Work
-// partitioning between warps"): one workgroup of four wavefronts owns a query
-// tile of one GQA group; the grid is batch x head-group x query tile, all
-// independent.  The four wavefronts split the queries (split-Q): with a group
-// of four q heads they take the four heads of the same 32 rows, so a K/V tile
-// staged once in LDS serves 4 x 32 query rows; with smaller groups they take
-// more rows of fewer heads.  No wavefront ever reads another's results.
+// partitioning between warps"): one workgroup owns four 32-column blocks
+// (query rows x heads) of one GQA group; the grid is batch x head-group x
+// query tile, all independent.  The wavefronts split the queries (split-Q):
+// with a group of four q heads the blocks are the four heads of the same 32
+// rows, so a K/V tile staged once in LDS serves 4 x 32 query rows; with
+// smaller groups they are more rows of fewer heads.  Each wavefront owns BPW
+// blocks (every operand it reads from LDS feeds BPW MFMAs).  No wavefront
+// ever reads another's results.
 //
 // Tile products on gfx950 bf16 MFMA with fp32 accumulation, 32x32x16 shape:
 //   S^T[32 keys][32 rows] = K[32 keys][16 d] x Q^T[16 d][32 rows]
@@ -48,8 +54,7 @@ namespace pa {
 namespace {
 
 constexpr int kBN = 64;        // keys per tile
-constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;
+constexpr int kBlocks = 4;     // 32-column (query row x head) blocks per workgroup
 
 struct PrefillArgs {
   const uint16_t *q;           // [B][T][Hq][D]
@@ -85,28 +90,32 @@ struct Swz {
   __device__ static int v(int key) { return 4 * ((key / (128 / D)) % (D / 32)); }
 };
 
-template <int D, int G, bool PAGED, int NS, int OCC>
-__global__ __launch_bounds__(kThreads, OCC) void prefill_kernel(PrefillArgs a) {
-  constexpr int HW = G < kWaves ? G : kWaves;      // heads per workgroup
-  constexpr int RW = kWaves / HW;                  // 32-row blocks per workgroup
+template <int D, int G, bool PAGED, int NS, int OCC, int BPW>
+__global__ __launch_bounds__(64 * (kBlocks / BPW), OCC) void prefill_kernel(PrefillArgs a) {
+  constexpr int NW = kBlocks / BPW;                // waves per workgroup
+  constexpr int HW = G < kBlocks ? G : kBlocks;    // heads per workgroup
+  constexpr int RW = kBlocks / HW;                 // 32-row blocks per workgroup
   constexpr int BM = 32 * RW;                      // query rows per workgroup
   constexpr int CH = D / 8;                        // 16-byte chunks per K/V row
   constexpr int ROWB = D * 2;                      // bytes of one K/V row (one head)
   constexpr int TILEB = kBN * ROWB;                // bytes of one K (or V) tile
   constexpr int KPI = 64 / CH;                     // keys per 1-KB wave transfer
-  constexpr int NDMA = TILEB / (kWaves * 1024);    // transfers per wave per tile, for K and for V
-  static_assert(NDMA * KPI == kPageTokens, "each wave fetches exactly one page of every key tile");
+  constexpr int NDMA = TILEB / (NW * 1024);        // transfers per wave per tile, for K and for V
+  constexpr int PPW = NDMA * KPI / kPageTokens;    // pages per wave per tile
+  constexpr int TPP = kPageTokens / KPI;           // transfers per page
+  static_assert(PPW >= 1 && PPW * kPageTokens == NDMA * KPI, "each wave fetches whole pages of every key tile");
   static_assert(NS >= 2 && NS <= 4, "LDS ring depth");
-  // A running max is only raised when a row's tile max exceeds it by more
-  // than this (log2 units), so most tiles skip the rescale; p stays <= 2^8.
-  constexpr float kRescaleSlack = 8.f;
+  // The running max m is only moved when some p = 2^(s*c - m) of a tile would
+  // reach 2^64 (or on a row's first tile): fp32 and bf16 hold such p exactly
+  // as well as p <= 1, and O, l stay far from overflow, so most tiles skip
+  // the tile max and the rescale altogether.
+  constexpr float kSpecLimit = 0x1p64f;
   constexpr float kMaxFloor = -1e30f;              // finite start of the running max
 
   // Ring of NS stages, each a K tile and a V tile ([key][chunk], swizzled).
   // Tile u lives in stage u % NS; it is fetched NS-1 tiles ahead of use.
-  // Every tile buffer is a variable of its own: the compiler can then tell
-  // a transfer into one stage from a read of another and does not drain the
-  // transfers in flight before each LDS read.
+  // Every tile buffer is a variable of its own so that the compiler can tell
+  // the stages apart.
   __shared__ __attribute__((aligned(1024))) uint8_t lk0[TILEB], lv0[TILEB], lk1[TILEB], lv1[TILEB];
   __shared__ __attribute__((aligned(1024))) uint8_t lk2[NS > 2 ? TILEB : 16], lv2[NS > 2 ? TILEB : 16];
   __shared__ __attribute__((aligned(1024))) uint8_t lk3[NS > 3 ? TILEB : 16], lv3[NS > 3 ? TILEB : 16];
@@ -128,7 +137,7 @@ __global__ __launch_bounds__(kThreads, OCC) void prefill_kernel(PrefillArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (scalar branches)
-  const int lr = lane & 31;      // query row within the wave's 32 rows
+  const int lr = lane & 31;      // query row within a 32-row block
   const int lh = lane >> 5;      // lane half
   const int l16 = lane & 15;     // lane within its 16-lane group
   const int g16 = lane >> 4;     // 16-lane group
@@ -151,9 +160,17 @@ __global__ __launch_bounds__(kThreads, OCC) void prefill_kernel(PrefillArgs a) {
   const int hg = pair % a.n_hgroups;
   const int Hq = a.Hkv * G;
   const int kvh = (hg * HW) / G;
-  const int head = hg * HW + (wave % HW);
-  const int row0 = rb * BM + 32 * (wave / HW);
   const int T = a.T;
+  // this wave's column blocks: block j = wave*BPW + i is head hg*HW + j%HW,
+  // rows rb*BM + 32*(j/HW) .. +31
+  int head[BPW], row0[BPW];
+#pragma unroll
+  for (int i = 0; i < BPW; ++i) {
+    const int j = wave * BPW + i;
+    head[i] = hg * HW + j % HW;
+    row0[i] = rb * BM + 32 * (j / HW);
+  }
+  const int wave_row_end = row0[BPW - 1] + 31;   // last row of this wave
 
   int len = T;
   // Errors are collected here and reported once at the end.
@@ -183,13 +200,17 @@ __global__ __launch_bounds__(kThreads, OCC) void prefill_kernel(PrefillArgs a) {
     trow = as_const(trow_v);
   }
 
-  const int row = row0 + lr;
   const int wg_row_end = min(rb * BM + BM, len);
   const int kv_end = a.causal ? wg_row_end : len;   // keys past this are never visible here
   const int n_tiles = (kv_end > 0 && rb * BM < len) ? (kv_end + kBN - 1) / kBN : 0;
   const int nblk = (kv_end + kPageTokens - 1) / kPageTokens;   // blocks read (paged)
-  // last key this lane's row may see (-1: padding row, sees nothing)
-  const int lim = row < len ? (a.causal ? row : len - 1) : -1;
+  // last key each of this lane's rows may see (-1: padding row, sees nothing)
+  int lim[BPW];
+#pragma unroll
+  for (int i = 0; i < BPW; ++i) {
+    const int row = row0[i] + lr;
+    lim[i] = row < len ? (a.causal ? row : len - 1) : -1;
+  }
 
   // ---- pages: validated once for the whole workgroup.  A key that must not
   // count (past kv_end, or on a missing page) is fetched from a safe token
@@ -220,28 +241,31 @@ __global__ __launch_bounds__(kThreads, OCC) void prefill_kernel(PrefillArgs a) {
     return v >= 0 && (int64_t)v < a.n_pages;
   };
 
-  // ---- Q^T as B operands: lane holds row `row`, d = lh*(D/2) + k*8 + i
-  bf16x8 qf[D / 16];
-  {
+  // ---- Q^T as B operands: lane holds row row0[i] + lr, d = lh*(D/2) + k*8 + e
+  bf16x8 qf[BPW][D / 16];
+#pragma unroll
+  for (int i = 0; i < BPW; ++i) {
+    const int row = row0[i] + lr;
     const bool ok = row < len;
     const u32x4 *qp = reinterpret_cast<const u32x4 *>(
-        a.q + (((int64_t)b * T + (ok ? row : 0)) * Hq + head) * D + lh * (D / 2));
+        a.q + (((int64_t)b * T + (ok ? row : 0)) * Hq + head[i]) * D + lh * (D / 2));
 #pragma unroll
     for (int k = 0; k < D / 16; ++k)
-      qf[k] = __builtin_bit_cast(bf16x8, ok ? qp[k] : u32x4{0u, 0u, 0u, 0u});
+      qf[i][k] = __builtin_bit_cast(bf16x8, ok ? qp[k] : u32x4{0u, 0u, 0u, 0u});
   }
-  // Let Q land before the first K/V transfer is issued: otherwise the
-  // compiler's wait bookkeeping counts Q as in flight at the top of every
-  // tile.  (An empty asm that takes the Q registers forces the wait.)
+  // Let Q land before the first K/V transfer is issued.  (An empty asm that
+  // takes the Q registers forces the wait.)
 #pragma unroll
-  for (int k = 0; k < D / 16; ++k) asm("" : "+v"(qf[k]));
+  for (int i = 0; i < BPW; ++i)
+#pragma unroll
+    for (int k = 0; k < D / 16; ++k) asm("" : "+v"(qf[i][k]));
 
   // ---- per-lane transfer offsets, the same for every tile.  Transfer i of
-  // this wave carries tile keys kt = (wave*NDMA + i)*KPI + lane/CH, which all
-  // lie on page `wave` of the tile, at key kt % 16 of that page.
-  const int64_t tok_bytes = (int64_t)a.Hkv * ROWB;   // one token, all KV heads
+  // this wave carries tile keys kt = (wave*NDMA + i)*KPI + lane/CH, on page
+  // wave*PPW + i/TPP of the tile, at key (i%TPP)*KPI + lane/CH of that page.
   // ksafe/vsafe: the same chunks of the safe token.  All of these stay in
   // registers for the whole kernel, so a transfer never waits on a register.
+  const int64_t tok_bytes = (int64_t)a.Hkv * ROWB;   // one token, all KV heads
   uint32_t koff[NDMA], voff[NDMA], ksafe[NDMA], vsafe[NDMA];
 #pragma unroll
   for (int i = 0; i < NDMA; ++i) {
@@ -251,7 +275,7 @@ __global__ __launch_bounds__(kThreads, OCC) void prefill_kernel(PrefillArgs a) {
     const uint32_t vc = (uint32_t)(pos ^ Swz<D>::v(kt)) * 16;
     if constexpr (PAGED) {
       const uint32_t h = (uint32_t)(kvh * ROWB);
-      const uint32_t r = (uint32_t)((i * KPI + lane / CH) * tok_bytes);
+      const uint32_t r = (uint32_t)(((i % TPP) * KPI + lane / CH) * tok_bytes);
       koff[i] = r + h + kc;
       voff[i] = v_offset + r + h + vc;
       ksafe[i] = h + kc;
@@ -268,50 +292,55 @@ __global__ __launch_bounds__(kThreads, OCC) void prefill_kernel(PrefillArgs a) {
   auto fetch = [&](int u, auto S_) {
     uint8_t *kdst = kbuf(S_) + wave * NDMA * 1024;
     uint8_t *vdst = vbuf(S_) + wave * NDMA * 1024;
-    const int key0 = u * kBN + wave * kPageTokens;   // first key of this wave's page
-    const uint8_t *kb, *vb, *sk, *sv;                // normal and safe bases
-    bool page_good = true;
-    if constexpr (PAGED) {
-      const int blk = u * (kBN / kPageTokens) + wave;
-      int64_t page = safe_page;
-      if (blk < nblk) {
-        const int32_t v = trow[blk];
-        page_good = v >= 0 && (int64_t)v < a.n_pages;
-        if (page_good) page = v;
+#pragma unroll
+    for (int pp = 0; pp < PPW; ++pp) {
+      const int key0 = u * kBN + (wave * PPW + pp) * kPageTokens;   // first key of the page
+      const uint8_t *kb, *vb, *sk, *sv;                             // normal and safe bases
+      bool page_good = true;
+      if constexpr (PAGED) {
+        const int blk = key0 / kPageTokens;
+        int64_t page = safe_page;
+        if (blk < nblk) {
+          const int32_t v = trow[blk];
+          page_good = v >= 0 && (int64_t)v < a.n_pages;
+          if (page_good) page = v;
+        } else {
+          page_good = false;
+        }
+        kb = a.pool + page * page_bytes;
+        vb = kb;
+        sk = a.pool + safe_page * page_bytes;
+        sv = sk;
       } else {
-        page_good = false;
+        const int64_t base = (((int64_t)b * T + u * kBN) * a.Hkv + kvh) * ROWB;
+        const int64_t safe = ((int64_t)b * T * a.Hkv + kvh) * ROWB;
+        kb = reinterpret_cast<const uint8_t *>(a.k) + base;
+        vb = reinterpret_cast<const uint8_t *>(a.v) + base;
+        sk = reinterpret_cast<const uint8_t *>(a.k) + safe;
+        sv = reinterpret_cast<const uint8_t *>(a.v) + safe;
       }
-      kb = a.pool + page * page_bytes;
-      vb = kb;
-      sk = a.pool + safe_page * page_bytes;
-      sv = sk;
-    } else {
-      const int64_t base = (((int64_t)b * T + u * kBN) * a.Hkv + kvh) * ROWB;
-      const int64_t safe = ((int64_t)b * T * a.Hkv + kvh) * ROWB;
-      kb = reinterpret_cast<const uint8_t *>(a.k) + base;
-      vb = reinterpret_cast<const uint8_t *>(a.v) + base;
-      sk = reinterpret_cast<const uint8_t *>(a.k) + safe;
-      sv = reinterpret_cast<const uint8_t *>(a.v) + safe;
-    }
-    if (page_good && key0 + kPageTokens <= kv_end) {
+      if (page_good && key0 + kPageTokens <= kv_end) {
 #pragma unroll
-      for (int i = 0; i < NDMA; ++i) dma16(kb, koff[i], kdst + i * 1024);
-#pragma unroll
-      for (int i = 0; i < NDMA; ++i) dma16(vb, voff[i], vdst + i * 1024);
-    } else {
-      // some keys of this page must not count: those lanes fetch the safe
-      // token instead (two masked transfers; at least one per chunk runs).
-      // (The safe ones carry the non-temporal hint: they are few bytes, read
-      // again and again.)
-#pragma unroll
-      for (int i = 0; i < NDMA; ++i) {
-        const bool ok = page_good && key0 + i * KPI + lane / CH < kv_end;
-        if (ok) {
+        for (int e = 0; e < TPP; ++e) {
+          const int i = pp * TPP + e;
           dma16(kb, koff[i], kdst + i * 1024);
           dma16(vb, voff[i], vdst + i * 1024);
-        } else {
-          dma16<1>(sk, ksafe[i], kdst + i * 1024);
-          dma16<1>(sv, vsafe[i], vdst + i * 1024);
+        }
+      } else {
+        // some keys of this page must not count: those lanes fetch the safe
+        // token instead (two masked transfers; at least one per chunk runs;
+        // the safe ones carry the non-temporal hint)
+#pragma unroll
+        for (int e = 0; e < TPP; ++e) {
+          const int i = pp * TPP + e;
+          const bool ok = page_good && key0 + e * KPI + lane / CH < kv_end;
+          if (ok) {
+            dma16(kb, koff[i], kdst + i * 1024);
+            dma16(vb, voff[i], vdst + i * 1024);
+          } else {
+            dma16<1>(sk, ksafe[i], kdst + i * 1024);
+            dma16<1>(sv, vsafe[i], vdst + i * 1024);
+          }
         }
       }
     }
@@ -324,8 +353,8 @@ __global__ __launch_bounds__(kThreads, OCC) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
   for (int k = 0; k < CH / 2; ++k)
     kaddr[k] = lr * ROWB + (uint32_t)(((lh * (CH / 2) + k) ^ Swz<D>::k(lr)) * 16);
-  // PV: operand kk covers keys 16kk..16kk+15; contraction slot (lh*8 + i) is
-  // key 16kk + 8*(i/4) + 4*lh + i%4.  Each half of the A operand is one
+  // PV: operand kk covers keys 16kk..16kk+15; contraction slot (lh*8 + e) is
+  // key 16kk + 8*(e/4) + 4*lh + e%4.  Each half of the A operand is one
   // transposing LDS read: in 16-lane group g, lane L points at
   // V[key0 + L/4][d0 + 4*(L%4)] and receives V[key0..key0+3][d0 + L].
   uint32_t vaddr[D / 32];
@@ -336,35 +365,46 @@ __global__ __launch_bounds__(kThreads, OCC) void prefill_kernel(PrefillArgs a) {
     vaddr[mb] = key * ROWB + (uint32_t)((((dcol / 8) ^ Swz<D>::v(key)) * 16) + (dcol % 8) * 2);
   }
 
-  f32x16 acc[D / 32];
+  f32x16 acc[BPW][D / 32];
 #pragma unroll
-  for (int i = 0; i < D / 32; ++i)
+  for (int i = 0; i < BPW; ++i)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) acc[i][r] = 0.f;
-  float m_run = kMaxFloor;   // reference max of the row (log2 units)
-  float l_lane = 0.f;        // this lane's half of the row's exp-sum
+    for (int mb = 0; mb < D / 32; ++mb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][mb][r] = 0.f;
+  float m_run[BPW], l_lane[BPW];   // reference max of the row (log2 units); this lane's half of l
+#pragma unroll
+  for (int i = 0; i < BPW; ++i) {
+    m_run[i] = kMaxFloor;
+    l_lane[i] = 0.f;
+  }
+  bool started = false;            // some tile processed (wave-uniform)
   const float c = a.scale_log2;
 
-  // ---- one key tile: S = K Q^T, online softmax, O^T += V^T P^T
+  // ---- one key tile: S = K Q^T, online softmax, O^T += V^T P^T.  Every
+  // operand read from LDS feeds the MFMAs of all BPW column blocks.
   auto compute = [&](int t, auto S_) {
     const uint8_t *kt = kbuf(S_);
     const uint8_t *vt = vbuf(S_);
     const int kv0 = t * kBN;
 
-    f32x16 s[2];
+    f32x16 s[BPW][2];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s[h][r] = 0.f;
+      for (int i = 0; i < BPW; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[i][h][r] = 0.f;
 #pragma unroll
       for (int k = 0; k < CH / 2; ++k) {
         const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(kt + kaddr[k] + h * 32 * ROWB);
-        s[h] = mfma32(kf, qf[k], s[h]);
+#pragma unroll
+        for (int i = 0; i < BPW; ++i) s[i][h] = mfma32(kf, qf[i][k], s[i][h]);
       }
     }
 
-    // mask: only tiles that cross the diagonal, kv_end or a missing page.
-    // The lane holds keys kv0 + h*32 + 8*(r/4) + 4*lh + r%4.
+    // mask: only tiles that cross a diagonal, kv_end or a missing page.  The
+    // lane holds keys kv0 + h*32 + 8*(r/4) + 4*lh + r%4.
     uint32_t bad_pages = 0;
     if constexpr (PAGED) {
       if (any_bad) {
@@ -375,59 +415,79 @@ __global__ __launch_bounds__(kThreads, OCC) void prefill_kernel(PrefillArgs a) {
         }
       }
     }
-    const bool need_mask = (a.causal && kv0 + kBN - 1 > row0) | (kv0 + kBN > kv_end) | (bad_pages != 0);
-    if (need_mask) {
-      const int rel = lim - (kv0 + 4 * lh);      // visible iff key offset <= rel
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int off = h * 32 + 8 * (r / 4) + (r % 4);
-          s[h][r] = off <= rel ? s[h][r] : -INFINITY;
-        }
-      if (bad_pages) {
+    for (int i = 0; i < BPW; ++i) {
+      const bool need_mask = (a.causal && kv0 + kBN - 1 > row0[i]) | (kv0 + kBN > kv_end) | (bad_pages != 0);
+      if (need_mask) {
+        const int rel = lim[i] - (kv0 + 4 * lh);      // visible iff key offset <= rel
 #pragma unroll
         for (int h = 0; h < 2; ++h)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const int pidx = (h * 32 + 8 * (r / 4) + 4 * lh) / kPageTokens;
-            s[h][r] = ((bad_pages >> pidx) & 1u) ? -INFINITY : s[h][r];
+            const int off = h * 32 + 8 * (r / 4) + (r % 4);
+            s[i][h][r] = off <= rel ? s[i][h][r] : -INFINITY;
           }
+        if (bad_pages) {
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int pidx = (h * 32 + 8 * (r / 4) + 4 * lh) / kPageTokens;
+              s[i][h][r] = ((bad_pages >> pidx) & 1u) ? -INFINITY : s[i][h][r];
+            }
+        }
       }
     }
 
-    // tile row max of the raw scores (scale >= 0 keeps the order)
-    float rmax = -INFINITY;
+    // P = 2^(s*c - m) (bf16), the B operands of the PV product: 16 keys each
+    bf16x8 pb[BPW][4];
+    float psum[BPW];
+    auto exps = [&](int i) {
+      float sum = 0.f;
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
+      for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) rmax = fmaxf(rmax, s[h][r]);
-    auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(rmax), __float_as_uint(rmax), false, false);
-    rmax = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-    const float mt = rmax * c;
-    if (__any(mt > m_run + kRescaleSlack)) {
-      const float m_new = fmaxf(m_run, mt);
-      const float corr = fast_exp2(m_run - m_new);
-      m_run = m_new;
-      l_lane *= corr;
+        for (int r = 0; r < 16; ++r) {
+          const float p = fast_exp2(__builtin_fmaf(s[i][h][r], c, -m_run[i]));
+          sum += p;
+          pb[i][h * 2 + r / 8][r % 8] = (__bf16)p;
+        }
+      psum[i] = sum;
+    };
+    // move the running max to the tile max (row max of the raw scores;
+    // scale >= 0 keeps the order) and rescale what is accumulated
+    auto remax = [&](int i) {
+      float rmax = -INFINITY;
 #pragma unroll
-      for (int i = 0; i < D / 32; ++i)
+      for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[i][r] *= corr;
-    }
-
-    // P = 2^(s*c - m) (bf16) as B operands of the PV product: 16 keys each
-    bf16x8 pb[4];
-    float psum = 0.f;
+        for (int r = 0; r < 16; ++r) rmax = fmaxf(rmax, s[i][h][r]);
+      auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(rmax), __float_as_uint(rmax), false, false);
+      rmax = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+      const float m_new = fmaxf(m_run[i], rmax * c);
+      const float corr = fast_exp2(m_run[i] - m_new);
+      m_run[i] = m_new;
+      l_lane[i] *= corr;
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
+      for (int mb = 0; mb < D / 32; ++mb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = fast_exp2(__builtin_fmaf(s[h][r], c, -m_run));
-        psum += p;
-        pb[h * 2 + r / 8][r % 8] = (__bf16)p;
+        for (int r = 0; r < 16; ++r) acc[i][mb][r] *= corr;
+    };
+#pragma unroll
+    for (int i = 0; i < BPW; ++i) {
+      if (!started) {
+        remax(i);
+        exps(i);
+      } else {
+        exps(i);
+        if (__any(!(psum[i] < kSpecLimit))) {   // some p would be too large: redo with the tile max
+          remax(i);
+          exps(i);
+        }
       }
-    l_lane += psum;
+      l_lane[i] += psum[i];
+    }
+    started = true;
 
 #pragma unroll
     for (int mb = 0; mb < D / 32; ++mb) {
@@ -441,7 +501,8 @@ __global__ __launch_bounds__(kThreads, OCC) void prefill_kernel(PrefillArgs a) {
                                                      (__attribute__((address_space(3))) i16x4 *)(src)));
         }
         const bf16x8 va = __builtin_bit_cast(bf16x8, u32x4{part[0].x, part[0].y, part[1].x, part[1].y});
-        acc[mb] = mfma32(va, pb[kk], acc[mb]);
+#pragma unroll
+        for (int i = 0; i < BPW; ++i) acc[i][mb] = mfma32(va, pb[i][kk], acc[i][mb]);
       }
     }
   };
@@ -453,7 +514,7 @@ __global__ __launch_bounds__(kThreads, OCC) void prefill_kernel(PrefillArgs a) {
   // the safe token), so the number in flight is the same on every path and
   // one constant wait is exact; the compiler's own bookkeeping then agrees
   // and adds no drain of its own.
-  auto skip = [&](int t) { return a.causal && t * kBN > row0 + 31; };   // rows all precede the tile
+  auto skip = [&](int t) { return a.causal && t * kBN > wave_row_end; };   // rows all precede the tile
   auto step = [&](int t, auto S_) {
     constexpr int S = decltype(S_)::value;
     wait_vm_lgkm0<(NS - 2) * 2 * NDMA>();
@@ -487,23 +548,27 @@ __global__ __launch_bounds__(kThreads, OCC) void prefill_kernel(PrefillArgs a) {
   if (err_bits && tid == 0) raise_err(a.err, err_bits);
 
   // ---- epilogue: one divide per row, LSE in natural-log units
-  auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_lane), __float_as_uint(l_lane), false, false);
-  const float l_row = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-  const bool has = row < len && l_row > 0.f;
-  const float inv_l = has ? 1.f / l_row : 0.f;
-  if (row < T) {
-    uint16_t *op = a.O + (((int64_t)b * T + row) * Hq + head) * D;
 #pragma unroll
-    for (int mb = 0; mb < D / 32; ++mb)
+  for (int i = 0; i < BPW; ++i) {
+    const int row = row0[i] + lr;
+    auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_lane[i]), __float_as_uint(l_lane[i]), false, false);
+    const float l_row = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+    const bool has = row < len && l_row > 0.f;
+    const float inv_l = has ? 1.f / l_row : 0.f;
+    if (row < T) {
+      uint16_t *op = a.O + (((int64_t)b * T + row) * Hq + head[i]) * D;
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        uint2 w;
-        w.x = has ? pack_bf16x2(acc[mb][4 * g + 0] * inv_l, acc[mb][4 * g + 1] * inv_l) : 0u;
-        w.y = has ? pack_bf16x2(acc[mb][4 * g + 2] * inv_l, acc[mb][4 * g + 3] * inv_l) : 0u;
-        *reinterpret_cast<uint2 *>(op + mb * 32 + 8 * g + 4 * lh) = w;
-      }
-    if (lh == 0)
-      a.LSE[((int64_t)b * Hq + head) * T + row] = has ? (m_run + fast_log2(l_row)) * kLn2 : -INFINITY;
+      for (int mb = 0; mb < D / 32; ++mb)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          uint2 w;
+          w.x = has ? pack_bf16x2(acc[i][mb][4 * g + 0] * inv_l, acc[i][mb][4 * g + 1] * inv_l) : 0u;
+          w.y = has ? pack_bf16x2(acc[i][mb][4 * g + 2] * inv_l, acc[i][mb][4 * g + 3] * inv_l) : 0u;
+          *reinterpret_cast<uint2 *>(op + mb * 32 + 8 * g + 4 * lh) = w;
+        }
+      if (lh == 0)
+        a.LSE[((int64_t)b * Hq + head[i]) * T + row] = has ? (m_run[i] + fast_log2(l_row)) * kLn2 : -INFINITY;
+    }
   }
 }
 
@@ -513,18 +578,25 @@ __global__ __launch_bounds__(kThreads, OCC) void prefill_kernel(PrefillArgs a) {
 #ifndef PA_PREFILL_OCC64
 #define PA_PREFILL_OCC64 3
 #endif
-// ring depth and target waves per SIMD: d=64 keeps 3 tiles in flight (48 KB
-// of LDS, 3 workgroups per CU); d=128 two (64 KB, 2 per CU)
+// Per head size: 32-column blocks per wave (two: every K/V operand read from
+// LDS feeds two MFMAs, at 2 waves per SIMD; one: 3 waves per SIMD, measured
+// faster for d=64), ring depth, and target waves per SIMD.  d=128 keeps one
+// block and a 2-deep ring (64 KB of LDS, 2 workgroups per CU).
+#ifndef PA_PREFILL_BPW64
+#define PA_PREFILL_BPW64 1
+#endif
 template <int D>
 struct PrefillCfg {
+  static constexpr int BPW = D == 64 ? PA_PREFILL_BPW64 : 1;
   static constexpr int NS = D == 64 ? PA_PREFILL_NS64 : 2;
   static constexpr int OCC = D == 64 ? PA_PREFILL_OCC64 : 2;
 };
 
 template <int D, int G, bool PAGED>
 static int launch_prefill_t(PrefillArgs a, hipStream_t stream) {
-  constexpr int HW = G < kWaves ? G : kWaves;
-  constexpr int RW = kWaves / HW;
+  using C = PrefillCfg<D>;
+  constexpr int HW = G < kBlocks ? G : kBlocks;
+  constexpr int RW = kBlocks / HW;
   constexpr int BM = 32 * RW;
   const int Hq = a.Hkv * G;
   a.n_hgroups = Hq / HW;
@@ -532,8 +604,8 @@ static int launch_prefill_t(PrefillArgs a, hipStream_t stream) {
   const int64_t grid = (int64_t)a.B * a.n_hgroups * a.n_rowblocks;
   if (grid == 0) return PA_OK;
   if (grid > 0x7fffffff) return PA_ERR_RANGE;
-  hipLaunchKernelGGL((prefill_kernel<D, G, PAGED, PrefillCfg<D>::NS, PrefillCfg<D>::OCC>), dim3((unsigned)grid),
-                     dim3(kThreads), 0, stream, a);
+  hipLaunchKernelGGL((prefill_kernel<D, G, PAGED, C::NS, C::OCC, C::BPW>), dim3((unsigned)grid),
+                     dim3(64 * (kBlocks / C::BPW)), 0, stream, a);
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
 

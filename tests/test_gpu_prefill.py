@@ -43,6 +43,43 @@ def test_prefill_ragged(Hq, Hkv, d, causal):
     assert torch.all(O[4] == 0) and torch.all(torch.isneginf(L[4]))
 
 
+def _ramped(k: torch.Tensor, pos: torch.Tensor, top: float) -> torch.Tensor:
+    """|k| scaled by 1 + top*pos/max(pos): with |q| the scores climb along the keys."""
+    ramp = 1.0 + top * pos.float() / max(1, int(pos.max()))
+    return (k.float().abs() * ramp.view(-1, *([1] * (k.dim() - 1)))).to(torch.bfloat16)
+
+
+@pytest.mark.parametrize("top", [15.0, 40.0])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [True, False])
+def test_prefill_climbing_scores(top, d, causal):
+    """Scores that rise by tens (top=15) to hundreds (top=40) of log2 units from
+    one key tile to the next, so the kernel's reference max has to move after
+    a row's first tile, sometimes by more than its 2^64 allowance in one step.
+    Attention then sits on a few keys, so O is close to single V rows; V is
+    scaled by 1/4 to keep |O| in the range the absolute O tolerance is set
+    for (P in bf16 bounds the O error by 2^-9 max|V| plus rounding of O)."""
+    lens = [300, 257]
+    case = W.make_prefill("climbing", B=2, T=300, Hq=8, Hkv=2, d=d, n_pages=64, seed=int(top) + d,
+                          seq_lens=lens, causal=causal)
+    case.q = case.q.float().abs().to(torch.bfloat16)
+    t = case.tokens
+    t.k = _ramped(t.k, torch.as_tensor(t.positions), top)
+    t.v = (t.v.float() * 0.25).to(torch.bfloat16)
+    _full_parity(case)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_dense_climbing_scores(d):
+    case = W.make_dense("climbing", B=2, T=330, Hq=8, Hkv=2, d=d, causal=True, seed=5)
+    case.q = case.q.float().abs().to(torch.bfloat16)
+    pos = torch.arange(case.k.shape[1]).repeat(case.k.shape[0])
+    k = _ramped(case.k.reshape(-1, *case.k.shape[2:]), pos, 30.0)
+    case.k = k.reshape(case.k.shape)
+    case.v = (case.v.float() * 0.25).to(torch.bfloat16)
+    _dense_parity(case)
+
+
 def test_prefill_llama_sampled_rows():
     case = W.llama_prefill()
     O, L, _ = run_prefill(case)
