@@ -74,30 +74,43 @@ def capture(fn, reps: int = 1) -> torch.cuda.CUDAGraph:
 
 
 def kernel_time(fn, reps: int = 20, trials: int = 5) -> float:
-    """Mean device time (s) of one call of fn: a graph of `reps` back-to-back
-    calls is replayed between two HIP events on the launching stream; the
-    best of `trials` replays is kept."""
+    """Average device time (s) of one call of fn: a graph of `reps` back-to-back
+    calls is replayed `trials` times between two HIP events on the launching
+    stream (after one untimed replay); total time / (reps * trials)."""
     g = capture(fn, reps)
-    best = float("inf")
+    g.replay()
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
     for _ in range(trials):
-        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        s.record()
         g.replay()
-        e.record()
-        torch.cuda.synchronize()
-        best = min(best, s.elapsed_time(e) / 1e3 / reps)
-    return best
+    e.record()
+    torch.cuda.synchronize()
+    return s.elapsed_time(e) / 1e3 / (reps * trials)
 
 
-def timed_steps(graphs, steps: int, warmup: int) -> float:
-    """Wall time (s) of `steps` graph-replayed steps after `warmup`, bracketed
-    by device syncs; step i replays graphs[i % len(graphs)]."""
-    for i in range(warmup):
-        graphs[i % len(graphs)].replay()
+def timed_steps(step_fns, steps: int, warmup: int, per_graph: int = 8) -> float:
+    """Wall time (s) of exactly `steps` steps after `warmup`, bracketed by device
+    syncs.  Step i runs step_fns[i % n]; the steps are replayed from HIP graphs
+    of `per_graph` consecutive steps (a multiple of n) plus one graph of the
+    remainder, so the host launches one graph per `per_graph` steps."""
+    n = len(step_fns)
+    per_graph = max(n, per_graph - per_graph % n)
+
+    def steps_graph(count: int):
+        return capture(lambda: [step_fns[j % n]() for j in range(count)])
+
+    full = steps_graph(per_graph)
+    rem = steps % per_graph
+    tail = steps_graph(rem) if rem else None
+    for _ in range(-(-warmup // per_graph)):
+        full.replay()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(steps):
-        graphs[i % len(graphs)].replay()
+    for _ in range(steps // per_graph):
+        full.replay()
+    if tail is not None:
+        tail.replay()
     torch.cuda.synchronize()
     return time.perf_counter() - t0
 
@@ -116,8 +129,8 @@ def source_digest(*names: str) -> str:
 # was taken on (digest of the .hip files), null otherwise.
 TRAFFIC = {
     # kernel: (source digest, fetched bytes, written bytes)
-    "prefill": ("d26f8685317684ef", 25323131, 17301504),
-    "decode": ("64158c1b145b3a25", 152454348, 278528),
+    "prefill": ("2c6f52cb2a4cdc20", 25448050, 17301504),
+    "decode": ("b4ffccba2f648b7e", 154503880, 278528),
 }
 
 
@@ -160,8 +173,7 @@ def bench_prefill(steps: int, warmup: int):
     step()
     torch.cuda.synchronize()
     O_ref, L_ref = O.clone(), L.clone()
-    g = capture(step)
-    wall = timed_steps([g], steps, warmup)
+    wall = timed_steps([step], steps, warmup)
     assert torch.equal(O, O_ref) and torch.equal(L, L_ref), "graph replay differs from eager"
     flops = prefill_flops(case.B, case.T, case.Hq, case.d, True)
     alg_bytes = (q.numel() + O.numel()) * 2 + L.numel() * 4 + 2 * k.numel() * 2
@@ -218,8 +230,7 @@ def bench_decode(steps: int, warmup: int, replicas: int = 8):
     step(0)
     torch.cuda.synchronize()
     O_ref, L_ref = O.clone(), L.clone()
-    graphs = [capture(lambda r=r: step(r)) for r in range(replicas)]
-    wall = timed_steps(graphs, steps, warmup)
+    wall = timed_steps([lambda r=r: step(r) for r in range(replicas)], steps, warmup)
     assert torch.equal(O, O_ref) and torch.equal(L, L_ref), "graph replay differs from eager"
     n_ctx = int(case.ctx_lens.sum())
     kv_bytes = n_ctx * c.n_kv_heads * case.d * 2 * 2

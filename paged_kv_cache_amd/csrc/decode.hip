@@ -29,10 +29,14 @@
 // chunks XOR-swizzled per token against bank conflicts) and read back with
 // the gfx950 transposing LDS read, 4 tokens of one d column per read.
 //
-// Pipeline.  The loads of a wavefront's next chunk are in flight while its
-// current chunk is computed (two register sets used in turn).  A missing page
-// is never dereferenced: its lanes read page 0 instead and its tokens are
-// masked.
+// Pipeline.  A ring of register chunks: the loads of a wavefront's next
+// chunk are in flight while its current chunk is computed.  Every step
+// issues the same loads (a chunk past the end reads a safe page), so the
+// compiler's wait before a chunk's first use covers that chunk only.  A
+// missing page is never dereferenced: its lanes read the safe page instead
+// and its tokens are masked.
+
+#include <type_traits>
 
 #include "device.h"
 #include "kernels.h"
@@ -48,7 +52,14 @@ constexpr int kChunk = 32;             // tokens per wavefront step (two pages)
 #ifndef PA_DECODE_MIN_WAVES_PER_SIMD
 #define PA_DECODE_MIN_WAVES_PER_SIMD 2
 #endif
+#ifndef PA_DECODE_TARGET_WAVES
+#define PA_DECODE_TARGET_WAVES 4096
+#endif
+#ifndef PA_DECODE_RING
+#define PA_DECODE_RING 2
+#endif
 constexpr int kWaves = PA_DECODE_WAVES;  // wavefronts per workgroup
+constexpr int kRing = PA_DECODE_RING;    // chunks per wavefront in the register ring
 constexpr float kRescaleSlack = 8.f;   // see prefill.hip: lazy max, p <= 2^8
 constexpr float kMaxFloor = -1e30f;
 
@@ -88,8 +99,8 @@ __device__ __forceinline__ float rows_sum(float x) {
 
 template <int D>
 struct Chunk {
-  uint4 k[2][D / 32];   // [16-token half][16-byte piece]
-  uint4 v[2][D / 32];
+  u32x4 k[2][D / 32];   // [16-token half][16-byte piece]
+  u32x4 v[2][D / 32];
   bool ok[2];           // the half's page exists
 };
 
@@ -151,17 +162,19 @@ __global__ __launch_bounds__(64 * kWaves, PA_DECODE_MIN_WAVES_PER_SIMD) void dec
   const int64_t row_bytes = (int64_t)a.Hkv * D * 2;
   const int64_t page_bytes = row_bytes * 2 * kPageTokens;
   const int64_t v_offset = page_bytes / 2;
-  // this lane's pieces inside a page: token lrow, kv head, d = lgrp*(D/4) ..
-  const int64_t lane_off = (int64_t)lrow * row_bytes + (int64_t)kvh * D * 2 + (int64_t)lgrp * (D / 4) * 2;
+  // this lane's pieces inside a page: token lrow, kv head, 16 bytes at
+  // p*64 + lgrp*16 of the head row for piece p, so that each load
+  // instruction reads 64 contiguous bytes of every one of its 16 rows
+  const int64_t lane_off = (int64_t)lrow * row_bytes + (int64_t)kvh * D * 2 + (int64_t)lgrp * 16;
 
-  // Q^T as the B operand: column lrow -> q head kvh*G + lrow%G; contraction
-  // slots hold d = lgrp*(D/4) + piece*8 + i
+  // Q^T as the B operand: column lrow -> q head kvh*G + lrow%G; the
+  // contraction slots of piece p hold d = p*32 + lgrp*8 + i (as K's)
   bf16x8 qb[P];
   {
     const int hq = kvh * G + (lrow % G);
-    const uint4 *qp = reinterpret_cast<const uint4 *>(a.q + ((int64_t)b * Hq + hq) * D + lgrp * (D / 4));
+    const uint16_t *qp = a.q + ((int64_t)b * Hq + hq) * D + lgrp * 8;
 #pragma unroll
-    for (int p = 0; p < P; ++p) qb[p] = __builtin_bit_cast(bf16x8, qp[p]);
+    for (int p = 0; p < P; ++p) qb[p] = *reinterpret_cast<const bf16x8 *>(qp + p * 32);
   }
 
   f32x4 acc[D / 16];
@@ -172,38 +185,57 @@ __global__ __launch_bounds__(64 * kWaves, PA_DECODE_MIN_WAVES_PER_SIMD) void dec
   const float c = a.scale_log2;
   uint16_t *vw = vl[w];
 
-  auto load = [&](Chunk<D> &r, int c0) {
+  // ---- this wavefront's chunks: number i covers tokens from t_begin + (w + kWaves*i)*kChunk
+  const int stride = kWaves * kChunk;
+  const int first_tok = t_begin + w * kChunk;
+  const int n_my = first_tok < t_end ? (t_end - first_tok + stride - 1) / stride : 0;
+  // block-table row read through the constant address space: a uniform
+  // entry is then always a scalar load
+  const const_i32_ptr trow_c = as_const(trow);
+  // page the loads of a missing page or of a chunk past the end read
+  // instead (their tokens never count): the split's first page, else page 0
+  int64_t safe_page = 0;
+  if (t_end > t_begin) {
+    const int32_t e = trow_c[t_begin / kPageTokens];
+    if (e >= 0 && (int64_t)e < a.n_pages) safe_page = e;
+  }
+  // Issue the loads of chunk i.  Every call issues the same loads, also past
+  // the end, so that the number of loads in flight is the same on every path
+  // and the compiler's wait before a chunk's use covers exactly that chunk.
+  auto issue = [&](Chunk<D> &r, int i) {
+    const int c0 = t_begin + (w + kWaves * i) * kChunk;
+    const bool real = i < n_my;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int first = c0 + 16 * h;
       int64_t page = -1;
-      if (first < t_end) {               // uniform: the same entry for every lane
-        const int32_t e = trow[uniform(first / kPageTokens)];
+      if (real && first < t_end) {          // uniform: the same entry for every lane
+        const int32_t e = trow_c[first / kPageTokens];
         page = (e < 0 || (int64_t)e >= a.n_pages) ? -1 : (int64_t)e;
         if (page < 0) err_bits |= PA_DEVERR_BAD_PAGE;
       }
       r.ok[h] = page >= 0;
-      const uint8_t *base = a.pool + (page < 0 ? 0 : page) * page_bytes + lane_off;
+      const uint8_t *base = a.pool + (page < 0 ? safe_page : page) * page_bytes + lane_off;
 #pragma unroll
       for (int p = 0; p < P; ++p) {
-        r.k[h][p] = *reinterpret_cast<const uint4 *>(base + p * 16);
-        r.v[h][p] = *reinterpret_cast<const uint4 *>(base + v_offset + p * 16);
+        r.k[h][p] = *reinterpret_cast<const u32x4 *>(base + p * 64);
+        r.v[h][p] = *reinterpret_cast<const u32x4 *>(base + v_offset + p * 64);
       }
     }
   };
 
   auto process = [&](const Chunk<D> &r, int c0) {
     const bool tail = (c0 + kChunk > t_end) | !r.ok[0] | !r.ok[1];
-    // stage V (token 16h + lrow, chunk lgrp*P + p), zero rows that must not count
+    // stage V (token 16h + lrow, chunk 4p + lgrp), zero rows that must not count
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int tok = 16 * h + lrow;
       const bool keep = !tail || (r.ok[h] && c0 + tok < t_end);
 #pragma unroll
       for (int p = 0; p < P; ++p) {
-        const int ch = lgrp * P + p;
-        *reinterpret_cast<uint4 *>(&vw[tok * D + (ch ^ swz(tok)) * 8]) =
-            keep ? r.v[h][p] : uint4{0u, 0u, 0u, 0u};
+        const int ch = 4 * p + lgrp;
+        *reinterpret_cast<u32x4 *>(&vw[tok * D + (ch ^ swz(tok)) * 8]) =
+            keep ? r.v[h][p] : u32x4{0u, 0u, 0u, 0u};
       }
     }
 
@@ -271,17 +303,40 @@ __global__ __launch_bounds__(64 * kWaves, PA_DECODE_MIN_WAVES_PER_SIMD) void dec
     }
   };
 
-  // this wavefront's chunks: t_begin + (w + kWaves*i) * kChunk
-  const int stride = kWaves * kChunk;
-  Chunk<D> ca, cb;
-  int c0 = t_begin + w * kChunk;
-  if (c0 < t_end) load(ca, c0);
-  for (; c0 < t_end; c0 += 2 * stride) {
-    if (c0 + stride < t_end) load(cb, c0 + stride);
-    process(ca, c0);
-    if (c0 + stride >= t_end) break;
-    if (c0 + 2 * stride < t_end) load(ca, c0 + 2 * stride);
-    process(cb, c0 + stride);
+  // ---- ring of NCH register chunks: chunk i is processed while chunks
+  // i+1 .. i+NCH-1 are in flight
+  Chunk<D> r0, r1, r2, r3;
+  auto buf = [&](auto S_) -> Chunk<D> & {
+    constexpr int S = decltype(S_)::value;
+    if constexpr (S == 0) return r0;
+    else if constexpr (S == 1) return r1;
+    else if constexpr (S == 2) return r2;
+    else return r3;
+  };
+  constexpr int NR = D == 64 ? kRing : 2;   // d=128: two chunks (registers)
+  auto step = [&](int i, auto S_) {
+    constexpr int S = decltype(S_)::value;
+    issue(buf(std::integral_constant<int, (S + NR - 1) % NR>{}), i + NR - 1);
+    process(buf(S_), t_begin + (w + kWaves * i) * kChunk);
+  };
+  if (n_my > 0) {
+    issue(r0, 0);
+    if constexpr (NR > 2) issue(r1, 1);
+    if constexpr (NR > 3) issue(r2, 2);
+    for (int i = 0;;) {
+      step(i, std::integral_constant<int, 0>{});
+      if (++i >= n_my) break;
+      step(i, std::integral_constant<int, 1 % NR>{});
+      if (++i >= n_my) break;
+      if constexpr (NR > 2) {
+        step(i, std::integral_constant<int, 2 % NR>{});
+        if (++i >= n_my) break;
+      }
+      if constexpr (NR > 3) {
+        step(i, std::integral_constant<int, 3 % NR>{});
+        if (++i >= n_my) break;
+      }
+    }
   }
 
   if (err_bits && lane == 0) raise_err(a.err, err_bits);
@@ -368,7 +423,7 @@ Split split_policy(int B, int Hq, int Hkv, int D, int max_ctx) {
   auto up = [](int64_t x) { return (x + 255) / 256 * 256; };
   Split s{};
   const int64_t groups = (int64_t)B * Hkv;
-  int64_t n = (4096 + groups * kWaves - 1) / (groups * kWaves);
+  int64_t n = (PA_DECODE_TARGET_WAVES + groups * kWaves - 1) / (groups * kWaves);
   const int64_t min_tokens = 2LL * kWaves * kChunk;
   const int64_t n_max = max_ctx <= 0 ? 1 : (max_ctx + min_tokens - 1) / min_tokens;
   if (n > n_max) n = n_max;
