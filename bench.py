@@ -317,6 +317,84 @@ def kernels_only(n: int) -> None:
     print(f"kernels-only: {n} launches each", flush=True)
 
 
+def sweep() -> None:
+    """The other configurations' measurements (one line each, then a
+    markdown table): the 17-token prompt (latency), the dense FA2-shape grid
+    (MHA, d 64 / 128, T 512..16k, B*T = 16k, causal and full), the long dense
+    prefill (B=1, T=16384, 16x128, causal) and the long decode (4 x 16384).
+    Kernel times are HIP-event averages over graph replays (kernel_time)."""
+    rows = []
+
+    def emit(name, us, metric, unit, extra=""):
+        rows.append((name, us, metric, unit, extra))
+        print(f"sweep: {name}: {us:.2f} us, {metric:.2f} {unit} {extra}", flush=True)
+
+    # 17-token prefill: scatter and prefill separately
+    case = W.tiny_prefill()
+    c = case.cache
+    pool = device_pool(c)
+    bt = i32(c.block_table)
+    k, v = case.tokens.k.to(DEV), case.tokens.v.to(DEV)
+    slots, pos = i32(case.tokens.slot_ids), i32(case.tokens.positions)
+    q, lens, sid = case.q.to(DEV), i32(case.seq_lens), i32(case.slot_ids)
+    t_sc = kernel_time(lambda: pa.kv_scatter(k, v, slots, pos, pool, bt, c.layer))
+    t_pf = kernel_time(lambda: pa.attn_prefill(q, pool, bt, c.layer, lens, c.n_kv_heads, case.scale,
+                                               True, slot_ids=sid))
+    emit("17-token kv_scatter", t_sc * 1e6, t_sc * 1e6, "us")
+    emit("17-token prefill (32/8/64, paged)", t_pf * 1e6, prefill_flops(1, 17, 32, 64, True) / t_pf / 1e9,
+         "GFLOP/s")
+    del pool
+
+    # dense FA2 shapes
+    for d, H in W.FA2_HEADS:
+        for T in W.FA2_SEQLENS:
+            res = {}
+            for causal in (False, True):
+                dc = W.fa2_dense(T, d, causal)
+                qd, kd, vd = dc.q.to(DEV), dc.k.to(DEV), dc.v.to(DEV)
+                Od = torch.empty_like(qd)
+                Ld = torch.empty(dc.q.shape[0], H, T, dtype=torch.float32, device=DEV)
+                t = kernel_time(lambda: pa.attn_prefill_dense(qd, kd, vd, dc.scale, causal, out=Od, lse=Ld),
+                                reps=10, trials=3)
+                B = 16384 // T
+                res[causal] = t
+                emit(f"dense d={d} H={H} T={T} B={B} {'causal' if causal else 'full'}", t * 1e6,
+                     prefill_flops(B, T, H, d, causal) / t / 1e12, "TFLOP/s")
+                del qd, kd, vd, Od, Ld
+            rows[-1] = rows[-1][:4] + (f"full/causal time ratio {res[False] / res[True]:.2f}",)
+
+    # long dense prefill
+    lc = W.long_prefill()
+    ql, kl, vl = lc.q.to(DEV), lc.k.to(DEV), lc.v.to(DEV)
+    t = kernel_time(lambda: pa.attn_prefill_dense(ql, kl, vl, lc.scale, True), reps=5, trials=3)
+    emit("long prefill B=1 T=16384 16x128 causal (dense)", t * 1e6,
+         prefill_flops(1, 16384, 16, 128, True) / t / 1e12, "TFLOP/s")
+    del ql, kl, vl
+
+    # long decode, 2 page-disjoint replicas cycled
+    dcase = W.long_decode()
+    c = dcase.cache
+    pool = device_pool(c)
+    tables = [i32(tb) for tb in decode_replicas(dcase, 2)]
+    for tb in tables:
+        for tok in (dcase.context, dcase.new_tokens):
+            pa.kv_scatter(tok.k.to(DEV), tok.v.to(DEV), i32(tok.slot_ids), i32(tok.positions), pool, tb,
+                          c.layer)
+    qd, lens, sid = dcase.q.to(DEV), i32(dcase.ctx_lens), i32(dcase.slot_ids)
+    ws = pa.decode_workspace(dcase.B, dcase.Hq, c.n_kv_heads, dcase.d, dcase.max_ctx, DEV)
+    t = kernel_time(lambda: [pa.attn_decode(qd, pool, tb, c.layer, lens, c.n_kv_heads, dcase.scale,
+                                            dcase.max_ctx, slot_ids=sid, workspace=ws) for tb in tables],
+                    reps=4) / len(tables)
+    kvb = int(dcase.ctx_lens.sum()) * c.n_kv_heads * dcase.d * 2 * 2
+    n_splits = pa.decode_splits(dcase.B, dcase.Hq, c.n_kv_heads, dcase.d, dcase.max_ctx)
+    emit("long decode 4 x 16384 (32/8/64, paged)", t * 1e6, kvb / t / 1e9, "GB/s",
+         f"{n_splits} workgroup splits per context (+ combine kernel)")
+
+    print("\n| workload | time (us) | throughput | note |\n|---|---:|---:|---|")
+    for name, us, metric, unit, extra in rows:
+        print(f"| {name} | {us:.2f} | {metric:.2f} {unit} | {extra} |")
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -325,6 +403,9 @@ def main() -> int:
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--kernels-only", type=int, default=0, metavar="N",
                     help="launch each dominant kernel N times for a counter run; no JSON")
+    ap.add_argument("--sweep", action="store_true",
+                    help="measure the other configurations (17-token prompt, dense FA2 grid, "
+                         "long prefill, long decode); no JSON")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -334,6 +415,9 @@ def main() -> int:
     pa.load()
     if args.kernels_only:
         kernels_only(args.kernels_only)
+        return 0
+    if args.sweep:
+        sweep()
         return 0
 
     p = bench_prefill(args.steps, args.warmup)

@@ -139,6 +139,14 @@ def decode_workspace_size(B: int, Hq: int, Hkv: int, head_dim: int, max_ctx: int
     return int(load().attn_decode_workspace_size(B, Hq, Hkv, head_dim, max_ctx))
 
 
+def decode_splits(B: int, Hq: int, Hkv: int, head_dim: int, max_ctx: int) -> int:
+    """Workgroup splits per context that attn_decode uses for this shape (1: no
+    workspace).  Read off the workspace size, whose fp32 partial outputs
+    [B, Hq, splits, head_dim] dominate it."""
+    ws = decode_workspace_size(B, Hq, Hkv, head_dim, max_ctx)
+    return 1 if ws == 0 else ws // (B * Hq * head_dim * 4)
+
+
 def decode_workspace(B: int, Hq: int, Hkv: int, head_dim: int, max_ctx: int,
                      device=None) -> torch.Tensor:
     """A decode workspace of the size attn_decode needs for this shape (may be 16 B)."""

@@ -29,12 +29,17 @@
 // chunks XOR-swizzled per token against bank conflicts) and read back with
 // the gfx950 transposing LDS read, 4 tokens of one d column per read.
 //
-// Pipeline.  A ring of register chunks: the loads of a wavefront's next
-// chunk are in flight while its current chunk is computed.  Every step
-// issues the same loads (a chunk past the end reads a safe page), so the
-// compiler's wait before a chunk's first use covers that chunk only.  A
-// missing page is never dereferenced: its lanes read the safe page instead
-// and its tokens are masked.
+// Pipeline.  Two register steps used in turn: the loads of a wavefront's
+// next step are in flight while its current step is computed.  Exactly one
+// step is in flight at the top of every iteration on every path (the last
+// step is processed in a branch of its own), so the compiler's wait before a
+// chunk's first use covers that chunk only, and nothing is loaded past the
+// end.  A missing page is never dereferenced: its lanes read a safe page (the
+// split's first valid one) instead and its tokens are masked.
+//
+// Order.  Workgroups are launched in id order into free slots; the r-th row
+// of workgroups takes the r-th longest context, so the longest work starts
+// first and the CUs finish together (contexts differ by up to 2048x).
 
 #include <type_traits>
 
@@ -55,15 +60,17 @@ constexpr int kChunk = 32;             // tokens per wavefront step (two pages)
 #ifndef PA_DECODE_TARGET_WAVES
 #define PA_DECODE_TARGET_WAVES 4096
 #endif
-#ifndef PA_DECODE_RING
-#define PA_DECODE_RING 2
+#ifndef PA_DECODE_SUB
+#define PA_DECODE_SUB 1
 #endif
 constexpr int kWaves = PA_DECODE_WAVES;  // wavefronts per workgroup
-constexpr int kRing = PA_DECODE_RING;    // chunks per wavefront in the register ring
 constexpr float kRescaleSlack = 8.f;   // see prefill.hip: lazy max, p <= 2^8
 constexpr float kMaxFloor = -1e30f;
 
+constexpr int kSortMax = 512;   // batches up to this are scheduled longest context first
+
 struct DecodeArgs {
+  int B;
   const uint16_t *q;            // [B][Hq][D]
   const uint8_t *pool;
   int64_t n_pages;
@@ -126,6 +133,7 @@ __device__ __forceinline__ int clamped_ctx(const DecodeArgs &a, int b, int *slot
 
 template <int D, int G>
 __global__ __launch_bounds__(64 * kWaves, PA_DECODE_MIN_WAVES_PER_SIMD) void decode_kernel(DecodeArgs a) {
+  constexpr int kSub = D == 64 ? PA_DECODE_SUB : 1;   // chunks per step (registers: d=128 one)
   static_assert(D % 32 == 0 && 16 % G == 0, "unsupported shape");
   constexpr int P = D / 32;          // 16-byte pieces per lane per token row
   constexpr int CH = D / 8;          // 16-byte chunks per V row
@@ -142,10 +150,33 @@ __global__ __launch_bounds__(64 * kWaves, PA_DECODE_MIN_WAVES_PER_SIMD) void dec
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lrow = lane & 15;        // MFMA row/column lane index
   const int lgrp = lane >> 4;        // MFMA k-group / output row group
+  // ---- workgroup -> (sequence, kv head, split).  Sequences are taken
+  // longest context first (the r-th workgroup row gets the r-th longest
+  // sequence, ties by index): workgroups are launched in id order into free
+  // slots, so this schedules the longest work first and the CUs finish
+  // together.  Batches above kSortMax keep the identity order.
   const int xs = blockIdx.x % a.n_xsplits;
   const int rest = blockIdx.x / a.n_xsplits;
   const int kvh = rest % a.Hkv;
-  const int b = rest / a.Hkv;
+  int b = rest / a.Hkv;
+  if (a.B <= kSortMax) {
+    __shared__ int lens_s[kSortMax];
+    __shared__ int sorted_b;
+    auto key = [&](int x) { return x < 0 ? 0 : min(x, a.max_ctx); };
+    for (int i = tid; i < a.B; i += 64 * kWaves) lens_s[i] = key(a.ctx_lens[i]);
+    __syncthreads();
+    for (int i = tid; i < a.B; i += 64 * kWaves) {
+      const int li = lens_s[i];
+      int rank = 0;
+      for (int j = 0; j < a.B; ++j) {
+        const int lj = lens_s[j];
+        rank += (lj > li) | ((lj == li) & (j < i));
+      }
+      if (rank == b) sorted_b = i;
+    }
+    __syncthreads();
+    b = uniform(sorted_b);
+  }
   const int Hq = a.Hkv * G;
 
   // Errors are collected here and reported once at the end: a global atomic
@@ -185,9 +216,10 @@ __global__ __launch_bounds__(64 * kWaves, PA_DECODE_MIN_WAVES_PER_SIMD) void dec
   const float c = a.scale_log2;
   uint16_t *vw = vl[w];
 
-  // ---- this wavefront's chunks: number i covers tokens from t_begin + (w + kWaves*i)*kChunk
-  const int stride = kWaves * kChunk;
-  const int first_tok = t_begin + w * kChunk;
+  // ---- this wavefront's steps: step i covers the kSub chunks from token
+  // t_begin + (w + kWaves*i)*kChunk*kSub
+  const int stride = kWaves * kChunk * kSub;
+  const int first_tok = t_begin + w * kChunk * kSub;
   const int n_my = first_tok < t_end ? (t_end - first_tok + stride - 1) / stride : 0;
   // block-table row read through the constant address space: a uniform
   // entry is then always a scalar load
@@ -202,14 +234,12 @@ __global__ __launch_bounds__(64 * kWaves, PA_DECODE_MIN_WAVES_PER_SIMD) void dec
   // Issue the loads of chunk i.  Every call issues the same loads, also past
   // the end, so that the number of loads in flight is the same on every path
   // and the compiler's wait before a chunk's use covers exactly that chunk.
-  auto issue = [&](Chunk<D> &r, int i) {
-    const int c0 = t_begin + (w + kWaves * i) * kChunk;
-    const bool real = i < n_my;
+  auto issue = [&](Chunk<D> &r, int c0) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int first = c0 + 16 * h;
       int64_t page = -1;
-      if (real && first < t_end) {          // uniform: the same entry for every lane
+      if (first < t_end) {                  // uniform: the same entry for every lane
         const int32_t e = trow_c[first / kPageTokens];
         page = (e < 0 || (int64_t)e >= a.n_pages) ? -1 : (int64_t)e;
         if (page < 0) err_bits |= PA_DEVERR_BAD_PAGE;
@@ -303,39 +333,44 @@ __global__ __launch_bounds__(64 * kWaves, PA_DECODE_MIN_WAVES_PER_SIMD) void dec
     }
   };
 
-  // ---- ring of NCH register chunks: chunk i is processed while chunks
-  // i+1 .. i+NCH-1 are in flight
-  Chunk<D> r0, r1, r2, r3;
-  auto buf = [&](auto S_) -> Chunk<D> & {
-    constexpr int S = decltype(S_)::value;
-    if constexpr (S == 0) return r0;
-    else if constexpr (S == 1) return r1;
-    else if constexpr (S == 2) return r2;
-    else return r3;
+  // ---- ring of register steps: step i is processed while step i+1 is in
+  // flight.  A step is kSub chunks (kSub*32 tokens): the more bytes a step
+  // moves, the fewer latency-bound steps a workgroup takes.
+  struct Step {
+    Chunk<D> c[kSub];
   };
-  constexpr int NR = D == 64 ? kRing : 2;   // d=128: two chunks (registers)
-  auto step = [&](int i, auto S_) {
-    constexpr int S = decltype(S_)::value;
-    issue(buf(std::integral_constant<int, (S + NR - 1) % NR>{}), i + NR - 1);
-    process(buf(S_), t_begin + (w + kWaves * i) * kChunk);
+  Step r0, r1;
+  auto issue_step = [&](Step &st, int i) {
+#pragma unroll
+    for (int j = 0; j < kSub; ++j) issue(st.c[j], t_begin + ((w + kWaves * i) * kSub + j) * kChunk);
   };
+  auto process_step = [&](Step &st, int i) {
+#pragma unroll
+    for (int j = 0; j < kSub; ++j) {
+      const int c0 = t_begin + ((w + kWaves * i) * kSub + j) * kChunk;
+      if (c0 < t_end) process(st.c[j], c0);
+    }
+  };
+  // Exactly one step is in flight at the top of every iteration, on every
+  // path; the last step is processed in a branch of its own, with nothing
+  // issued after it, so no load is made past the end.
   if (n_my > 0) {
-    issue(r0, 0);
-    if constexpr (NR > 2) issue(r1, 1);
-    if constexpr (NR > 3) issue(r2, 2);
+    issue_step(r0, 0);
     for (int i = 0;;) {
-      step(i, std::integral_constant<int, 0>{});
-      if (++i >= n_my) break;
-      step(i, std::integral_constant<int, 1 % NR>{});
-      if (++i >= n_my) break;
-      if constexpr (NR > 2) {
-        step(i, std::integral_constant<int, 2 % NR>{});
-        if (++i >= n_my) break;
+      if (i + 1 >= n_my) {
+        process_step(r0, i);
+        break;
       }
-      if constexpr (NR > 3) {
-        step(i, std::integral_constant<int, 3 % NR>{});
-        if (++i >= n_my) break;
+      issue_step(r1, i + 1);
+      process_step(r0, i);
+      ++i;
+      if (i + 1 >= n_my) {
+        process_step(r1, i);
+        break;
       }
+      issue_step(r0, i + 1);
+      process_step(r1, i);
+      ++i;
     }
   }
 
@@ -466,6 +501,7 @@ int launch_decode(const void *q, const void *kv_cache, int64_t n_pages, const in
   const Split s = split_policy(B, Hq, Hkv, D, max_ctx);
   uint8_t *ws = static_cast<uint8_t *>(workspace);
   DecodeArgs a{};
+  a.B = B;
   a.q = static_cast<const uint16_t *>(q);
   a.pool = static_cast<const uint8_t *>(kv_cache);
   a.n_pages = n_pages;

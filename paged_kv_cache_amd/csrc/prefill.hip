@@ -212,6 +212,20 @@ __global__ __launch_bounds__(64 * (kBlocks / BPW), OCC) void prefill_kernel(Pref
     lim[i] = row < len ? (a.causal ? row : len - 1) : -1;
   }
 
+  // ---- Q^T as B operands: lane holds row row0[i] + lr, d = lh*(D/2) + k*8 + e
+  // A padding row (row >= len) takes the sequence's row 0 instead: its
+  // results are never written (O = 0, LSE = -inf), and a real row keeps its
+  // scores finite.  (Unconditional loads: no wait between them.)
+  bf16x8 qf[BPW][D / 16];
+#pragma unroll
+  for (int i = 0; i < BPW; ++i) {
+    const int row = row0[i] + lr;
+    const bf16x8 *qp = reinterpret_cast<const bf16x8 *>(
+        a.q + (((int64_t)b * T + (row < len ? row : 0)) * Hq + head[i]) * D + lh * (D / 2));
+#pragma unroll
+    for (int k = 0; k < D / 16; ++k) qf[i][k] = qp[k];
+  }
+
   // ---- pages: validated once for the whole workgroup.  A key that must not
   // count (past kv_end, or on a missing page) is fetched from a safe token
   // instead (token 0 of the first valid block, or of pool page 0 if there is
@@ -219,7 +233,13 @@ __global__ __launch_bounds__(64 * (kBlocks / BPW), OCC) void prefill_kernel(Pref
   // its score is masked.
   bool any_bad = false;
   int64_t safe_page = 0;
+  int32_t raw0[PPW];   // first window of this wave's pages, read with the pass below
   if constexpr (PAGED) {
+#pragma unroll
+    for (int pp = 0; pp < PPW; ++pp) {
+      const int blk = lane * (kBN / kPageTokens) + wave * PPW + pp;
+      raw0[pp] = blk < nblk ? trow_v[blk] : -1;
+    }
     bool found = false;
     for (int b0 = 0; b0 < nblk; b0 += 64) {
       const int blk = b0 + lane;
@@ -240,25 +260,6 @@ __global__ __launch_bounds__(64 * (kBlocks / BPW), OCC) void prefill_kernel(Pref
     const int32_t v = trow[blk];
     return v >= 0 && (int64_t)v < a.n_pages;
   };
-
-  // ---- Q^T as B operands: lane holds row row0[i] + lr, d = lh*(D/2) + k*8 + e
-  bf16x8 qf[BPW][D / 16];
-#pragma unroll
-  for (int i = 0; i < BPW; ++i) {
-    const int row = row0[i] + lr;
-    const bool ok = row < len;
-    const u32x4 *qp = reinterpret_cast<const u32x4 *>(
-        a.q + (((int64_t)b * T + (ok ? row : 0)) * Hq + head[i]) * D + lh * (D / 2));
-#pragma unroll
-    for (int k = 0; k < D / 16; ++k)
-      qf[i][k] = __builtin_bit_cast(bf16x8, ok ? qp[k] : u32x4{0u, 0u, 0u, 0u});
-  }
-  // Let Q land before the first K/V transfer is issued.  (An empty asm that
-  // takes the Q registers forces the wait.)
-#pragma unroll
-  for (int i = 0; i < BPW; ++i)
-#pragma unroll
-    for (int k = 0; k < D / 16; ++k) asm("" : "+v"(qf[i][k]));
 
   // ---- per-lane transfer offsets, the same for every tile.  Transfer i of
   // this wave carries tile keys kt = (wave*NDMA + i)*KPI + lane/CH, on page
@@ -288,28 +289,65 @@ __global__ __launch_bounds__(64 * (kBlocks / BPW), OCC) void prefill_kernel(Pref
     }
   }
 
+  // ---- byte offsets of this wave's pages, 64 tiles at a time (paged): lane
+  // u holds the offset of its page of tile 64*win + u (the safe page's when
+  // the page is missing or past the end); bit u of good_m / clean_m: the page
+  // exists / every key on it counts.  One vector read of the block table per
+  // 64 tiles; a tile then costs two lane reads.
+  uint32_t off_lo[PPW], off_hi[PPW];
+  uint64_t good_m[PPW], clean_m[PPW];
+  int win = -1;
+  // raw table entries of a window (-1 past nblk): read first, used later
+  auto window_raw = [&](int w_, int32_t (&raw)[PPW]) {
+#pragma unroll
+    for (int pp = 0; pp < PPW; ++pp) {
+      const int blk = (64 * w_ + lane) * (kBN / kPageTokens) + wave * PPW + pp;
+      raw[pp] = blk < nblk ? trow_v[blk] : -1;
+    }
+  };
+  auto window_set = [&](int w_, const int32_t (&raw)[PPW]) {
+    win = w_;
+#pragma unroll
+    for (int pp = 0; pp < PPW; ++pp) {
+      const int blk = (64 * w_ + lane) * (kBN / kPageTokens) + wave * PPW + pp;
+      const bool good = blk < nblk && raw[pp] >= 0 && (int64_t)raw[pp] < a.n_pages;
+      const int64_t page = good ? (int64_t)raw[pp] : safe_page;
+      const bool clean = good && (blk + 1) * kPageTokens <= kv_end;
+      const uint64_t off = (uint64_t)page * (uint64_t)page_bytes;
+      off_lo[pp] = (uint32_t)off;
+      off_hi[pp] = (uint32_t)(off >> 32);
+      good_m[pp] = __ballot(good);
+      clean_m[pp] = __ballot(clean);
+    }
+  };
+  auto load_window = [&](int w_) {
+    int32_t raw[PPW];
+    window_raw(w_, raw);
+    window_set(w_, raw);
+  };
+  const uint8_t *safe_base = a.pool + safe_page * page_bytes;
+
   // ---- fetch tile u into stage S: 2*NDMA transfers per wave, always
   auto fetch = [&](int u, auto S_) {
     uint8_t *kdst = kbuf(S_) + wave * NDMA * 1024;
     uint8_t *vdst = vbuf(S_) + wave * NDMA * 1024;
+    if constexpr (PAGED) {
+      if ((u >> 6) != win) load_window(u >> 6);
+    }
 #pragma unroll
     for (int pp = 0; pp < PPW; ++pp) {
       const int key0 = u * kBN + (wave * PPW + pp) * kPageTokens;   // first key of the page
       const uint8_t *kb, *vb, *sk, *sv;                             // normal and safe bases
-      bool page_good = true;
+      bool page_good = true, clean;
       if constexpr (PAGED) {
-        const int blk = key0 / kPageTokens;
-        int64_t page = safe_page;
-        if (blk < nblk) {
-          const int32_t v = trow[blk];
-          page_good = v >= 0 && (int64_t)v < a.n_pages;
-          if (page_good) page = v;
-        } else {
-          page_good = false;
-        }
-        kb = a.pool + page * page_bytes;
+        const int idx = u & 63;
+        const uint64_t off = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane(off_hi[pp], idx) << 32) |
+                             (uint32_t)__builtin_amdgcn_readlane(off_lo[pp], idx);
+        page_good = (good_m[pp] >> idx) & 1;
+        clean = (clean_m[pp] >> idx) & 1;
+        kb = a.pool + off;
         vb = kb;
-        sk = a.pool + safe_page * page_bytes;
+        sk = safe_base;
         sv = sk;
       } else {
         const int64_t base = (((int64_t)b * T + u * kBN) * a.Hkv + kvh) * ROWB;
@@ -318,8 +356,9 @@ __global__ __launch_bounds__(64 * (kBlocks / BPW), OCC) void prefill_kernel(Pref
         vb = reinterpret_cast<const uint8_t *>(a.v) + base;
         sk = reinterpret_cast<const uint8_t *>(a.k) + safe;
         sv = reinterpret_cast<const uint8_t *>(a.v) + safe;
+        clean = key0 + kPageTokens <= kv_end;
       }
-      if (page_good && key0 + kPageTokens <= kv_end) {
+      if (clean) {
 #pragma unroll
         for (int e = 0; e < TPP; ++e) {
           const int i = pp * TPP + e;
@@ -379,6 +418,11 @@ __global__ __launch_bounds__(64 * (kBlocks / BPW), OCC) void prefill_kernel(Pref
     l_lane[i] = 0.f;
   }
   bool started = false;            // some tile processed (wave-uniform)
+  // first tile whose scores need the mask: the causal diagonal of the block's
+  // rows (row0 is a multiple of 32) or the tile that crosses kv_end
+  int t_mask[BPW];
+#pragma unroll
+  for (int i = 0; i < BPW; ++i) t_mask[i] = min(a.causal ? row0[i] / kBN : 0x7fffffff, kv_end / kBN);
   const float c = a.scale_log2;
 
   // ---- one key tile: S = K Q^T, online softmax, O^T += V^T P^T.  Every
@@ -417,7 +461,7 @@ __global__ __launch_bounds__(64 * (kBlocks / BPW), OCC) void prefill_kernel(Pref
     }
 #pragma unroll
     for (int i = 0; i < BPW; ++i) {
-      const bool need_mask = (a.causal && kv0 + kBN - 1 > row0[i]) | (kv0 + kBN > kv_end) | (bad_pages != 0);
+      const bool need_mask = (t >= t_mask[i]) | (bad_pages != 0);
       if (need_mask) {
         const int rel = lim[i] - (kv0 + 4 * lh);      // visible iff key offset <= rel
 #pragma unroll
@@ -439,29 +483,29 @@ __global__ __launch_bounds__(64 * (kBlocks / BPW), OCC) void prefill_kernel(Pref
       }
     }
 
-    // P = 2^(s*c - m) (bf16), the B operands of the PV product: 16 keys each
-    bf16x8 pb[BPW][4];
+    // The two 32-key halves of the tile are two online-softmax steps.  The PV
+    // products of a half are issued as soon as its P is ready, so they run
+    // while the exponentials of the next half are computed.
+    // P = 2^(s*c - m) (bf16) of half h, the B operands of its PV products:
+    // pb[i][q] covers keys 32h + 16q .. +15.
+    bf16x8 pb[BPW][2];
     float psum[BPW];
-    auto exps = [&](int i) {
+    auto exps = [&](int i, int h) {
       float sum = 0.f;
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float p = fast_exp2(__builtin_fmaf(s[i][h][r], c, -m_run[i]));
-          sum += p;
-          pb[i][h * 2 + r / 8][r % 8] = (__bf16)p;
-        }
+      for (int r = 0; r < 16; ++r) {
+        const float p = fast_exp2(__builtin_fmaf(s[i][h][r], c, -m_run[i]));
+        sum += p;
+        pb[i][r / 8][r % 8] = (__bf16)p;
+      }
       psum[i] = sum;
     };
-    // move the running max to the tile max (row max of the raw scores;
+    // move the running max to the half's max (row max of the raw scores;
     // scale >= 0 keeps the order) and rescale what is accumulated
-    auto remax = [&](int i) {
+    auto remax = [&](int i, int h) {
       float rmax = -INFINITY;
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) rmax = fmaxf(rmax, s[i][h][r]);
+      for (int r = 0; r < 16; ++r) rmax = fmaxf(rmax, s[i][h][r]);
       auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(rmax), __float_as_uint(rmax), false, false);
       rmax = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
       const float m_new = fmaxf(m_run[i], rmax * c);
@@ -474,36 +518,44 @@ __global__ __launch_bounds__(64 * (kBlocks / BPW), OCC) void prefill_kernel(Pref
         for (int r = 0; r < 16; ++r) acc[i][mb][r] *= corr;
     };
 #pragma unroll
-    for (int i = 0; i < BPW; ++i) {
-      if (!started) {
-        remax(i);
-        exps(i);
-      } else {
-        exps(i);
-        if (__any(!(psum[i] < kSpecLimit))) {   // some p would be too large: redo with the tile max
-          remax(i);
-          exps(i);
+    for (int h = 0; h < 2; ++h) {
+      // V^T operands of this half, read before the exponentials so that their
+      // LDS latency is hidden behind them
+      bf16x8 vop[D / 32][2];
+#pragma unroll
+      for (int mb = 0; mb < D / 32; ++mb)
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          uint2 part[2];
+#pragma unroll
+          for (int half = 0; half < 2; ++half) {
+            const uint8_t *src = vt + vaddr[mb] + (32 * h + 16 * q + 8 * half) * ROWB;
+            part[half] = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                                       (__attribute__((address_space(3))) i16x4 *)(src)));
+          }
+          vop[mb][q] = __builtin_bit_cast(bf16x8, u32x4{part[0].x, part[0].y, part[1].x, part[1].y});
         }
-      }
-      l_lane[i] += psum[i];
-    }
-    started = true;
-
 #pragma unroll
-    for (int mb = 0; mb < D / 32; ++mb) {
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        uint2 part[2];
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          const uint8_t *src = vt + vaddr[mb] + (16 * kk + 8 * half) * ROWB;
-          part[half] = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                                                     (__attribute__((address_space(3))) i16x4 *)(src)));
+      for (int i = 0; i < BPW; ++i) {
+        if (!started) {
+          remax(i, h);
+          exps(i, h);
+        } else {
+          exps(i, h);
+          if (__any(!(psum[i] < kSpecLimit))) {   // some p would be too large: redo with the half's max
+            remax(i, h);
+            exps(i, h);
+          }
         }
-        const bf16x8 va = __builtin_bit_cast(bf16x8, u32x4{part[0].x, part[0].y, part[1].x, part[1].y});
-#pragma unroll
-        for (int i = 0; i < BPW; ++i) acc[i][mb] = mfma32(va, pb[i][kk], acc[i][mb]);
+        l_lane[i] += psum[i];
       }
+      started = true;
+#pragma unroll
+      for (int mb = 0; mb < D / 32; ++mb)
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+#pragma unroll
+          for (int i = 0; i < BPW; ++i) acc[i][mb] = mfma32(vop[mb][q], pb[i][q], acc[i][mb]);
     }
   };
 
@@ -514,7 +566,9 @@ __global__ __launch_bounds__(64 * (kBlocks / BPW), OCC) void prefill_kernel(Pref
   // the safe token), so the number in flight is the same on every path and
   // one constant wait is exact; the compiler's own bookkeeping then agrees
   // and adds no drain of its own.
-  auto skip = [&](int t) { return a.causal && t * kBN > wave_row_end; };   // rows all precede the tile
+  // last tile this wave's rows see (causal): later tiles are skipped
+  const int t_last = a.causal ? wave_row_end / kBN : 0x7fffffff;
+  auto skip = [&](int t) { return t > t_last; };
   auto step = [&](int t, auto S_) {
     constexpr int S = decltype(S_)::value;
     wait_vm_lgkm0<(NS - 2) * 2 * NDMA>();
@@ -523,7 +577,16 @@ __global__ __launch_bounds__(64 * (kBlocks / BPW), OCC) void prefill_kernel(Pref
     if (!skip(t)) compute(t, S_);
   };
 
+  // Let Q land before the first K/V transfer is issued, so that no wait for
+  // Q sits inside the loop (it would drain the transfers in flight).  (An
+  // empty asm that takes the Q registers forces the wait; the Q loads and the
+  // block-table reads above are in flight together until here.)
+#pragma unroll
+  for (int i = 0; i < BPW; ++i)
+#pragma unroll
+    for (int k = 0; k < D / 16; ++k) asm("" : "+v"(qf[i][k]));
   if (n_tiles > 0) {
+    if constexpr (PAGED) window_set(0, raw0);
     fetch(0, std::integral_constant<int, 0>{});
     if constexpr (NS > 2) fetch(1, std::integral_constant<int, 1>{});
     if constexpr (NS > 3) fetch(2, std::integral_constant<int, 2>{});

@@ -47,6 +47,8 @@ def test_decode_workspace_size():
     # a few long contexts are split across workgroups: O and LSE partials
     assert pa.decode_workspace_size(4, 32, 8, 64, 16384) >= 4 * 32 * 2 * (64 + 1) * 4
     assert pa.decode_workspace_size(0, 32, 8, 64, 2048) == 0
+    assert pa.decode_splits(64, 32, 8, 64, 2048) == 1
+    assert pa.decode_splits(4, 32, 8, 64, 16384) >= 2
 
 
 P = ctypes.c_void_p
