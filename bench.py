@@ -129,8 +129,8 @@ def source_digest(*names: str) -> str:
 # was taken on (digest of the .hip files), null otherwise.
 TRAFFIC = {
     # kernel: (source digest, fetched bytes, written bytes)
-    "prefill": ("2c6f52cb2a4cdc20", 25448050, 17301504),
-    "decode": ("b4ffccba2f648b7e", 154503880, 278528),
+    "prefill": ("ba8a300d5c336164", 25452339, 17301811),
+    "decode": ("e27f38959c7032ea", 153246310, 278528),
 }
 
 
