@@ -68,6 +68,15 @@ def _bind(lib):
     lib.oracle_attn_decode.restype = _I64
     lib.oracle_attn_decode.argtypes = [_P, _P, _I64, _P, _I, _I, _I, _I, _P, _P,
                                        _I, _I, _I, _I, _D, _P, _P]
+    lib.oracle_round_bf16.restype = None
+    lib.oracle_round_bf16.argtypes = [_P, _I64, _P]
+    lib.oracle_rope.restype = _I64
+    lib.oracle_rope.argtypes = [_P, _I64, _I, _I, _P, _P, _P, _I, _P]
+    lib.oracle_kv_append.restype = _I
+    lib.oracle_kv_append.argtypes = [_P, _I64, _P, _P, _P, _P, _I, _I, _P, _P, _P, _P, _I,
+                                     _P, _I, _I, _I, _I, _P, _P, _I, _I]
+    lib.oracle_kv_release.restype = _I
+    lib.oracle_kv_release.argtypes = [_P, _I, _P, _I, _I, _I, _P, _P, _I]
     lib.oracle_attn_dense.restype = None
     lib.oracle_attn_dense.argtypes = [_P, _P, _P, _I, _I, _I, _I, _I, _D, _I, _P, _I64, _P, _P]
     return lib
@@ -165,6 +174,71 @@ def attn_dense(q, k, v, scale: float, causal: bool, rows=None):
     load().oracle_attn_dense(_ptr(qb), _ptr(kb), _ptr(vb), B, T, Hq, Hkv, d, float(scale),
                              int(bool(causal)), _ptr(rws), n_rows, _ptr(O), _ptr(L))
     return O, L
+
+
+# Error bits of the device flag (the library's ABI values).
+ERR_BAD_PAGE, ERR_BAD_SLOT, ERR_BAD_POS = 1, 2, 4
+ERR_NO_FREE_PAGE, ERR_DUP_SLOT, ERR_REASSIGNED, ERR_STACK_FULL = 8, 16, 32, 64
+
+
+def round_bf16(x) -> np.ndarray:
+    """Nearest bfloat16 (ties to even) of each float64 value, as uint16 bit patterns."""
+    xa = np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+    out = np.empty(xa.shape, np.uint16)
+    load().oracle_round_bf16(_ptr(xa), xa.size, _ptr(out))
+    return out
+
+
+def _f32(x) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(x, dtype=np.float32))
+
+
+def rope(x, positions, cos_t, sin_t) -> np.ndarray:
+    """RoPE of x [n_tok, n_heads, d] (bf16 bits) at positions: float64, unrounded."""
+    xb = _bits(x)
+    n_tok, n_heads, d = xb.shape
+    ct, st = _f32(cos_t), _f32(sin_t)
+    assert ct.shape == st.shape and ct.shape[1] == d // 2
+    out = np.empty((n_tok, n_heads, d), np.float64)
+    load().oracle_rope(_ptr(xb), n_tok, n_heads, d, _ptr(_i32(positions)), _ptr(ct), _ptr(st),
+                       ct.shape[0], _ptr(out))
+    return out
+
+
+def kv_append(pool: np.ndarray, n_pages: int, k, v, positions, cos_t, sin_t, block_table: np.ndarray,
+              layer: int, free_pages, top: int, slot_ids=None, q=None):
+    """One decode step's writes (pool and block_table updated in place).
+
+    Returns (q_out bits or None, new top, error bits)."""
+    kb, vb = _bits(k), _bits(v)
+    B, Hkv, d = kb.shape
+    assert block_table.dtype == np.int32 and block_table.flags.c_contiguous and block_table.ndim == 3
+    ct, st = _f32(cos_t), _f32(sin_t)
+    qb = None if q is None else _bits(q)
+    Hq = 0 if qb is None else qb.shape[1]
+    q_out = None if qb is None else qb.copy()
+    fp = _i32(free_pages)
+    t = np.array([top], np.int32)
+    errs = load().oracle_kv_append(
+        _ptr(pool), n_pages, _ptr(kb), _ptr(vb), _ptr(qb), _ptr(q_out), Hq, B,
+        _ptr(None if slot_ids is None else _i32(slot_ids)), _ptr(_i32(positions)), _ptr(ct), _ptr(st),
+        ct.shape[0], _ptr(block_table), block_table.shape[0], block_table.shape[1], block_table.shape[2],
+        layer, _ptr(fp), _ptr(t), Hkv, d)
+    return q_out, int(t[0]), int(errs)
+
+
+def kv_release(slots, block_table: np.ndarray, free_pages: np.ndarray, top: int):
+    """Push the pages of finished slots back onto the free stack (both updated in place).
+
+    Returns (new top, error bits)."""
+    assert block_table.dtype == np.int32 and block_table.flags.c_contiguous and block_table.ndim == 3
+    assert free_pages.dtype == np.int32 and free_pages.flags.c_contiguous
+    sl = _i32(slots)
+    t = np.array([top], np.int32)
+    errs = load().oracle_kv_release(_ptr(sl), sl.size, _ptr(block_table), block_table.shape[0],
+                                    block_table.shape[1], block_table.shape[2], _ptr(free_pages),
+                                    _ptr(t), free_pages.size)
+    return int(t[0]), int(errs)
 
 
 # Convenience wrappers over the seeded cases (duck-typed: any object with the

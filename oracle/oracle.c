@@ -343,3 +343,245 @@ void oracle_attn_dense(const uint16_t *q, const uint16_t *k, const uint16_t *v,
         free(qd);
     }
 }
+
+/* ------------------------------------------------------------------------ */
+/* Decode append: RoPE, page allocation from a free stack, page release.    */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * Device-error bits of the library's ABI, written out again here (the values
+ * are an interface both sides must agree on, not shared code).
+ */
+#define ORACLE_ERR_BAD_PAGE 1
+#define ORACLE_ERR_BAD_SLOT 2
+#define ORACLE_ERR_BAD_POS 4
+#define ORACLE_ERR_NO_FREE_PAGE 8
+#define ORACLE_ERR_DUP_SLOT 16
+#define ORACLE_ERR_REASSIGNED 32
+#define ORACLE_ERR_STACK_FULL 64
+
+/*
+ * Round a double to the nearest bfloat16, ties to even, from the definition:
+ * a bfloat16 has 8 significant bits and fp32's exponent range, so the spacing
+ * of bfloat16 values around |x| in [2^(e-1), 2^e) is 2^(e-8), and 2^-133 in the
+ * subnormal range (|x| < 2^-126).  Dividing by that spacing, rounding to the
+ * nearest integer (ties to even, the default rounding mode) and multiplying
+ * back is exact in double.  Overflow gives infinity.  Returns the bit pattern.
+ */
+static uint16_t double_to_bf16(double x)
+{
+    if (isnan(x))
+        return 0x7FC0;
+    if (x == 0.0 || isinf(x)) {
+        float f = (float)x;
+        uint32_t u;
+        memcpy(&u, &f, sizeof u);
+        return (uint16_t)(u >> 16);
+    }
+    int e;
+    frexp(fabs(x), &e);
+    int qexp = (e > -125 ? e : -125) - 8;
+    double r = ldexp(nearbyint(ldexp(x, -qexp)), qexp);
+    float f = (float)r; /* exact: r is a bfloat16 value (or beyond fp32 range: inf) */
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    return (uint16_t)(u >> 16);
+}
+
+void oracle_round_bf16(const double *x, int64_t n, uint16_t *out)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = double_to_bf16(x[i]);
+}
+
+/*
+ * RoPE of one head vector (tiny-vllm part 3, "RoPE: a rotation that references
+ * a table"): element i of the first half and element i + d/2 of the second
+ * half form pair i, which is turned by the angle whose cosine and sine sit at
+ * row `pos`, column i of the tables ([max_pos][d/2] fp32; the page's tables
+ * repeat each value twice, one per element of the pair, which carries the
+ * same information):
+ *     y[i]       = x[i] * cos - x[i + d/2] * sin
+ *     y[i + d/2] = x[i] * sin + x[i + d/2] * cos
+ * Each product of a bf16 and an fp32 value is exact in double, so each output
+ * is the exact result rounded once to double.
+ */
+static void rope_head(const uint16_t *x, int d, const float *cos_row, const float *sin_row,
+                      double *y)
+{
+    int half = d / 2;
+    for (int i = 0; i < half; ++i) {
+        double x1 = bf16_to_double(x[i]), x2 = bf16_to_double(x[i + half]);
+        double c = (double)cos_row[i], s = (double)sin_row[i];
+        y[i] = x1 * c - x2 * s;
+        y[i + half] = x1 * s + x2 * c;
+    }
+}
+
+/*
+ * RoPE of n_tok tokens' head vectors x [n_tok][n_heads][d] at positions[t]:
+ * out [n_tok][n_heads][d] in double (unrounded).  A token whose position is
+ * outside [0, max_pos) gets NaN rows; the count of such tokens is returned.
+ */
+int64_t oracle_rope(const uint16_t *x, int64_t n_tok, int n_heads, int d, const int32_t *positions,
+                    const float *cos_t, const float *sin_t, int max_pos, double *out)
+{
+    int64_t bad = 0;
+    for (int64_t t = 0; t < n_tok; ++t) {
+        int pos = positions[t];
+        for (int h = 0; h < n_heads; ++h) {
+            double *y = out + (t * n_heads + h) * d;
+            if (pos < 0 || pos >= max_pos) {
+                for (int c = 0; c < d; ++c)
+                    y[c] = NAN;
+                continue;
+            }
+            rope_head(x + (t * n_heads + h) * d, d, cos_t + (int64_t)pos * (d / 2),
+                      sin_t + (int64_t)pos * (d / 2), y);
+        }
+        if (pos < 0 || pos >= max_pos)
+            ++bad;
+    }
+    return bad;
+}
+
+/*
+ * One decode step's writes for B new tokens, in batch order (tiny-vllm part 3,
+ * "RoPE: a rotation that references a table" and "Distributing K/V into paged
+ * blocks"; part 6, "The lifetime of a physical block: free_blocks"):
+ *
+ *   for b = 0 .. B-1:
+ *     slot = slot_ids[b] (NULL: b), pos = positions[b], block = pos / 16
+ *     if pos % 16 == 0 (the token opens a block, the decode allocation rule):
+ *         page = free_pages[top - 1]; top -= 1      (pop from the back)
+ *         block_table[slot][layer][block] = page
+ *     else page = block_table[slot][layer][block]
+ *     K row of the token = bf16(RoPE(k[b], pos)), V row = v[b], written into
+ *     the page at row pos % 16 (layout as in oracle_kv_scatter);
+ *     q_out[b] = bf16(RoPE(q_in[b], pos)) when q_in is given.
+ *
+ * Checks, each OR-ing an error bit and skipping what it cannot do:
+ *   slot outside [0, n_slots)                 BAD_SLOT  (token not written)
+ *   pos outside [0, mbps*16) or >= max_pos    BAD_POS   (token not written;
+ *                                             q rotated only if pos < max_pos
+ *                                             and pos >= 0)
+ *   a slot named twice in the call            DUP_SLOT  (both still processed)
+ *   opening token, empty stack                NO_FREE_PAGE (not written, entry kept)
+ *   opening token, entry was not -1           REASSIGNED (entry overwritten)
+ *   popped page or looked-up entry outside [0, n_pages)   BAD_PAGE (not written)
+ * A token that cannot be written still takes its place in the pop order:
+ * tokens with invalid slot or position do not pop; opening tokens pop (or
+ * find the stack empty) in batch order.
+ *
+ * pool, block_table, *top are updated in place; free_pages is read only
+ * (entries at and above the new top are simply no longer free).  Returns the
+ * OR of the error bits.
+ */
+int oracle_kv_append(uint8_t *pool, int64_t n_pages, const uint16_t *k, const uint16_t *v,
+                     const uint16_t *q_in, uint16_t *q_out, int Hq, int B,
+                     const int32_t *slot_ids, const int32_t *positions,
+                     const float *cos_t, const float *sin_t, int max_pos,
+                     int32_t *block_table, int n_slots, int n_layers, int mbps, int layer,
+                     const int32_t *free_pages, int32_t *top, int n_kv_heads, int head_dim)
+{
+    int errs = 0;
+    int d = head_dim;
+    int64_t row_elems = (int64_t)n_kv_heads * d;
+    double *y = malloc(sizeof(double) * (size_t)d);
+    paged_src s = {pool, n_pages, block_table, n_slots, n_layers, mbps, layer, n_kv_heads, d};
+    for (int b = 0; b < B; ++b) {
+        int slot = slot_ids ? slot_ids[b] : b;
+        int pos = positions[b];
+        for (int o = 0; o < B; ++o)
+            if (o != b && (slot_ids ? slot_ids[o] : o) == slot)
+                errs |= ORACLE_ERR_DUP_SLOT;
+        int pos_ok = pos >= 0 && pos < max_pos;
+        if (q_in && pos_ok)
+            for (int h = 0; h < Hq; ++h) {
+                rope_head(q_in + ((int64_t)b * Hq + h) * d, d, cos_t + (int64_t)pos * (d / 2),
+                          sin_t + (int64_t)pos * (d / 2), y);
+                oracle_round_bf16(y, d, q_out + ((int64_t)b * Hq + h) * d);
+            }
+        if (slot < 0 || slot >= n_slots) {
+            errs |= ORACLE_ERR_BAD_SLOT;
+            continue;
+        }
+        if (!pos_ok || pos >= mbps * ORACLE_PAGE_TOKENS) {
+            errs |= ORACLE_ERR_BAD_POS;
+            continue;
+        }
+        int32_t *entry = block_table + (int64_t)slot * n_layers * mbps + (int64_t)layer * mbps
+                       + pos / ORACLE_PAGE_TOKENS;
+        int64_t page;
+        if (pos % ORACLE_PAGE_TOKENS == 0) {
+            if (*top <= 0) {
+                errs |= ORACLE_ERR_NO_FREE_PAGE;
+                continue;
+            }
+            page = free_pages[*top - 1];
+            *top -= 1;
+            if (page < 0 || page >= n_pages) {
+                errs |= ORACLE_ERR_BAD_PAGE;
+                continue;
+            }
+            if (*entry != -1)
+                errs |= ORACLE_ERR_REASSIGNED;
+            *entry = (int32_t)page;
+        } else {
+            page = *entry;
+            if (page < 0 || page >= n_pages) {
+                errs |= ORACLE_ERR_BAD_PAGE;
+                continue;
+            }
+        }
+        for (int h = 0; h < n_kv_heads; ++h) {
+            int64_t off = k_offset(&s, page, pos, h);
+            rope_head(k + b * row_elems + (int64_t)h * d, d, cos_t + (int64_t)pos * (d / 2),
+                      sin_t + (int64_t)pos * (d / 2), y);
+            for (int c = 0; c < d; ++c) {
+                uint16_t kb = double_to_bf16(y[c]);
+                uint16_t vb = v[b * row_elems + (int64_t)h * d + c];
+                memcpy(pool + off + 2 * c, &kb, 2);
+                memcpy(pool + off + v_offset_bytes(&s) + 2 * c, &vb, 2);
+            }
+        }
+    }
+    free(y);
+    return errs;
+}
+
+/*
+ * Release the pages of n finished slots (tiny-vllm part 6, "The lifetime of a
+ * physical block: free_blocks"): for each slot in the given order, for every
+ * layer, for every logical block in increasing order, a table entry that is
+ * not -1 is pushed onto the back of the free stack and reset to -1.
+ * free_pages has room for `capacity` entries; a push beyond it sets
+ * STACK_FULL and leaves that entry (and the page) as it was.  A slot outside
+ * [0, n_slots) sets BAD_SLOT and is skipped.  Returns the OR of the bits.
+ */
+int oracle_kv_release(const int32_t *slots, int n, int32_t *block_table, int n_slots,
+                      int n_layers, int mbps, int32_t *free_pages, int32_t *top, int capacity)
+{
+    int errs = 0;
+    for (int i = 0; i < n; ++i) {
+        int slot = slots[i];
+        if (slot < 0 || slot >= n_slots) {
+            errs |= ORACLE_ERR_BAD_SLOT;
+            continue;
+        }
+        for (int l = 0; l < n_layers; ++l)
+            for (int blk = 0; blk < mbps; ++blk) {
+                int32_t *entry = block_table + ((int64_t)slot * n_layers + l) * mbps + blk;
+                if (*entry == -1)
+                    continue;
+                if (*top >= capacity) {
+                    errs |= ORACLE_ERR_STACK_FULL;
+                    continue;
+                }
+                free_pages[*top] = *entry;
+                *top += 1;
+                *entry = -1;
+            }
+    }
+    return errs;
+}

@@ -3,7 +3,7 @@
 Each mutant is a plausible slip in ``oracle/oracle.c`` (a dropped term, a
 wrong sign, a wrong index or stride, a transposed operand).  The copy is
 compiled on the CPU into a temporary library and the pins of
-``test_oracle.py`` run against it in a child process (a mutant may read out of
+``test_oracle.py`` and ``test_oracle_append.py`` run against it in a child process (a mutant may read out of
 bounds and crash, which also counts as caught).  The real oracle is never
 modified.
 """
@@ -40,12 +40,27 @@ MUTANTS = [
      "return (int64_t)ORACLE_PAGE_TOKENS * s->n_kv_heads * s->head_dim;"),
     ("q_row_stride", "q + (((int64_t)b * T + t) * Hq + h) * d;", "q + (((int64_t)t * B + b) * Hq + h) * d;"),
     ("bf16_widen", "uint32_t u = (uint32_t)bits << 16;", "uint32_t u = (uint32_t)bits << 15;"),
+    # decode append: rounding, RoPE, allocation, release
+    ("round_precision", "int qexp = (e > -125 ? e : -125) - 8;", "int qexp = (e > -125 ? e : -125) - 7;"),
+    ("round_ties_away", "ldexp(nearbyint(ldexp(x, -qexp)), qexp)", "ldexp(round(ldexp(x, -qexp)), qexp)"),
+    ("rope_sign", "y[i] = x1 * c - x2 * s;", "y[i] = x1 * c + x2 * s;"),
+    ("rope_cos_sin_swapped", "double c = (double)cos_row[i], s = (double)sin_row[i];",
+     "double c = (double)sin_row[i], s = (double)cos_row[i];"),
+    ("rope_adjacent_pairs", "double x1 = bf16_to_double(x[i]), x2 = bf16_to_double(x[i + half]);",
+     "double x1 = bf16_to_double(x[i]), x2 = bf16_to_double(x[(i + 1) % d]);"),
+    ("rope_table_stride", "cos_t + (int64_t)pos * (d / 2)", "cos_t + (int64_t)pos * d"),
+    ("pop_from_front", "page = free_pages[*top - 1];", "page = free_pages[0];"),
+    ("alloc_when_unassigned", "if (pos % ORACLE_PAGE_TOKENS == 0) {", "if (*entry == -1) {"),
+    ("append_v_rotated", "uint16_t vb = v[b * row_elems + (int64_t)h * d + c];",
+     "uint16_t vb = double_to_bf16(y[c]);"),
+    ("release_descending", "for (int blk = 0; blk < mbps; ++blk) {", "for (int blk = mbps - 1; blk >= 0; --blk) {"),
+    ("release_keeps_entry", "                *entry = -1;\n", "\n"),
 ]
 
 RUNNER = textwrap.dedent("""
     import sys, traceback
     sys.path.insert(0, {root!r}); sys.path.insert(0, {tests!r})
-    import oracle, test_oracle as T
+    import oracle, test_oracle as T, test_oracle_append as A
     import inspect
     failed = []
     pins = [
@@ -60,6 +75,18 @@ RUNNER = textwrap.dedent("""
         (T.test_decode_matches_brute_force, {{}}),
         (T.test_scatter_places_rows_at_page_addresses, dict(Hkv=8, d=64)),
         (T.test_page_geometry_matches_printed_constants, {{}}),
+        (A.test_round_bf16_brute_force, {{}}),
+        (A.test_round_bf16_matches_torch_on_fp32_values, {{}}),
+        (A.test_rope_is_complex_rotation, dict(d=64)),
+        (A.test_rope_special_angles, {{}}),
+        (A.test_rope_relative_position, {{}}),
+        (A.test_append_pop_order_by_hand, {{}}),
+        (A.test_append_equals_rope_then_scatter, {{}}),
+        (A.test_append_runs_out_of_pages, {{}}),
+        (A.test_append_flags, {{}}),
+        (A.test_release_push_order_by_hand, {{}}),
+        (A.test_release_stack_full_and_bad_slot, {{}}),
+        (A.test_append_release_round_trip, {{}}),
     ]
     for fn, kw in pins:
         try:

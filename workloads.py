@@ -337,3 +337,79 @@ def fa2_dense(T: int, d: int, causal: bool, seed: int = 0) -> DenseCase:
     H = 2048 // d
     return make_dense(f"dense_fa2_t{T}_d{d}_{'causal' if causal else 'full'}", B=16384 // T, T=T,
                       Hq=H, Hkv=H, d=d, causal=causal, seed=seed)
+
+
+# ---------------------------------------------------------------------------
+# Decode append: RoPE angle tables and a cache state ready for one more token.
+# ---------------------------------------------------------------------------
+
+def rope_tables(max_pos: int, d: int, base: float = 500000.0) -> tuple[np.ndarray, np.ndarray]:
+    """cos/sin tables [max_pos, d/2] fp32 of the angles pos * base^(-2i/d).
+
+    The pages build such tables once at start-up and only look them up; they
+    do not print the frequencies, so the usual geometric progression is used
+    here with Llama 3's base.  Any table is a valid input.
+    """
+    i = np.arange(d // 2, dtype=np.float64)
+    inv = base ** (-2.0 * i / d)
+    ang = np.arange(max_pos, dtype=np.float64)[:, None] * inv[None, :]
+    return np.cos(ang).astype(np.float32), np.sin(ang).astype(np.float32)
+
+
+def random_angle_tables(max_pos: int, d: int, seed: int = 0) -> tuple[np.ndarray, np.ndarray]:
+    """cos/sin tables [max_pos, d/2] fp32 of angles drawn uniformly in [-pi, pi)."""
+    rng = np.random.default_rng(seed + 7919)
+    ang = rng.uniform(-np.pi, np.pi, size=(max_pos, d // 2))
+    return np.cos(ang).astype(np.float32), np.sin(ang).astype(np.float32)
+
+
+@dataclass
+class AppendCase:
+    """A cache whose sequences hold ctx_lens[b] - 1 tokens, plus the next token of each.
+
+    ``block_table`` has pages for the cached tokens only: the block a new token
+    opens (position % 16 == 0) is still -1.  ``free_pages`` is the stack of
+    every page not in the table (a permutation tail), all of it free (top =
+    its length); pops take from the back.
+    """
+
+    name: str
+    decode: DecodeCase               # q (before RoPE), context, new tokens (K before RoPE)
+    block_table: np.ndarray          # int32 table before the append
+    free_pages: np.ndarray           # int32 [n_free]
+    cos_t: np.ndarray                # fp32 [max_pos, d/2]
+    sin_t: np.ndarray
+
+    @property
+    def top(self) -> int:
+        return int(self.free_pages.shape[0])
+
+
+def make_append(name: str, *, B: int, Hq: int, Hkv: int, d: int, n_pages: int, ctx_lens=None,
+                max_ctx: int = 2048, seed: int = 0, mbps: int | None = None, n_layers: int = 1,
+                layer: int = 0, n_slots: int | None = None, slot_ids=None,
+                random_angles: bool = False, page_fill: int = BF16_QNAN) -> AppendCase:
+    dc = make_decode(name, B=B, Hq=Hq, Hkv=Hkv, d=d, n_pages=n_pages, ctx_lens=ctx_lens,
+                     max_ctx=max_ctx, seed=seed, n_layers=n_layers, layer=layer, mbps=mbps,
+                     n_slots=n_slots, slot_ids=slot_ids, page_fill=page_fill)
+    table = dc.cache.block_table.copy()
+    for b in range(B):
+        p = int(dc.ctx_lens[b]) - 1
+        if p >= 0 and p % PAGE_TOKENS == 0:
+            table[dc.slot_ids[b], layer, p // PAGE_TOKENS] = -1
+    used = set(int(x) for x in table.ravel() if x >= 0)
+    rng = np.random.default_rng(seed + 104729)
+    free = np.array([p for p in rng.permutation(n_pages) if int(p) not in used], dtype=np.int32)
+    max_pos = int(table.shape[2]) * PAGE_TOKENS
+    if random_angles:
+        cos_t, sin_t = random_angle_tables(max_pos, d, seed)
+    else:
+        cos_t, sin_t = rope_tables(max_pos, d)
+    return AppendCase(name=name, decode=dc, block_table=table, free_pages=free, cos_t=cos_t,
+                      sin_t=sin_t)
+
+
+def llama_append(seed: int = 0) -> AppendCase:
+    """Decode append for the 64-sequence Llama decode batch (context U[1, 2048])."""
+    return make_append("append_llama_b64", B=64, Hq=LLAMA_HQ, Hkv=LLAMA_HKV, d=LLAMA_D,
+                       n_pages=POOL_PAGES, max_ctx=2048, seed=seed, mbps=128)
