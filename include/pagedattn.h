@@ -74,6 +74,10 @@ typedef enum pa_status {
 #define PA_DEVERR_BAD_PAGE 1 /* needed block-table entry is -1 or >= n_pages         */
 #define PA_DEVERR_BAD_SLOT 2 /* slot id outside [0, n_slots)                          */
 #define PA_DEVERR_BAD_POS 4  /* position/length outside the table (mbps*16) or T     */
+#define PA_DEVERR_NO_FREE_PAGE 8 /* kv_append: the free stack ran out                 */
+#define PA_DEVERR_DUP_SLOT 16    /* kv_append: a slot is named by two tokens           */
+#define PA_DEVERR_REASSIGNED 32  /* kv_append: an opened block's entry was not -1      */
+#define PA_DEVERR_STACK_FULL 64  /* kv_release: the free stack has no room left        */
 
 /* Human-readable name of a pa_status value (static string, never NULL). */
 const char *pa_status_string(int status);
@@ -174,6 +178,80 @@ size_t attn_decode_workspace_size(int B, int Hq, int Hkv, int head_dim, int max_
  */
 int attn_prefill_dense(const void *q, const void *k, const void *v, int B, int T, int Hq, int Hkv,
                        int head_dim, float scale, int causal, void *O, float *LSE, void *stream);
+
+/*
+ * kv_append -- the cache writes of one decode step in one launch: for each of
+ * B new tokens (one per sequence), in batch order,
+ *   1. if its position opens a block (position % 16 == 0: tiny-vllm part 6,
+ *      "The lifetime of a physical block: free_blocks", the decode rule), a
+ *      page is popped from the back of the free stack and recorded in the
+ *      block-table entry of that block;
+ *   2. its K row is rotated by RoPE (tiny-vllm part 3, "RoPE: a rotation that
+ *      references a table": pair i of a head is elements i and i + head_dim/2,
+ *      y_i = x_i cos - x_{i+d/2} sin, y_{i+d/2} = x_i sin + x_{i+d/2} cos, with
+ *      the angle of row `position`, column i of the tables) and written with
+ *      its V row into the page, as kv_scatter would;
+ *   3. if q_in is given, the token's query is rotated the same way into q_out.
+ * Rotation arithmetic: fp64 (each product of a bf16 and an fp32 table value
+ * is exact), one rounding to double, then to the nearest bf16, ties to even.
+ *
+ *   k, v         [B][n_kv_heads][head_dim] bf16 (k before rotation).
+ *   q_in, q_out  [B][Hq][head_dim] bf16, both NULL (no query rotation) or
+ *                both given; they may be the same buffer.  Hq is ignored when
+ *                q_in is NULL.
+ *   slot_ids     [B] int32 (NULL: slot b); positions [B] int32, the position
+ *                of the new token (its sequence's length before the append).
+ *   cos_t, sin_t [max_pos][head_dim/2] fp32 angle tables (the pages keep
+ *                [max_pos][head_dim] with each value twice; one copy is kept
+ *                here).
+ *   block_table  as for kv_scatter, READ AND WRITTEN: the entry of each
+ *                opened block receives its page.
+ *   free_pages   int32 [capacity] stack of free page ids, read only here:
+ *                entries [0, top) are free, the last one is popped first
+ *                (a top outside [0, capacity] is clamped into it).
+ *   alloc_state  int32 [2] device: [0] = top, the number of free pages on the
+ *                stack (lowered by the number of opening tokens, not below 0);
+ *                [1] = an arrival counter used inside the launch, which must
+ *                be 0 between calls (initialise the pair as {top, 0}).
+ * Device errors (OR-ed into *err): BAD_SLOT, BAD_POS (position outside the
+ * table or >= max_pos; the query is still rotated when 0 <= position <
+ * max_pos), DUP_SLOT (two tokens of the call name one slot: their writes
+ * race), NO_FREE_PAGE (the opening token finds the stack empty: not written,
+ * entry left as it was), REASSIGNED (an opened block's entry was not -1: it
+ * is overwritten, the old page is no longer referenced), BAD_PAGE (a popped
+ * page or a looked-up entry outside [0, n_pages)).  A token with an invalid
+ * slot or position pops nothing; every valid opening token takes its place in
+ * the pop order even when it cannot be written.  Calls that overlap in time on
+ * the same alloc_state race.  head_dim must be a multiple of 16; tensors and
+ * tables 16-byte aligned, alloc_state 4-byte aligned.  B == 0 is a no-op.
+ */
+int kv_append(const void *k, const void *v, const void *q_in, void *q_out, int Hq, int B,
+              const int32_t *slot_ids, const int32_t *positions, const float *cos_t,
+              const float *sin_t, int max_pos, void *kv_cache, int64_t n_pages,
+              int32_t *block_table, int n_slots, int n_layers, int max_blocks_per_seq, int layer,
+              const int32_t *free_pages, int capacity, int32_t *alloc_state, int n_kv_heads,
+              int head_dim, int32_t *err, void *stream);
+
+/*
+ * kv_release -- return the pages of finished slots to the free stack
+ * (tiny-vllm part 6, "The lifetime of a physical block: free_blocks"): for
+ * each slot of slots[0..n) in order, for every layer, for every logical block
+ * in increasing order, an entry that is not -1 is pushed onto the back of the
+ * stack (free_pages[top++] = entry) and reset to -1.
+ *
+ *   slots        [n] int32 device array of slot ids.
+ *   block_table  [n_slots][n_layers][max_blocks_per_seq] int32, written.
+ *   free_pages   int32 [capacity] stack, written at [top, top + pushed).
+ *   alloc_state  int32 [2] as for kv_append; [0] is raised by the pushes (a
+ *                top outside [0, capacity] is clamped into it first).
+ * Device errors: BAD_SLOT (slot skipped), STACK_FULL (a push beyond capacity:
+ * that entry and its page stay as they were).  One workgroup does the whole
+ * release in order, so it suits occasional calls, not per-token ones.
+ * n == 0 is a no-op.
+ */
+int kv_release(const int32_t *slots, int n, int32_t *block_table, int n_slots, int n_layers,
+               int max_blocks_per_seq, int32_t *free_pages, int capacity, int32_t *alloc_state,
+               int32_t *err, void *stream);
 
 #ifdef __cplusplus
 }

@@ -23,6 +23,10 @@ _lib = None
 PA_DEVERR_BAD_PAGE = 1
 PA_DEVERR_BAD_SLOT = 2
 PA_DEVERR_BAD_POS = 4
+PA_DEVERR_NO_FREE_PAGE = 8
+PA_DEVERR_DUP_SLOT = 16
+PA_DEVERR_REASSIGNED = 32
+PA_DEVERR_STACK_FULL = 64
 
 _P = ctypes.c_void_p
 _I = ctypes.c_int
@@ -56,6 +60,11 @@ def load():
                                     _I, _P, _SZ, _P, _P, _P, _P]
         lib.attn_decode_workspace_size.restype = _SZ
         lib.attn_decode_workspace_size.argtypes = [_I, _I, _I, _I, _I]
+        lib.kv_append.restype = _I
+        lib.kv_append.argtypes = [_P, _P, _P, _P, _I, _I, _P, _P, _P, _P, _I, _P, _I64, _P, _I, _I,
+                                  _I, _I, _P, _I, _P, _I, _I, _P, _P]
+        lib.kv_release.restype = _I
+        lib.kv_release.argtypes = [_P, _I, _P, _I, _I, _I, _P, _I, _P, _P, _P]
         lib.attn_prefill_dense.restype = _I
         lib.attn_prefill_dense.argtypes = [_P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P, _P, _P]
         _lib = lib
@@ -196,3 +205,50 @@ def attn_prefill_dense(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale:
         _dev(lse, torch.float32, "lse"), _stream(stream))
     _check(rc, "attn_prefill_dense")
     return out, lse
+
+
+def kv_append(k: torch.Tensor, v: torch.Tensor, positions: torch.Tensor, cos_t: torch.Tensor,
+              sin_t: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tensor, layer: int,
+              free_pages: torch.Tensor, alloc_state: torch.Tensor,
+              slot_ids: torch.Tensor | None = None, q: torch.Tensor | None = None,
+              q_out: torch.Tensor | None = None, err: torch.Tensor | None = None,
+              stream=None) -> torch.Tensor | None:
+    """One decode step's cache writes: k, v [B, Hkv, d] (k before RoPE) for the token at
+    positions[b]; pages popped from free_pages for opening tokens (block_table and
+    alloc_state [2] int32 updated).  Rotates q [B, Hq, d] into q_out (default: a new
+    tensor; pass q itself to rotate in place) and returns it (None without q)."""
+    B, Hkv, d = k.shape
+    assert v.shape == k.shape and block_table.dim() == 3 and cos_t.shape == sin_t.shape
+    n_slots, n_layers, mbps = block_table.shape
+    Hq = 0
+    if q is not None:
+        Hq = q.shape[1]
+        if q_out is None:
+            q_out = torch.empty_like(q)
+    rc = load().kv_append(
+        _dev(k, torch.bfloat16, "k"), _dev(v, torch.bfloat16, "v"), _dev(q, torch.bfloat16, "q"),
+        _dev(q_out, torch.bfloat16, "q_out") if q is not None else None, Hq, B,
+        _dev(slot_ids, torch.int32, "slot_ids"), _dev(positions, torch.int32, "positions"),
+        _dev(cos_t, torch.float32, "cos_t"), _dev(sin_t, torch.float32, "sin_t"), cos_t.shape[0],
+        _dev(kv_cache, None, "kv_cache"), _n_pages(kv_cache, Hkv, d),
+        _dev(block_table, torch.int32, "block_table"), n_slots, n_layers, mbps, layer,
+        _dev(free_pages, torch.int32, "free_pages"), free_pages.numel(),
+        _dev(alloc_state, torch.int32, "alloc_state"), Hkv, d, _dev(err, torch.int32, "err"), _stream(stream))
+    _check(rc, "kv_append")
+    return q_out if q is not None else None
+
+
+def kv_release(slots: torch.Tensor, block_table: torch.Tensor, free_pages: torch.Tensor,
+               alloc_state: torch.Tensor, err: torch.Tensor | None = None, stream=None) -> None:
+    """Push the pages of the given slots back onto free_pages; their entries become -1."""
+    n_slots, n_layers, mbps = block_table.shape
+    rc = load().kv_release(
+        _dev(slots, torch.int32, "slots"), slots.numel(), _dev(block_table, torch.int32, "block_table"),
+        n_slots, n_layers, mbps, _dev(free_pages, torch.int32, "free_pages"), free_pages.numel(),
+        _dev(alloc_state, torch.int32, "alloc_state"), _dev(err, torch.int32, "err"), _stream(stream))
+    _check(rc, "kv_release")
+
+
+def new_alloc_state(top: int, device=None) -> torch.Tensor:
+    """The int32 [2] allocator state for kv_append / kv_release: {top, 0}."""
+    return torch.tensor([int(top), 0], dtype=torch.int32, device=device or torch.device("cuda"))

@@ -134,4 +134,43 @@ int attn_prefill_dense(const void *q, const void *k, const void *v, int B, int T
                                   static_cast<hipStream_t>(stream));
 }
 
+int kv_append(const void *k, const void *v, const void *q_in, void *q_out, int Hq, int B,
+              const int32_t *slot_ids, const int32_t *positions, const float *cos_t,
+              const float *sin_t, int max_pos, void *kv_cache, int64_t n_pages,
+              int32_t *block_table, int n_slots, int n_layers, int max_blocks_per_seq, int layer,
+              const int32_t *free_pages, int capacity, int32_t *alloc_state, int n_kv_heads,
+              int head_dim, int32_t *err, void *stream) {
+  if (B < 0 || max_pos <= 0 || capacity < 0) return PA_ERR_SHAPE;
+  int rc = check_cache(kv_cache, n_pages, block_table, n_slots, n_layers, max_blocks_per_seq, layer,
+                       n_kv_heads, head_dim);
+  if (rc != PA_OK) return rc;
+  if (head_dim % 16 != 0) return PA_ERR_UNSUPPORTED;
+  if ((q_in == nullptr) != (q_out == nullptr)) return PA_ERR_NULL;
+  if (q_in && Hq <= 0) return PA_ERR_SHAPE;
+  if ((int64_t)max_pos * (head_dim / 2) > 0x7fffffffLL) return PA_ERR_RANGE;
+  if (B == 0) return PA_OK;
+  if (!k || !v || !positions || !cos_t || !sin_t || !free_pages || !alloc_state) return PA_ERR_NULL;
+  if (!aligned16(k) || !aligned16(v) || !aligned16(cos_t) || !aligned16(sin_t)) return PA_ERR_ALIGN;
+  if (q_in && (!aligned16(q_in) || !aligned16(q_out))) return PA_ERR_ALIGN;
+  if ((reinterpret_cast<uintptr_t>(alloc_state) & 3u) != 0) return PA_ERR_ALIGN;
+  return pa::launch_kv_append(k, v, q_in, q_out, q_in ? Hq : 0, B, slot_ids, positions, cos_t,
+                              sin_t, max_pos, kv_cache, n_pages, block_table, n_slots, n_layers,
+                              max_blocks_per_seq, layer, free_pages, capacity, alloc_state,
+                              n_kv_heads, head_dim, err, static_cast<hipStream_t>(stream));
+}
+
+int kv_release(const int32_t *slots, int n, int32_t *block_table, int n_slots, int n_layers,
+               int max_blocks_per_seq, int32_t *free_pages, int capacity, int32_t *alloc_state,
+               int32_t *err, void *stream) {
+  if (n < 0 || n_slots <= 0 || n_layers <= 0 || max_blocks_per_seq <= 0 || capacity < 0)
+    return PA_ERR_SHAPE;
+  if ((int64_t)n_slots * n_layers * max_blocks_per_seq > 0x7fffffffLL) return PA_ERR_RANGE;
+  if (n == 0) return PA_OK;
+  if (!slots || !block_table || !free_pages || !alloc_state) return PA_ERR_NULL;
+  if ((reinterpret_cast<uintptr_t>(alloc_state) & 3u) != 0) return PA_ERR_ALIGN;
+  return pa::launch_kv_release(slots, n, block_table, n_slots, n_layers, max_blocks_per_seq,
+                               free_pages, capacity, alloc_state, err,
+                               static_cast<hipStream_t>(stream));
+}
+
 }  // extern "C"

@@ -28,4 +28,15 @@ int launch_decode(const void *q, const void *kv_cache, int64_t n_pages, const in
                   const int32_t *ctx_lens, int B, int Hq, int Hkv, int D, float scale, int max_ctx,
                   void *workspace, void *O, float *LSE, int32_t *err, hipStream_t stream);
 
+int launch_kv_append(const void *k, const void *v, const void *q_in, void *q_out, int Hq, int B,
+                     const int32_t *slot_ids, const int32_t *positions, const float *cos_t,
+                     const float *sin_t, int max_pos, void *kv_cache, int64_t n_pages,
+                     int32_t *block_table, int n_slots, int n_layers, int mbps, int layer,
+                     const int32_t *free_pages, int capacity, int32_t *alloc_state, int n_kv_heads,
+                     int head_dim, int32_t *err, hipStream_t stream);
+
+int launch_kv_release(const int32_t *slots, int n, int32_t *block_table, int n_slots, int n_layers,
+                      int mbps, int32_t *free_pages, int capacity, int32_t *alloc_state,
+                      int32_t *err, hipStream_t stream);
+
 }  // namespace pa

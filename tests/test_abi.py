@@ -22,7 +22,8 @@ def declared_functions():
 def test_header_declares_the_path():
     names = declared_functions()
     for n in ["kv_scatter", "attn_prefill", "attn_decode", "attn_prefill_dense",
-              "attn_decode_workspace_size", "pa_status_string", "pa_page_bytes"]:
+              "attn_decode_workspace_size", "pa_status_string", "pa_page_bytes", "kv_append",
+              "kv_release"]:
         assert n in names
 
 
@@ -88,6 +89,35 @@ def test_host_checks_reject_bad_arguments():
     assert lib.kv_scatter(good, good, 1, good, good, good, 1 << 31, good, 1, 1, 128, 0, 8, 64,
                           None, None) == -6
     assert lib.attn_prefill_dense(good, good, None, 1, 16, 4, 4, 64, 0.125, 1, good, good, None) == -1
+
+
+def _append(lib, **kw):
+    good = _fake()
+    a = dict(k=good, v=good, q_in=None, q_out=None, Hq=0, B=4, slot_ids=None, positions=good,
+             cos_t=good, sin_t=good, max_pos=2048, kv_cache=good, n_pages=64, block_table=good,
+             n_slots=4, n_layers=1, mbps=128, layer=0, free_pages=good, capacity=64, alloc=good, Hkv=8, d=64,
+             err=None, stream=None)
+    a.update(kw)
+    return lib.kv_append(*a.values())
+
+
+def test_append_release_host_checks():
+    lib = pa.load()
+    assert _append(lib, B=0, k=None, v=None, positions=None) == 0        # no-op
+    assert _append(lib, alloc=None) == -1
+    assert _append(lib, q_in=_fake()) == -1                              # q_in without q_out
+    assert _append(lib, q_in=_fake(), q_out=_fake(), Hq=0) == -2
+    assert _append(lib, d=72) == -3                                      # not a multiple of 16
+    assert _append(lib, cos_t=_fake(0x10008)) == -4
+    assert _append(lib, alloc=_fake(0x10002)) == -4
+    assert _append(lib, max_pos=0) == -2
+    assert _append(lib, layer=1) == -2
+    assert _append(lib, capacity=-1) == -2
+    good = _fake()
+    assert lib.kv_release(None, 0, good, 4, 1, 128, good, 64, good, None, None) == 0
+    assert lib.kv_release(None, 2, good, 4, 1, 128, good, 64, good, None, None) == -1
+    assert lib.kv_release(good, 2, good, 4, 1, 128, good, -1, good, None, None) == -2
+    assert lib.kv_release(good, 2, good, 4, 1, 128, good, 64, _fake(0x10001), None, None) == -4
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
