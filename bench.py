@@ -321,7 +321,8 @@ def sweep() -> None:
     """The other configurations' measurements (one line each, then a
     markdown table): the 17-token prompt (latency), the dense FA2-shape grid
     (MHA, d 64 / 128, T 512..16k, B*T = 16k, causal and full), the long dense
-    prefill (B=1, T=16384, 16x128, causal) and the long decode (4 x 16384).
+    prefill (B=1, T=16384, 16x128, causal), the long decode (4 x 16384), the
+    decode append of the 64-sequence batch and a release of 8 of its slots.
     Kernel times are HIP-event averages over graph replays (kernel_time)."""
     rows = []
 
@@ -389,6 +390,50 @@ def sweep() -> None:
     n_splits = pa.decode_splits(dcase.B, dcase.Hq, c.n_kv_heads, dcase.d, dcase.max_ctx)
     emit("long decode 4 x 16384 (32/8/64, paged)", t * 1e6, kvb / t / 1e9, "GB/s",
          f"{n_splits} workgroup splits per context (+ combine kernel)")
+
+    # decode append for the 64-sequence batch: RoPE of K and q, page pops, K/V write
+    ac = W.llama_append()
+    dc = ac.decode
+    c = dc.cache
+    pool = device_pool(c)
+    bt = i32(ac.block_table)
+    free_np = np.full(c.n_pages, -1, np.int32)
+    free_np[:ac.top] = ac.free_pages
+    free = i32(free_np)
+    alloc = pa.new_alloc_state(ac.top, DEV)
+    cos_t = torch.from_numpy(ac.cos_t).to(DEV)
+    sin_t = torch.from_numpy(ac.sin_t).to(DEV)
+    nt = dc.new_tokens
+    nk, nv, npos, nsl = nt.k.to(DEV), nt.v.to(DEV), i32(nt.positions), i32(dc.slot_ids)
+    qa = dc.q.to(DEV)
+    q_out = torch.empty_like(qa)
+    t = kernel_time(lambda: pa.kv_append(nk, nv, npos, cos_t, sin_t, pool, bt, c.layer, free, alloc,
+                                         slot_ids=nsl, q=qa, q_out=q_out))
+    n_open = int(((nt.positions % 16) == 0).sum())
+    ab = (2 * nk.numel() + 2 * qa.numel()) * 2 * 2 + dc.B * ac.cos_t.shape[1] * 4 * 2 + n_open * 4
+    emit("kv_append B=64 (32/8/64): RoPE of K and q, page pops, K/V write", t * 1e6, ab / t / 1e9, "GB/s",
+         f"{n_open} of {dc.B} tokens open a page; {ab} bytes moved")
+
+    # release of 8 of the 64 sequences (one workgroup, in order): graphs of
+    # (restore the table and the stack top, release) minus graphs of the restore alone
+    bt0, alloc0 = bt.clone(), alloc.clone()
+    rel = i32(np.arange(8))
+    n_rel = int((ac.block_table[:8] >= 0).sum())
+
+    def restore():
+        bt.copy_(bt0)
+        alloc.copy_(alloc0)
+
+    def restore_release():
+        restore()
+        pa.kv_release(rel, bt, free, alloc)
+
+    t_rr = kernel_time(restore_release)
+    t_r = kernel_time(restore)
+    us = (t_rr - t_r) * 1e6
+    emit("kv_release of 8 slots (1 layer x 128 blocks each)", us, n_rel / us, "pages/us",
+         f"{n_rel} pages pushed; graph of restore+release minus graph of restore")
+    del pool
 
     print("\n| workload | time (us) | throughput | note |\n|---|---:|---:|---|")
     for name, us, metric, unit, extra in rows:

@@ -222,7 +222,8 @@ int attn_prefill_dense(const void *q, const void *k, const void *v, int B, int T
  * page or a looked-up entry outside [0, n_pages)).  A token with an invalid
  * slot or position pops nothing; every valid opening token takes its place in
  * the pop order even when it cannot be written.  Calls that overlap in time on
- * the same alloc_state race.  head_dim must be a multiple of 16; tensors and
+ * the same alloc_state race.  head_dim must be a multiple of 16 and
+ * n_kv_heads * head_dim at most 8192; tensors and
  * tables 16-byte aligned, alloc_state 4-byte aligned.  B == 0 is a no-op.
  */
 int kv_append(const void *k, const void *v, const void *q_in, void *q_out, int Hq, int B,

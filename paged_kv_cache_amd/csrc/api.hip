@@ -145,6 +145,7 @@ int kv_append(const void *k, const void *v, const void *q_in, void *q_out, int H
                        n_kv_heads, head_dim);
   if (rc != PA_OK) return rc;
   if (head_dim % 16 != 0) return PA_ERR_UNSUPPORTED;
+  if ((int64_t)n_kv_heads * head_dim > 8192) return PA_ERR_UNSUPPORTED;  // K+V row staged in LDS
   if ((q_in == nullptr) != (q_out == nullptr)) return PA_ERR_NULL;
   if (q_in && Hq <= 0) return PA_ERR_SHAPE;
   if ((int64_t)max_pos * (head_dim / 2) > 0x7fffffffLL) return PA_ERR_RANGE;

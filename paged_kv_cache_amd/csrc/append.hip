@@ -15,9 +15,10 @@
 // of every workgroup counts, over the whole batch, the openers before its own
 // token (its rank r) and all openers (n); an opener takes free_pages[top-1-r]
 // with top read from the allocator state.  The stack top is lowered once, by
-// whichever opener arrives last on a counter next to it (each opener reads top
-// before it arrives, so nobody reads a lowered top), and that opener resets
-// the counter for the next call.
+// whichever opener arrives last on a counter next to it (each opener has read
+// top before it arrives, so nobody reads a lowered top), and that opener
+// resets the counter for the next call.  The top and the counter are only
+// touched by device-scope atomics, so no memory fence is needed.
 //
 // Rotation arithmetic is fp64: a bf16 times an fp32 table value is exact in
 // fp64, so each output is the exact x1*c - x2*s (or x1*s + x2*c) rounded once,
@@ -36,7 +37,10 @@ namespace pa {
 
 namespace {
 
-constexpr int kAppendThreads = 256;
+constexpr int kAppendThreads = 512;
+// wave 0 takes the page, waves 1-2 rotate K and stage K/V, waves 3-7 rotate
+// the query: the three dependency chains run side by side
+constexpr int kKvThreads = 128;
 constexpr int kReleaseThreads = 1024;
 
 // Nearest bf16 of a double, ties to even.  The double is first rounded to fp32
@@ -127,6 +131,8 @@ __device__ __forceinline__ void rope_rows(const uint8_t *src, uint8_t *dst, int 
 }  // namespace
 
 __global__ __launch_bounds__(kAppendThreads) void kv_append_kernel(AppendArgs a) {
+  // stage: the rotated K row then the V row of this token (2 * Hkv * d * 2 bytes)
+  extern __shared__ u32x4 stage[];
   __shared__ int page_s;
   const int b = blockIdx.x;
   const int tid = threadIdx.x;
@@ -134,25 +140,31 @@ __global__ __launch_bounds__(kAppendThreads) void kv_append_kernel(AppendArgs a)
   const int slot = a.slot_ids ? a.slot_ids[b] : b;
   const int pos = a.positions[b];
   const bool pos_ok = pos >= 0 && pos < a.max_pos;
+  const bool valid = token_valid(a, slot, pos);
+  const bool opens = valid && (pos % kPageTokens) == 0;
   const float *cs_row = a.cos_t + (int64_t)(pos_ok ? pos : 0) * (a.d / 2);
   const float *sn_row = a.sin_t + (int64_t)(pos_ok ? pos : 0) * (a.d / 2);
+  const int64_t row_bytes = (int64_t)a.Hkv * a.d * 2;
+  int32_t *entry = a.block_table + ((int64_t)(valid ? slot : 0) * a.n_layers + a.layer) * a.mbps +
+                   (valid ? pos : 0) / kPageTokens;
+  int top = 0, old_entry = -1, rank = 0, total = 0;
 
   if (tid < 64) {
+    // wave 0: the page.  The stack top, the first 64 tokens' slots and
+    // positions and this token's entry are all requested at once; then the
     // rank of this token among the openers of the batch, their count, and
-    // whether another token names the same slot
-    const bool valid = token_valid(a, slot, pos);
-    const bool opens = valid && (pos % kPageTokens) == 0;
-    int rank = 0, total = 0;
+    // whether another token names the same slot.
+    top = __hip_atomic_load(&a.alloc[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    top = top < 0 ? 0 : (top > a.capacity ? a.capacity : top);
     bool dup = false;
     for (int base = 0; base < a.B; base += 64) {
       const int i = base + lane;
-      bool need = false, same = false;
-      if (i < a.B) {
-        const int si = a.slot_ids ? a.slot_ids[i] : i;
-        const int pi = a.positions[i];
-        need = token_valid(a, si, pi) && (pi % kPageTokens) == 0;
-        same = i != b && si == slot;
-      }
+      const int ic = i < a.B ? i : a.B - 1;
+      const int si = a.slot_ids ? a.slot_ids[ic] : ic;
+      const int pi = a.positions[ic];
+      if (base == 0 && valid) old_entry = *entry;
+      const bool need = i < a.B && token_valid(a, si, pi) && (pi % kPageTokens) == 0;
+      const bool same = i < a.B && i != b && si == slot;
       rank += __popcll(__ballot(need && i < b));
       total += __popcll(__ballot(need));
       dup |= __ballot(same) != 0;
@@ -164,54 +176,62 @@ __global__ __launch_bounds__(kAppendThreads) void kv_append_kernel(AppendArgs a)
         raise_err(a.err, PA_DEVERR_BAD_SLOT);
       } else if (!valid) {
         raise_err(a.err, PA_DEVERR_BAD_POS);
-      } else {
-        int32_t *entry = a.block_table + ((int64_t)slot * a.n_layers + a.layer) * a.mbps +
-                         pos / kPageTokens;
-        if (opens) {
-          int top = __hip_atomic_load(&a.alloc[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          top = top < 0 ? 0 : (top > a.capacity ? a.capacity : top);
-          const bool have = rank < top;
-          const int popped = have ? a.free_pages[top - 1 - rank] : -1;
-          __threadfence();
-          if (atomicAdd(&a.alloc[1], 1) == total - 1) {
-            // last opener to arrive: every opener has read top by now
-            atomicExch(&a.alloc[0], top > total ? top - total : 0);
-            atomicExch(&a.alloc[1], 0);
-          }
-          if (!have) {
-            raise_err(a.err, PA_DEVERR_NO_FREE_PAGE);
-          } else if (popped < 0 || (int64_t)popped >= a.n_pages) {
-            raise_err(a.err, PA_DEVERR_BAD_PAGE);
-          } else {
-            if (*entry != -1) raise_err(a.err, PA_DEVERR_REASSIGNED);
-            *entry = popped;
-            page = popped;
-          }
+      } else if (opens) {
+        if (rank >= top) {
+          raise_err(a.err, PA_DEVERR_NO_FREE_PAGE);
         } else {
-          const int e = *entry;
-          if (e < 0 || (int64_t)e >= a.n_pages)
+          const int popped = a.free_pages[top - 1 - rank];
+          if (popped < 0 || (int64_t)popped >= a.n_pages)
             raise_err(a.err, PA_DEVERR_BAD_PAGE);
           else
-            page = e;
+            page = popped;
         }
+      } else if (old_entry < 0 || (int64_t)old_entry >= a.n_pages) {
+        raise_err(a.err, PA_DEVERR_BAD_PAGE);
+      } else {
+        page = old_entry;
       }
       page_s = page;
     }
+  } else if (tid < 64 + kKvThreads) {
+    // rotate K and copy V into the stage
+    const int t = tid - 64;
+    if (valid) {
+      const int vchunks = (int)(row_bytes / 16);
+      const u32x4 *vsrc = reinterpret_cast<const u32x4 *>(a.v + (int64_t)b * row_bytes);
+      for (int c = t; c < vchunks; c += kKvThreads) stage[vchunks + c] = vsrc[c];
+      rope_rows(a.k + (int64_t)b * row_bytes, reinterpret_cast<uint8_t *>(stage), a.Hkv, a.d, cs_row,
+                sn_row, t, kKvThreads);
+    }
   } else if (a.q_in && pos_ok) {
-    // the query, by the other waves while wave 0 allocates
+    // rotate the query
+    const int t = tid - 64 - kKvThreads;
     rope_rows(a.q_in + (int64_t)b * a.Hq * a.d * 2, a.q_out + (int64_t)b * a.Hq * a.d * 2, a.Hq,
-              a.d, cs_row, sn_row, tid - 64, kAppendThreads - 64);
+              a.d, cs_row, sn_row, t, kAppendThreads - 64 - kKvThreads);
   }
   __syncthreads();
   const int page = page_s;
+  if (tid == 0 && opens) {
+    // Every opener has read top before it arrives (its value was used above,
+    // before the barrier, so the load has completed), and the last one to
+    // arrive lowers it and resets the counter for the next call.  No fence:
+    // an agent-scope fence here would write back this XCD's whole L2.
+    if (atomicAdd(&a.alloc[1], 1) == total - 1) {
+      atomicExch(&a.alloc[0], top > total ? top - total : 0);
+      atomicExch(&a.alloc[1], 0);
+    }
+    if (page >= 0) {
+      if (old_entry != -1) raise_err(a.err, PA_DEVERR_REASSIGNED);
+      *entry = page;
+    }
+  }
   if (page < 0) return;
-  const int64_t row_bytes = (int64_t)a.Hkv * a.d * 2;
   uint8_t *kdst = a.pool + (int64_t)page * a.page_bytes + (int64_t)(pos % kPageTokens) * row_bytes;
-  rope_rows(a.k + (int64_t)b * row_bytes, kdst, a.Hkv, a.d, cs_row, sn_row, tid, kAppendThreads);
   const int vchunks = (int)(row_bytes / 16);
-  for (int c = tid; c < vchunks; c += kAppendThreads)
-    *reinterpret_cast<u32x4 *>(kdst + a.v_offset + c * 16) =
-        *reinterpret_cast<const u32x4 *>(a.v + (int64_t)b * row_bytes + c * 16);
+  for (int c = tid; c < 2 * vchunks; c += kAppendThreads) {
+    uint8_t *dst = kdst + (c < vchunks ? (int64_t)c * 16 : a.v_offset + (int64_t)(c - vchunks) * 16);
+    *reinterpret_cast<u32x4 *>(dst) = stage[c];
+  }
 }
 
 __global__ __launch_bounds__(kReleaseThreads) void kv_release_kernel(
@@ -225,43 +245,49 @@ __global__ __launch_bounds__(kReleaseThreads) void kv_release_kernel(
     const int t = alloc[0];
     top_s = t < 0 ? 0 : (t > capacity ? capacity : t);
   }
-  __syncthreads();
+  // the released entries in push order (slot of the list, then layer, then
+  // logical block) as one flat index; 1024 of them per pass
   const int per_slot = n_layers * mbps;
-  for (int i = 0; i < n; ++i) {
-    const int slot = slots[i];
-    if (slot < 0 || slot >= n_slots) {
-      if (tid == 0) raise_err(err, PA_DEVERR_BAD_SLOT);
-      continue;
-    }
-    int32_t *row = block_table + (int64_t)slot * per_slot;
-    for (int base = 0; base < per_slot; base += kReleaseThreads) {
-      const int j = base + tid;
-      const int e = j < per_slot ? row[j] : -1;
-      const bool keep = e != -1;
-      const uint64_t m = __ballot(keep);
-      const int before_in_wave = __popcll(m & ((1ull << lane) - 1));
-      if (lane == 0) wave_cnt[wave] = __popcll(m);
-      __syncthreads();
-      int before = before_in_wave, total = 0;
-      for (int w = 0; w < kReleaseThreads / 64; ++w) {
-        const int c = wave_cnt[w];
-        before += w < wave ? c : 0;
-        total += c;
+  const int64_t n_entries = (int64_t)n * per_slot;
+  for (int64_t base = 0; base < n_entries; base += kReleaseThreads) {
+    const int64_t j = base + tid;
+    int e = -1;
+    int32_t *ent = nullptr;
+    if (j < n_entries) {
+      const int i = (int)(j / per_slot);
+      const int slot = slots[i];
+      const int r = (int)(j - (int64_t)i * per_slot);
+      if (slot >= 0 && slot < n_slots) {
+        ent = block_table + (int64_t)slot * per_slot + r;
+        e = *ent;
+      } else if (r == 0) {
+        raise_err(err, PA_DEVERR_BAD_SLOT);
       }
-      const int top = top_s;
-      if (keep) {
-        const int at = top + before;
-        if (at < capacity) {
-          free_pages[at] = e;
-          row[j] = -1;
-        } else {
-          raise_err(err, PA_DEVERR_STACK_FULL);
-        }
-      }
-      __syncthreads();
-      if (tid == 0) top_s = top + total < capacity ? top + total : capacity;
-      __syncthreads();
     }
+    const bool keep = e != -1;
+    const uint64_t m = __ballot(keep);
+    const int before_in_wave = __popcll(m & ((1ull << lane) - 1));
+    if (lane == 0) wave_cnt[wave] = __popcll(m);
+    __syncthreads();
+    int before = before_in_wave, cnt = 0;
+    for (int w = 0; w < kReleaseThreads / 64; ++w) {
+      const int c = wave_cnt[w];
+      before += w < wave ? c : 0;
+      cnt += c;
+    }
+    const int top = top_s;
+    if (keep) {
+      const int at = top + before;
+      if (at < capacity) {
+        free_pages[at] = e;
+        *ent = -1;
+      } else {
+        raise_err(err, PA_DEVERR_STACK_FULL);
+      }
+    }
+    __syncthreads();
+    if (tid == 0) top_s = top + cnt < capacity ? top + cnt : capacity;
+    __syncthreads();
   }
   if (tid == 0) alloc[0] = top_s;
 }
@@ -299,7 +325,8 @@ int launch_kv_append(const void *k, const void *v, const void *q_in, void *q_out
   a.n_layers = n_layers;
   a.mbps = mbps;
   a.layer = layer;
-  hipLaunchKernelGGL(kv_append_kernel, dim3(B), dim3(kAppendThreads), 0, stream, a);
+  const size_t stage_bytes = 2 * (size_t)n_kv_heads * head_dim * 2;
+  hipLaunchKernelGGL(kv_append_kernel, dim3(B), dim3(kAppendThreads), stage_bytes, stream, a);
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
 
