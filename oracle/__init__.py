@@ -63,7 +63,7 @@ def _bind(lib):
     lib.oracle_kv_scatter.restype = _I64
     lib.oracle_kv_scatter.argtypes = [_P, _I64, _P, _P, _I64, _P, _P, _P, _I, _I, _I, _I, _I, _I]
     lib.oracle_attn_prefill.restype = _I64
-    lib.oracle_attn_prefill.argtypes = [_P, _P, _I64, _P, _I, _I, _I, _I, _P, _P,
+    lib.oracle_attn_prefill.argtypes = [_P, _P, _I64, _P, _I, _I, _I, _I, _P, _P, _P,
                                         _I, _I, _I, _I, _I, _D, _I, _P, _I64, _P, _P]
     lib.oracle_attn_decode.restype = _I64
     lib.oracle_attn_decode.argtypes = [_P, _P, _I64, _P, _I, _I, _I, _I, _P, _P,
@@ -131,8 +131,10 @@ def kv_scatter(pool: np.ndarray, n_pages: int, k, v, slot_ids, positions, block_
 
 
 def attn_prefill(q, pool: np.ndarray, n_pages: int, block_table, layer: int, slot_ids, seq_lens,
-                 Hkv: int, scale: float, causal: bool, rows=None):
-    """Paged prefill rows. Returns (O [n_rows,Hq,d] f64, LSE [n_rows,Hq] f64, bad_lookups)."""
+                 Hkv: int, scale: float, causal: bool, rows=None, q_lens=None):
+    """Paged prefill rows (q_lens: queries are the last q_lens[b] of seq_lens[b] cached
+    tokens; None: the whole sequence). Returns (O [n_rows,Hq,d] f64, LSE [n_rows,Hq] f64,
+    bad_lookups)."""
     qb = _bits(q)
     B, T, Hq, d = q.shape
     bt = _i32(block_table)
@@ -143,6 +145,7 @@ def attn_prefill(q, pool: np.ndarray, n_pages: int, block_table, layer: int, slo
     bad = load().oracle_attn_prefill(
         _ptr(qb), _ptr(pool), n_pages, _ptr(bt), bt.shape[0], bt.shape[1], bt.shape[2], layer,
         _ptr(None if slot_ids is None else _i32(slot_ids)), _ptr(_i32(seq_lens)),
+        _ptr(None if q_lens is None else _i32(q_lens)),
         B, T, Hq, Hkv, d, float(scale), int(bool(causal)), _ptr(rws), n_rows, _ptr(O), _ptr(L))
     return O, L, int(bad)
 
@@ -262,7 +265,8 @@ def prefill_case(case, rows=None, pool: np.ndarray | None = None):
         assert bad == 0
     c = case.cache
     O, L, bad = attn_prefill(case.q, pool, c.n_pages, c.block_table, c.layer, case.slot_ids,
-                             case.seq_lens, c.n_kv_heads, case.scale, case.causal, rows)
+                             case.seq_lens, c.n_kv_heads, case.scale, case.causal, rows,
+                             q_lens=getattr(case, "q_lens", None))
     assert bad == 0
     return O, L, pool
 

@@ -206,16 +206,21 @@ int64_t oracle_kv_scatter(uint8_t *pool, int64_t n_pages,
 
 /*
  * Paged prefill.  q: [B][T][Hq][d]; sequence b lives in block-table slot
- * slot_ids[b] (NULL: slot b) and has seq_lens[b] <= T tokens, query t sitting
- * at position t.  Rows to evaluate are the (b, t) pairs rows[2i], rows[2i+1]
- * (rows == NULL: all B*T in order).  O: [n_rows][Hq][d], LSE: [n_rows][Hq].
- * A padding row (t >= seq_lens[b]) gets O = 0, LSE = -infinity.
+ * slot_ids[b] (NULL: slot b) and has seq_lens[b] tokens in the cache.  Its
+ * queries are the last q_lens[b] of those tokens (q_lens NULL: all of them,
+ * q_len = seq_len <= T): query row t sits at position seq_len - q_len + t, so
+ * a chunk continuing a cached prefix is aligned to the end of the sequence
+ * (bottom-right), and a single query row (q_len 1) is a decode step.  Rows to
+ * evaluate are the (b, t) pairs rows[2i], rows[2i+1] (rows == NULL: all B*T in
+ * order).  O: [n_rows][Hq][d], LSE: [n_rows][Hq].  A padding row (t >= q_len)
+ * gets O = 0, LSE = -infinity.
  */
 int64_t oracle_attn_prefill(const uint16_t *q, const uint8_t *pool, int64_t n_pages,
                             const int32_t *block_table, int n_slots, int n_layers, int mbps,
                             int layer, const int32_t *slot_ids, const int32_t *seq_lens,
-                            int B, int T, int Hq, int Hkv, int d, double scale, int causal,
-                            const int32_t *rows, int64_t n_rows, double *O, double *LSE)
+                            const int32_t *q_lens, int B, int T, int Hq, int Hkv, int d,
+                            double scale, int causal, const int32_t *rows, int64_t n_rows,
+                            double *O, double *LSE)
 {
     paged_src s = {pool, n_pages, block_table, n_slots, n_layers, mbps, layer, Hkv, d};
     int g = Hq / Hkv;
@@ -228,7 +233,9 @@ int64_t oracle_attn_prefill(const uint16_t *q, const uint8_t *pool, int64_t n_pa
         int t = rows ? rows[2 * r + 1] : (int)(r % T);
         int slot = slot_ids ? slot_ids[b] : b;
         int64_t len = seq_lens[b];
-        int64_t n_keys = t < len ? (causal ? (int64_t)t + 1 : len) : 0;
+        int64_t qlen = q_lens ? q_lens[b] : len;
+        int64_t pos = len - qlen + t; /* position of query row t */
+        int64_t n_keys = t < qlen ? (causal ? pos + 1 : len) : 0;
         const uint16_t **krow = malloc(sizeof(*krow) * (size_t)(n_keys + 1));
         const uint16_t **vrow = malloc(sizeof(*vrow) * (size_t)(n_keys + 1));
         double *scores = malloc(sizeof(double) * (size_t)(n_keys + 1));

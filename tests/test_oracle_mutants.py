@@ -3,7 +3,8 @@
 Each mutant is a plausible slip in ``oracle/oracle.c`` (a dropped term, a
 wrong sign, a wrong index or stride, a transposed operand).  The copy is
 compiled on the CPU into a temporary library and the pins of
-``test_oracle.py`` and ``test_oracle_append.py`` run against it in a child process (a mutant may read out of
+``test_oracle.py``, ``test_oracle_append.py`` and ``test_oracle_chunk.py``
+run against it in a child process (a mutant may read out of
 bounds and crash, which also counts as caught).  The real oracle is never
 modified.
 """
@@ -24,8 +25,10 @@ MUTANTS = [
     ("lse_without_max", "*lse = m + log(l);", "*lse = log(l);"),
     ("no_final_divide", "out[c] /= l;", "out[c] /= 1.0;"),
     ("max_reversed", "if (scores[j] > m)", "if (scores[j] < m && scores[j] > -INFINITY)"),
-    ("causal_off_by_one", "(causal ? (int64_t)t + 1 : len)", "(causal ? (int64_t)t : len)"),
-    ("causal_ignored", "(causal ? (int64_t)t + 1 : len)", "(len)"),
+    ("causal_off_by_one", "(causal ? pos + 1 : len)", "(causal ? pos : len)"),
+    ("causal_ignored", "(causal ? pos + 1 : len)", "(len)"),
+    ("chunk_top_left", "int64_t pos = len - qlen + t;", "int64_t pos = t;"),
+    ("chunk_query_rows", "n_keys = t < qlen ?", "n_keys = t < len ?"),
     ("gqa_interleaved", "int kvh = h / g;", "int kvh = h % Hkv;"),
     ("v_offset_dropped", "vrow[j] = (const uint16_t *)(pool + off + v_offset_bytes(&s));",
      "vrow[j] = (const uint16_t *)(pool + off);"),
@@ -60,7 +63,7 @@ MUTANTS = [
 RUNNER = textwrap.dedent("""
     import sys, traceback
     sys.path.insert(0, {root!r}); sys.path.insert(0, {tests!r})
-    import oracle, test_oracle as T, test_oracle_append as A
+    import oracle, test_oracle as T, test_oracle_append as A, test_oracle_chunk as C
     import inspect
     failed = []
     pins = [
@@ -87,6 +90,10 @@ RUNNER = textwrap.dedent("""
         (A.test_release_push_order_by_hand, {{}}),
         (A.test_release_stack_full_and_bad_slot, {{}}),
         (A.test_append_release_round_trip, {{}}),
+        (C.test_chunk_rows_equal_whole_prompt_rows, dict(causal=True)),
+        (C.test_chunk_single_row_is_decode, {{}}),
+        (C.test_chunk_zero_query_closed_form, {{}}),
+        (C.test_chunk_matches_numpy_direct, dict(causal=True)),
     ]
     for fn, kw in pins:
         try:

@@ -104,6 +104,8 @@ class PrefillCase:
     cache: PagedCache
     scale: float
     causal: bool = True
+    # queries are the last q_lens[b] of the seq_lens[b] cached tokens (None: all of them)
+    q_lens: np.ndarray | None = None
 
     @property
     def B(self) -> int:
@@ -223,6 +225,51 @@ def make_prefill(name: str, *, B: int, T: int, Hq: int, Hkv: int, d: int,
     scale = float(np.float32(1.0 / np.sqrt(d))) if scale is None else float(np.float32(scale))
     return PrefillCase(name=name, q=q, tokens=tokens, seq_lens=seq_lens, slot_ids=slot_ids,
                        cache=cache, scale=scale, causal=causal)
+
+
+def make_chunk(name: str, *, B: int, Hq: int, Hkv: int, d: int, n_pages: int, kv_lens, q_lens,
+               seed: int = 0, scale: float | None = None, causal: bool = True, n_layers: int = 1,
+               layer: int = 0, mbps: int | None = None, n_slots: int | None = None, slot_ids=None,
+               page_fill: int = BF16_QNAN) -> PrefillCase:
+    """A prompt chunk continuing a cached prefix: sequence b has kv_lens[b] tokens in the
+    cache (``tokens`` holds all of them, prefix and chunk), and its queries are the last
+    q_lens[b] of them, padded to T = max(q_lens).  The draws are those of ``make_prefill``
+    with T = max(kv_lens): query row t of the chunk is the full prompt's row
+    kv_lens[b] - q_lens[b] + t."""
+    kv_lens = np.asarray(kv_lens, np.int32)
+    q_lens = np.asarray(q_lens, np.int32)
+    assert kv_lens.shape == (B,) and q_lens.shape == (B,) and np.all(q_lens <= kv_lens)
+    full = make_prefill(name, B=B, T=max(int(kv_lens.max(initial=0)), 1), Hq=Hq, Hkv=Hkv, d=d,
+                        n_pages=n_pages, seed=seed, seq_lens=kv_lens, scale=scale, causal=causal,
+                        n_layers=n_layers, layer=layer, mbps=mbps, n_slots=n_slots,
+                        slot_ids=slot_ids, page_fill=page_fill)
+    T = max(int(q_lens.max(initial=0)), 1)
+    q = torch.zeros(B, T, Hq, d, dtype=torch.bfloat16)
+    for b in range(B):
+        ql, kv = int(q_lens[b]), int(kv_lens[b])
+        q[b, :ql] = full.q[b, kv - ql:kv]
+    full.q = q
+    full.q_lens = q_lens
+    return full
+
+
+def llama_chunk(seed: int = 0) -> PrefillCase:
+    """Prefix continuation: 2 sequences with 2048 cached tokens each take a 2048-token
+    chunk (4096 in the cache after it), 32/8/64, 2 GiB pool."""
+    return make_chunk("chunk_llama_b2_prefix2048_q2048", B=2, Hq=LLAMA_HQ, Hkv=LLAMA_HKV, d=LLAMA_D,
+                      n_pages=POOL_PAGES, kv_lens=[4096, 4096], q_lens=[2048, 2048], seed=seed,
+                      scale=1.0 / 8.0, mbps=256)
+
+
+def mixed_batch(seed: int = 0) -> PrefillCase:
+    """Mixed prefill + decode in one call: 2 prompt chunks of 512 tokens (after 1000 and
+    3000 cached tokens) and 62 decode rows (one query each, contexts U[1, 2048])."""
+    rng = np.random.default_rng(seed + 31)
+    dec = rng.integers(1, 2049, size=62)
+    kv = np.concatenate([[1512, 3512], dec]).astype(np.int32)
+    ql = np.concatenate([[512, 512], np.ones(62, np.int64)]).astype(np.int32)
+    return make_chunk("mixed_b64_2chunks512_62decode", B=64, Hq=LLAMA_HQ, Hkv=LLAMA_HKV, d=LLAMA_D,
+                      n_pages=POOL_PAGES, kv_lens=kv, q_lens=ql, seed=seed, scale=1.0 / 8.0, mbps=256)
 
 
 def make_decode(name: str, *, B: int, Hq: int, Hkv: int, d: int, n_pages: int,
