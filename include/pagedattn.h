@@ -137,6 +137,33 @@ int attn_prefill(const void *q, const void *kv_cache, int64_t n_pages, const int
                  void *stream);
 
 /*
+ * attn_prefill_chunk -- the prefill of a prompt chunk that continues a cached
+ * prefix, and of mixed batches: sequence b has kv_lens[b] tokens in the
+ * cache (prefix and chunk, the chunk's K/V already scattered) and its queries
+ * are the LAST q_lens[b] of them.  Query row t is the token at position
+ * kv_lens[b] - q_lens[b] + t (aligned to the end of the sequence); causal: it
+ * sees keys 0 .. that position; full: all kv_lens[b] keys.  q_lens[b] == 1 is
+ * a decode row (the newest token sees its whole context), q_lens[b] ==
+ * kv_lens[b] is attn_prefill.  The pages only prefill fresh prompts
+ * (tiny-vllm part 3, "Distributing K/V into paged blocks": the table entries
+ * are still unassigned); the end alignment is the reading that keeps every
+ * token's view the same as in a whole-prompt prefill.
+ *
+ *   q            [B][T][Hq][head_dim] bf16, row t < q_lens[b] as above.
+ *   q_lens       [B] int32, 0 <= q_lens[b] <= min(T, kv_lens[b]) (required).
+ *   kv_lens      [B] int32, cached tokens (no bound by T).
+ *   O, LSE, other arguments as for attn_prefill; rows t >= q_lens[b] are
+ *   written as O = 0, LSE = -INFINITY.  A q_len outside its range sets
+ *   PA_DEVERR_BAD_POS and is clamped into it.
+ */
+int attn_prefill_chunk(const void *q, const void *kv_cache, int64_t n_pages,
+                       const int32_t *block_table, int n_slots, int n_layers,
+                       int max_blocks_per_seq, int layer, const int32_t *slot_ids,
+                       const int32_t *q_lens, const int32_t *kv_lens, int B, int T, int Hq,
+                       int Hkv, int head_dim, float scale, int causal, void *O, float *LSE,
+                       int32_t *err, void *stream);
+
+/*
  * attn_decode -- attention of one new query per sequence over its whole cached
  * context, the newest token included (page 6, sections "pagedAttentionKernel"
  * and "logical block -> physical block -> byte address").  Long contexts are

@@ -55,6 +55,9 @@ def load():
         lib.attn_prefill.restype = _I
         lib.attn_prefill.argtypes = [_P, _P, _I64, _P, _I, _I, _I, _I, _P, _P, _I, _I, _I, _I, _I,
                                      _F, _I, _P, _P, _P, _P]
+        lib.attn_prefill_chunk.restype = _I
+        lib.attn_prefill_chunk.argtypes = [_P, _P, _I64, _P, _I, _I, _I, _I, _P, _P, _P, _I, _I, _I,
+                                           _I, _I, _F, _I, _P, _P, _P, _P]
         lib.attn_decode.restype = _I
         lib.attn_decode.argtypes = [_P, _P, _I64, _P, _I, _I, _I, _I, _P, _P, _I, _I, _I, _I, _F,
                                     _I, _P, _SZ, _P, _P, _P, _P]
@@ -125,22 +128,32 @@ def kv_scatter(k: torch.Tensor, v: torch.Tensor, slot_ids: torch.Tensor, positio
 def attn_prefill(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tensor, layer: int,
                  seq_lens: torch.Tensor, n_kv_heads: int, scale: float, causal: bool = True,
                  slot_ids: torch.Tensor | None = None, out: torch.Tensor | None = None,
-                 lse: torch.Tensor | None = None, err: torch.Tensor | None = None, stream=None):
-    """Paged prefill of q [B, T, Hq, d]; returns (O [B, T, Hq, d] bf16, LSE [B, Hq, T] fp32)."""
+                 lse: torch.Tensor | None = None, err: torch.Tensor | None = None, stream=None,
+                 q_lens: torch.Tensor | None = None):
+    """Paged prefill of q [B, T, Hq, d]; returns (O [B, T, Hq, d] bf16, LSE [B, Hq, T] fp32).
+
+    With q_lens, the queries of sequence b are the last q_lens[b] of its seq_lens[b] cached
+    tokens (attn_prefill_chunk: prefix continuation, mixed prefill + decode batches)."""
     B, T, Hq, d = q.shape
     n_slots, n_layers, mbps = block_table.shape
     if out is None:
         out = torch.empty_like(q)
     if lse is None:
         lse = torch.empty(B, Hq, T, dtype=torch.float32, device=q.device)
-    rc = load().attn_prefill(
-        _dev(q, torch.bfloat16, "q"), _dev(kv_cache, None, "kv_cache"),
-        _n_pages(kv_cache, n_kv_heads, d), _dev(block_table, torch.int32, "block_table"),
-        n_slots, n_layers, mbps, layer, _dev(slot_ids, torch.int32, "slot_ids"),
-        _dev(seq_lens, torch.int32, "seq_lens"), B, T, Hq, n_kv_heads, d, float(scale),
-        int(bool(causal)), _dev(out, torch.bfloat16, "out"), _dev(lse, torch.float32, "lse"),
-        _dev(err, torch.int32, "err"), _stream(stream))
-    _check(rc, "attn_prefill")
+    common = (_dev(kv_cache, None, "kv_cache"), _n_pages(kv_cache, n_kv_heads, d),
+              _dev(block_table, torch.int32, "block_table"), n_slots, n_layers, mbps, layer,
+              _dev(slot_ids, torch.int32, "slot_ids"))
+    tail = (B, T, Hq, n_kv_heads, d, float(scale), int(bool(causal)), _dev(out, torch.bfloat16, "out"),
+            _dev(lse, torch.float32, "lse"), _dev(err, torch.int32, "err"), _stream(stream))
+    if q_lens is None:
+        rc = load().attn_prefill(_dev(q, torch.bfloat16, "q"), *common,
+                                 _dev(seq_lens, torch.int32, "seq_lens"), *tail)
+        _check(rc, "attn_prefill")
+    else:
+        rc = load().attn_prefill_chunk(_dev(q, torch.bfloat16, "q"), *common,
+                                       _dev(q_lens, torch.int32, "q_lens"),
+                                       _dev(seq_lens, torch.int32, "seq_lens"), *tail)
+        _check(rc, "attn_prefill_chunk")
     return out, lse
 
 

@@ -30,6 +30,27 @@ int check_cache(const void *kv_cache, int64_t n_pages, const int32_t *block_tabl
   return PA_OK;
 }
 
+// Shared checks and launch of attn_prefill / attn_prefill_chunk.
+int prefill_common(const void *q, const void *kv_cache, int64_t n_pages, const int32_t *block_table,
+                   int n_slots, int n_layers, int max_blocks_per_seq, int layer,
+                   const int32_t *slot_ids, const int32_t *seq_lens, const int32_t *q_lens, int B,
+                   int T, int Hq, int Hkv, int head_dim, float scale, int causal, void *O,
+                   float *LSE, int32_t *err, void *stream) {
+  if (B < 0 || T < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0) return PA_ERR_SHAPE;
+  if (!supported_head_dim(head_dim)) return PA_ERR_UNSUPPORTED;
+  int rc = check_cache(kv_cache, n_pages, block_table, n_slots, n_layers, max_blocks_per_seq, layer,
+                       Hkv, head_dim);
+  if (rc != PA_OK) return rc;
+  if (B == 0 || T == 0) return PA_OK;
+  if (!q || !seq_lens || !O || !LSE) return PA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(O)) return PA_ERR_ALIGN;
+  if ((int64_t)B * T * Hq > 0x7fffffffLL) return PA_ERR_RANGE;
+  return pa::launch_prefill_paged(q, kv_cache, n_pages, block_table, n_slots, n_layers,
+                                  max_blocks_per_seq, layer, slot_ids, seq_lens, q_lens, B, T, Hq,
+                                  Hkv, head_dim, scale, causal, O, LSE, err,
+                                  static_cast<hipStream_t>(stream));
+}
+
 }  // namespace
 
 extern "C" {
@@ -75,19 +96,21 @@ int attn_prefill(const void *q, const void *kv_cache, int64_t n_pages, const int
                  const int32_t *slot_ids, const int32_t *seq_lens, int B, int T, int Hq, int Hkv,
                  int head_dim, float scale, int causal, void *O, float *LSE, int32_t *err,
                  void *stream) {
-  if (B < 0 || T < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0) return PA_ERR_SHAPE;
-  if (!supported_head_dim(head_dim)) return PA_ERR_UNSUPPORTED;
-  int rc = check_cache(kv_cache, n_pages, block_table, n_slots, n_layers, max_blocks_per_seq, layer,
-                       Hkv, head_dim);
-  if (rc != PA_OK) return rc;
-  if (B == 0 || T == 0) return PA_OK;
-  if (!q || !seq_lens || !O || !LSE) return PA_ERR_NULL;
-  if (!aligned16(q) || !aligned16(O)) return PA_ERR_ALIGN;
-  if ((int64_t)B * T * Hq > 0x7fffffffLL) return PA_ERR_RANGE;
-  return pa::launch_prefill_paged(q, kv_cache, n_pages, block_table, n_slots, n_layers,
-                                  max_blocks_per_seq, layer, slot_ids, seq_lens, B, T, Hq, Hkv,
-                                  head_dim, scale, causal, O, LSE, err,
-                                  static_cast<hipStream_t>(stream));
+  return prefill_common(q, kv_cache, n_pages, block_table, n_slots, n_layers, max_blocks_per_seq,
+                        layer, slot_ids, seq_lens, nullptr, B, T, Hq, Hkv, head_dim, scale, causal,
+                        O, LSE, err, stream);
+}
+
+int attn_prefill_chunk(const void *q, const void *kv_cache, int64_t n_pages,
+                       const int32_t *block_table, int n_slots, int n_layers,
+                       int max_blocks_per_seq, int layer, const int32_t *slot_ids,
+                       const int32_t *q_lens, const int32_t *kv_lens, int B, int T, int Hq,
+                       int Hkv, int head_dim, float scale, int causal, void *O, float *LSE,
+                       int32_t *err, void *stream) {
+  if (B > 0 && T > 0 && !q_lens) return PA_ERR_NULL;
+  return prefill_common(q, kv_cache, n_pages, block_table, n_slots, n_layers, max_blocks_per_seq,
+                        layer, slot_ids, kv_lens, q_lens, B, T, Hq, Hkv, head_dim, scale, causal,
+                        O, LSE, err, stream);
 }
 
 size_t attn_decode_workspace_size(int B, int Hq, int Hkv, int head_dim, int max_ctx) {

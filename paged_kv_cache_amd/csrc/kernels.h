@@ -14,9 +14,9 @@ int launch_kv_scatter(const void *k, const void *v, int64_t n_tokens, const int3
 
 int launch_prefill_paged(const void *q, const void *kv_cache, int64_t n_pages,
                          const int32_t *block_table, int n_slots, int n_layers, int mbps, int layer,
-                         const int32_t *slot_ids, const int32_t *seq_lens, int B, int T, int Hq,
-                         int Hkv, int D, float scale, int causal, void *O, float *LSE, int32_t *err,
-                         hipStream_t stream);
+                         const int32_t *slot_ids, const int32_t *seq_lens, const int32_t *q_lens,
+                         int B, int T, int Hq, int Hkv, int D, float scale, int causal, void *O,
+                         float *LSE, int32_t *err, hipStream_t stream);
 
 int launch_prefill_dense(const void *q, const void *k, const void *v, int B, int T, int Hq, int Hkv,
                          int D, float scale, int causal, void *O, float *LSE, hipStream_t stream);

@@ -62,7 +62,8 @@ struct PrefillArgs {
   int64_t n_pages;
   const int32_t *block_table;
   const int32_t *slot_ids;
-  const int32_t *seq_lens;
+  const int32_t *seq_lens;     // cached tokens (keys) per sequence
+  const int32_t *q_lens;       // query rows per sequence, the last of its tokens (null: all)
   int n_slots, n_layers, mbps, layer;
   const uint16_t *k;           // dense source [B][T][Hkv][D]
   const uint16_t *v;
@@ -172,7 +173,8 @@ __global__ __launch_bounds__(64 * (kBlocks / BPW), OCC) void prefill_kernel(Pref
   }
   const int wave_row_end = row0[BPW - 1] + 31;   // last row of this wave
 
-  int len = T;
+  int len = T;    // keys of this sequence (its cached tokens)
+  int qlen = T;   // its query rows: the last qlen of its len tokens
   // Errors are collected here and reported once at the end.
   int err_bits = 0;
   const int64_t page_bytes = 2LL * kPageTokens * a.Hkv * ROWB;
@@ -182,38 +184,49 @@ __global__ __launch_bounds__(64 * (kBlocks / BPW), OCC) void prefill_kernel(Pref
   if constexpr (PAGED) {
     const bool reporter = hg == 0 && rb == 0;   // one workgroup per sequence reports
     len = a.seq_lens[b];
-    if (len < 0 || len > T) {
+    if (len < 0 || (!a.q_lens && len > T)) {
       if (reporter) err_bits |= PA_DEVERR_BAD_POS;
       len = len < 0 ? 0 : T;
+    }
+    qlen = a.q_lens ? a.q_lens[b] : len;
+    if (qlen < 0 || qlen > T || qlen > len) {
+      if (reporter) err_bits |= PA_DEVERR_BAD_POS;
+      qlen = qlen < 0 ? 0 : min(min(qlen, T), len);
     }
     const int slot = a.slot_ids ? a.slot_ids[b] : b;
     if (slot < 0 || slot >= a.n_slots) {
       if (reporter) err_bits |= PA_DEVERR_BAD_SLOT;
       len = 0;
+      qlen = 0;
     }
     if (len > a.mbps * kPageTokens) {
       if (reporter) err_bits |= PA_DEVERR_BAD_POS;
       len = a.mbps * kPageTokens;
+      qlen = min(qlen, len);
     }
     len = uniform(len);
+    qlen = uniform(qlen);
     trow_v = a.block_table + ((int64_t)uniform(len > 0 ? slot : 0) * a.n_layers + a.layer) * a.mbps;
     trow = as_const(trow_v);
   }
 
-  const int wg_row_end = min(rb * BM + BM, len);
-  const int kv_end = a.causal ? wg_row_end : len;   // keys past this are never visible here
-  const int n_tiles = (kv_end > 0 && rb * BM < len) ? (kv_end + kBN - 1) / kBN : 0;
+  // query row t is the token at position off + t (a chunk continuing a cached
+  // prefix is aligned to the end of the sequence; off = 0 for a whole prompt)
+  const int off = len - qlen;
+  const int wg_row_end = min(rb * BM + BM, qlen);
+  const int kv_end = a.causal ? off + wg_row_end : len;   // keys past this are never visible here
+  const int n_tiles = (kv_end > 0 && rb * BM < qlen) ? (kv_end + kBN - 1) / kBN : 0;
   const int nblk = (kv_end + kPageTokens - 1) / kPageTokens;   // blocks read (paged)
   // last key each of this lane's rows may see (-1: padding row, sees nothing)
   int lim[BPW];
 #pragma unroll
   for (int i = 0; i < BPW; ++i) {
     const int row = row0[i] + lr;
-    lim[i] = row < len ? (a.causal ? row : len - 1) : -1;
+    lim[i] = row < qlen ? (a.causal ? off + row : len - 1) : -1;
   }
 
   // ---- Q^T as B operands: lane holds row row0[i] + lr, d = lh*(D/2) + k*8 + e
-  // A padding row (row >= len) takes the sequence's row 0 instead: its
+  // A padding row (row >= qlen) takes the sequence's row 0 instead: its
   // results are never written (O = 0, LSE = -inf), and a real row keeps its
   // scores finite.  (Unconditional loads: no wait between them.)
   bf16x8 qf[BPW][D / 16];
@@ -221,7 +234,7 @@ __global__ __launch_bounds__(64 * (kBlocks / BPW), OCC) void prefill_kernel(Pref
   for (int i = 0; i < BPW; ++i) {
     const int row = row0[i] + lr;
     const bf16x8 *qp = reinterpret_cast<const bf16x8 *>(
-        a.q + (((int64_t)b * T + (row < len ? row : 0)) * Hq + head[i]) * D + lh * (D / 2));
+        a.q + (((int64_t)b * T + (row < qlen ? row : 0)) * Hq + head[i]) * D + lh * (D / 2));
 #pragma unroll
     for (int k = 0; k < D / 16; ++k) qf[i][k] = qp[k];
   }
@@ -418,11 +431,13 @@ __global__ __launch_bounds__(64 * (kBlocks / BPW), OCC) void prefill_kernel(Pref
     l_lane[i] = 0.f;
   }
   bool started = false;            // some tile processed (wave-uniform)
-  // first tile whose scores need the mask: the causal diagonal of the block's
-  // rows (row0 is a multiple of 32) or the tile that crosses kv_end
+  // first tile whose scores need the mask: the first tile holding a key past
+  // the position of the block's first row (off + row0), or the tile that
+  // crosses kv_end
   int t_mask[BPW];
 #pragma unroll
-  for (int i = 0; i < BPW; ++i) t_mask[i] = min(a.causal ? row0[i] / kBN : 0x7fffffff, kv_end / kBN);
+  for (int i = 0; i < BPW; ++i)
+    t_mask[i] = min(a.causal ? (off + row0[i] + 1) / kBN : 0x7fffffff, kv_end / kBN);
   const float c = a.scale_log2;
 
   // ---- one key tile: S = K Q^T, online softmax, O^T += V^T P^T.  Every
@@ -567,7 +582,7 @@ __global__ __launch_bounds__(64 * (kBlocks / BPW), OCC) void prefill_kernel(Pref
   // one constant wait is exact; the compiler's own bookkeeping then agrees
   // and adds no drain of its own.
   // last tile this wave's rows see (causal): later tiles are skipped
-  const int t_last = a.causal ? wave_row_end / kBN : 0x7fffffff;
+  const int t_last = a.causal ? (off + wave_row_end) / kBN : 0x7fffffff;
   auto skip = [&](int t) { return t > t_last; };
   auto step = [&](int t, auto S_) {
     constexpr int S = decltype(S_)::value;
@@ -616,7 +631,7 @@ __global__ __launch_bounds__(64 * (kBlocks / BPW), OCC) void prefill_kernel(Pref
     const int row = row0[i] + lr;
     auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_lane[i]), __float_as_uint(l_lane[i]), false, false);
     const float l_row = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-    const bool has = row < len && l_row > 0.f;
+    const bool has = row < qlen && l_row > 0.f;
     const float inv_l = has ? 1.f / l_row : 0.f;
     if (row < T) {
       uint16_t *op = a.O + (((int64_t)b * T + row) * Hq + head[i]) * D;
@@ -690,9 +705,9 @@ static int dispatch_prefill(const PrefillArgs &a, int D, int G, hipStream_t stre
 
 int launch_prefill_paged(const void *q, const void *kv_cache, int64_t n_pages,
                          const int32_t *block_table, int n_slots, int n_layers, int mbps, int layer,
-                         const int32_t *slot_ids, const int32_t *seq_lens, int B, int T, int Hq,
-                         int Hkv, int D, float scale, int causal, void *O, float *LSE, int32_t *err,
-                         hipStream_t stream) {
+                         const int32_t *slot_ids, const int32_t *seq_lens, const int32_t *q_lens,
+                         int B, int T, int Hq, int Hkv, int D, float scale, int causal, void *O,
+                         float *LSE, int32_t *err, hipStream_t stream) {
   PrefillArgs a{};
   a.q = static_cast<const uint16_t *>(q);
   a.pool = static_cast<const uint8_t *>(kv_cache);
@@ -700,6 +715,7 @@ int launch_prefill_paged(const void *q, const void *kv_cache, int64_t n_pages,
   a.block_table = block_table;
   a.slot_ids = slot_ids;
   a.seq_lens = seq_lens;
+  a.q_lens = q_lens;
   a.n_slots = n_slots;
   a.n_layers = n_layers;
   a.mbps = mbps;

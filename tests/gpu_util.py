@@ -39,8 +39,10 @@ def run_prefill(case, pool: torch.Tensor | None = None, err: torch.Tensor | None
     if pool is None:
         pool = device_pool(c)
         scatter(pool, c, case.tokens, bt)
+    q_lens = getattr(case, "q_lens", None)
     O, L = pa.attn_prefill(case.q.to(DEV), pool, bt, c.layer, i32(case.seq_lens), c.n_kv_heads,
-                           case.scale, case.causal, slot_ids=i32(case.slot_ids), err=err)
+                           case.scale, case.causal, slot_ids=i32(case.slot_ids), err=err,
+                           q_lens=None if q_lens is None else i32(q_lens))
     return O, L, pool
 
 

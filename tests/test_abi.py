@@ -23,7 +23,7 @@ def test_header_declares_the_path():
     names = declared_functions()
     for n in ["kv_scatter", "attn_prefill", "attn_decode", "attn_prefill_dense",
               "attn_decode_workspace_size", "pa_status_string", "pa_page_bytes", "kv_append",
-              "kv_release"]:
+              "kv_release", "attn_prefill_chunk"]:
         assert n in names
 
 
@@ -89,6 +89,11 @@ def test_host_checks_reject_bad_arguments():
     assert lib.kv_scatter(good, good, 1, good, good, good, 1 << 31, good, 1, 1, 128, 0, 8, 64,
                           None, None) == -6
     assert lib.attn_prefill_dense(good, good, None, 1, 16, 4, 4, 64, 0.125, 1, good, good, None) == -1
+    # chunked prefill needs q_lens
+    assert lib.attn_prefill_chunk(good, good, 64, good, 1, 1, 128, 0, None, None, good, 1, 17, 32, 8,
+                                  64, 0.125, 1, good, good, None, None) == -1
+    assert lib.attn_prefill_chunk(good, good, 64, good, 1, 1, 128, 0, None, None, None, 0, 17, 32, 8,
+                                  64, 0.125, 1, good, good, None, None) == 0
 
 
 def _append(lib, **kw):
