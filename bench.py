@@ -317,12 +317,16 @@ def kernels_only(n: int) -> None:
     print(f"kernels-only: {n} launches each", flush=True)
 
 
-def sweep() -> None:
+SWEEP_PARTS = ("tiny", "dense", "long_prefill", "long_decode", "chunk", "append")
+
+
+def sweep(parts=SWEEP_PARTS) -> None:
     """The other configurations' measurements (one line each, then a
     markdown table): the 17-token prompt (latency), the dense FA2-shape grid
     (MHA, d 64 / 128, T 512..16k, B*T = 16k, causal and full), the long dense
-    prefill (B=1, T=16384, 16x128, causal), the long decode (4 x 16384), the
-    decode append of the 64-sequence batch and a release of 8 of its slots.
+    prefill (B=1, T=16384, 16x128, causal), the long decode (4 x 16384), a
+    prefix continuation and a mixed prefill + decode batch, the decode append
+    of the 64-sequence batch and a release of 8 of its slots.
     Kernel times are HIP-event averages over graph replays (kernel_time)."""
     rows = []
 
@@ -330,110 +334,136 @@ def sweep() -> None:
         rows.append((name, us, metric, unit, extra))
         print(f"sweep: {name}: {us:.2f} us, {metric:.2f} {unit} {extra}", flush=True)
 
-    # 17-token prefill: scatter and prefill separately
-    case = W.tiny_prefill()
-    c = case.cache
-    pool = device_pool(c)
-    bt = i32(c.block_table)
-    k, v = case.tokens.k.to(DEV), case.tokens.v.to(DEV)
-    slots, pos = i32(case.tokens.slot_ids), i32(case.tokens.positions)
-    q, lens, sid = case.q.to(DEV), i32(case.seq_lens), i32(case.slot_ids)
-    t_sc = kernel_time(lambda: pa.kv_scatter(k, v, slots, pos, pool, bt, c.layer))
-    t_pf = kernel_time(lambda: pa.attn_prefill(q, pool, bt, c.layer, lens, c.n_kv_heads, case.scale,
-                                               True, slot_ids=sid))
-    emit("17-token kv_scatter", t_sc * 1e6, t_sc * 1e6, "us")
-    emit("17-token prefill (32/8/64, paged)", t_pf * 1e6, prefill_flops(1, 17, 32, 64, True) / t_pf / 1e9,
-         "GFLOP/s")
-    del pool
+    if "tiny" in parts:
+        # 17-token prefill: scatter and prefill separately
+        case = W.tiny_prefill()
+        c = case.cache
+        pool = device_pool(c)
+        bt = i32(c.block_table)
+        k, v = case.tokens.k.to(DEV), case.tokens.v.to(DEV)
+        slots, pos = i32(case.tokens.slot_ids), i32(case.tokens.positions)
+        q, lens, sid = case.q.to(DEV), i32(case.seq_lens), i32(case.slot_ids)
+        t_sc = kernel_time(lambda: pa.kv_scatter(k, v, slots, pos, pool, bt, c.layer))
+        t_pf = kernel_time(lambda: pa.attn_prefill(q, pool, bt, c.layer, lens, c.n_kv_heads, case.scale,
+                                                   True, slot_ids=sid))
+        emit("17-token kv_scatter", t_sc * 1e6, t_sc * 1e6, "us")
+        emit("17-token prefill (32/8/64, paged)", t_pf * 1e6, prefill_flops(1, 17, 32, 64, True) / t_pf / 1e9,
+             "GFLOP/s")
+        del pool
 
-    # dense FA2 shapes
-    for d, H in W.FA2_HEADS:
-        for T in W.FA2_SEQLENS:
-            res = {}
-            for causal in (False, True):
-                dc = W.fa2_dense(T, d, causal)
-                qd, kd, vd = dc.q.to(DEV), dc.k.to(DEV), dc.v.to(DEV)
-                Od = torch.empty_like(qd)
-                Ld = torch.empty(dc.q.shape[0], H, T, dtype=torch.float32, device=DEV)
-                t = kernel_time(lambda: pa.attn_prefill_dense(qd, kd, vd, dc.scale, causal, out=Od, lse=Ld),
-                                reps=10, trials=3)
-                B = 16384 // T
-                res[causal] = t
-                emit(f"dense d={d} H={H} T={T} B={B} {'causal' if causal else 'full'}", t * 1e6,
-                     prefill_flops(B, T, H, d, causal) / t / 1e12, "TFLOP/s")
-                del qd, kd, vd, Od, Ld
-            rows[-1] = rows[-1][:4] + (f"full/causal time ratio {res[False] / res[True]:.2f}",)
+    if "dense" in parts:
+        # dense FA2 shapes
+        for d, H in W.FA2_HEADS:
+            for T in W.FA2_SEQLENS:
+                res = {}
+                for causal in (False, True):
+                    dc = W.fa2_dense(T, d, causal)
+                    qd, kd, vd = dc.q.to(DEV), dc.k.to(DEV), dc.v.to(DEV)
+                    Od = torch.empty_like(qd)
+                    Ld = torch.empty(dc.q.shape[0], H, T, dtype=torch.float32, device=DEV)
+                    t = kernel_time(lambda: pa.attn_prefill_dense(qd, kd, vd, dc.scale, causal, out=Od, lse=Ld),
+                                    reps=10, trials=3)
+                    B = 16384 // T
+                    res[causal] = t
+                    emit(f"dense d={d} H={H} T={T} B={B} {'causal' if causal else 'full'}", t * 1e6,
+                         prefill_flops(B, T, H, d, causal) / t / 1e12, "TFLOP/s")
+                    del qd, kd, vd, Od, Ld
+                rows[-1] = rows[-1][:4] + (f"full/causal time ratio {res[False] / res[True]:.2f}",)
 
-    # long dense prefill
-    lc = W.long_prefill()
-    ql, kl, vl = lc.q.to(DEV), lc.k.to(DEV), lc.v.to(DEV)
-    t = kernel_time(lambda: pa.attn_prefill_dense(ql, kl, vl, lc.scale, True), reps=5, trials=3)
-    emit("long prefill B=1 T=16384 16x128 causal (dense)", t * 1e6,
-         prefill_flops(1, 16384, 16, 128, True) / t / 1e12, "TFLOP/s")
-    del ql, kl, vl
+    if "long_prefill" in parts:
+        # long dense prefill
+        lc = W.long_prefill()
+        ql, kl, vl = lc.q.to(DEV), lc.k.to(DEV), lc.v.to(DEV)
+        t = kernel_time(lambda: pa.attn_prefill_dense(ql, kl, vl, lc.scale, True), reps=5, trials=3)
+        emit("long prefill B=1 T=16384 16x128 causal (dense)", t * 1e6,
+             prefill_flops(1, 16384, 16, 128, True) / t / 1e12, "TFLOP/s")
+        del ql, kl, vl
 
-    # long decode, 2 page-disjoint replicas cycled
-    dcase = W.long_decode()
-    c = dcase.cache
-    pool = device_pool(c)
-    tables = [i32(tb) for tb in decode_replicas(dcase, 2)]
-    for tb in tables:
-        for tok in (dcase.context, dcase.new_tokens):
-            pa.kv_scatter(tok.k.to(DEV), tok.v.to(DEV), i32(tok.slot_ids), i32(tok.positions), pool, tb,
-                          c.layer)
-    qd, lens, sid = dcase.q.to(DEV), i32(dcase.ctx_lens), i32(dcase.slot_ids)
-    ws = pa.decode_workspace(dcase.B, dcase.Hq, c.n_kv_heads, dcase.d, dcase.max_ctx, DEV)
-    t = kernel_time(lambda: [pa.attn_decode(qd, pool, tb, c.layer, lens, c.n_kv_heads, dcase.scale,
-                                            dcase.max_ctx, slot_ids=sid, workspace=ws) for tb in tables],
-                    reps=4) / len(tables)
-    kvb = int(dcase.ctx_lens.sum()) * c.n_kv_heads * dcase.d * 2 * 2
-    n_splits = pa.decode_splits(dcase.B, dcase.Hq, c.n_kv_heads, dcase.d, dcase.max_ctx)
-    emit("long decode 4 x 16384 (32/8/64, paged)", t * 1e6, kvb / t / 1e9, "GB/s",
-         f"{n_splits} workgroup splits per context (+ combine kernel)")
+    if "long_decode" in parts:
+        # long decode, 2 page-disjoint replicas cycled
+        dcase = W.long_decode()
+        c = dcase.cache
+        pool = device_pool(c)
+        tables = [i32(tb) for tb in decode_replicas(dcase, 2)]
+        for tb in tables:
+            for tok in (dcase.context, dcase.new_tokens):
+                pa.kv_scatter(tok.k.to(DEV), tok.v.to(DEV), i32(tok.slot_ids), i32(tok.positions), pool, tb,
+                              c.layer)
+        qd, lens, sid = dcase.q.to(DEV), i32(dcase.ctx_lens), i32(dcase.slot_ids)
+        ws = pa.decode_workspace(dcase.B, dcase.Hq, c.n_kv_heads, dcase.d, dcase.max_ctx, DEV)
+        t = kernel_time(lambda: [pa.attn_decode(qd, pool, tb, c.layer, lens, c.n_kv_heads, dcase.scale,
+                                                dcase.max_ctx, slot_ids=sid, workspace=ws) for tb in tables],
+                        reps=4) / len(tables)
+        kvb = int(dcase.ctx_lens.sum()) * c.n_kv_heads * dcase.d * 2 * 2
+        n_splits = pa.decode_splits(dcase.B, dcase.Hq, c.n_kv_heads, dcase.d, dcase.max_ctx)
+        emit("long decode 4 x 16384 (32/8/64, paged)", t * 1e6, kvb / t / 1e9, "GB/s",
+             f"{n_splits} workgroup splits per context (+ combine kernel)")
 
-    # decode append for the 64-sequence batch: RoPE of K and q, page pops, K/V write
-    ac = W.llama_append()
-    dc = ac.decode
-    c = dc.cache
-    pool = device_pool(c)
-    bt = i32(ac.block_table)
-    free_np = np.full(c.n_pages, -1, np.int32)
-    free_np[:ac.top] = ac.free_pages
-    free = i32(free_np)
-    alloc = pa.new_alloc_state(ac.top, DEV)
-    cos_t = torch.from_numpy(ac.cos_t).to(DEV)
-    sin_t = torch.from_numpy(ac.sin_t).to(DEV)
-    nt = dc.new_tokens
-    nk, nv, npos, nsl = nt.k.to(DEV), nt.v.to(DEV), i32(nt.positions), i32(dc.slot_ids)
-    qa = dc.q.to(DEV)
-    q_out = torch.empty_like(qa)
-    t = kernel_time(lambda: pa.kv_append(nk, nv, npos, cos_t, sin_t, pool, bt, c.layer, free, alloc,
-                                         slot_ids=nsl, q=qa, q_out=q_out))
-    n_open = int(((nt.positions % 16) == 0).sum())
-    ab = (2 * nk.numel() + 2 * qa.numel()) * 2 * 2 + dc.B * ac.cos_t.shape[1] * 4 * 2 + n_open * 4
-    emit("kv_append B=64 (32/8/64): RoPE of K and q, page pops, K/V write", t * 1e6, ab / t / 1e9, "GB/s",
-         f"{n_open} of {dc.B} tokens open a page; {ab} bytes moved")
+    if "chunk" in parts:
+        # prefix continuation and a mixed prefill + decode batch (attn_prefill_chunk);
+        # FLOPs count every visible (query, key) pair: 4 * d * Hq per pair
+        for cc, label in ((W.llama_chunk(), "chunk: 2 x (2048 cached + 2048 new), 32/8/64, causal"),
+                          (W.mixed_batch(), "mixed: 2 chunks of 512 + 62 decode rows, 32/8/64")):
+            c = cc.cache
+            pool = device_pool(c)
+            bt = i32(c.block_table)
+            pa.kv_scatter(cc.tokens.k.to(DEV), cc.tokens.v.to(DEV), i32(cc.tokens.slot_ids),
+                          i32(cc.tokens.positions), pool, bt, c.layer)
+            qc, kvl, ql, sid = cc.q.to(DEV), i32(cc.seq_lens), i32(cc.q_lens), i32(cc.slot_ids)
+            Oc = torch.empty_like(qc)
+            Lc = torch.empty(cc.B, cc.Hq, cc.T, dtype=torch.float32, device=DEV)
+            t = kernel_time(lambda: pa.attn_prefill(qc, pool, bt, c.layer, kvl, c.n_kv_heads, cc.scale, True,
+                                                    slot_ids=sid, out=Oc, lse=Lc, q_lens=ql), reps=10, trials=3)
+            pairs = sum(int(q) * (int(k) - int(q)) + int(q) * (int(q) + 1) // 2
+                        for q, k in zip(cc.q_lens, cc.seq_lens))
+            emit(label, t * 1e6, 4.0 * cc.d * cc.Hq * pairs / t / 1e12, "TFLOP/s",
+                 f"{pairs} visible (query, key) pairs per head")
+            del pool, qc, Oc, Lc
 
-    # release of 8 of the 64 sequences (one workgroup, in order): graphs of
-    # (restore the table and the stack top, release) minus graphs of the restore alone
-    bt0, alloc0 = bt.clone(), alloc.clone()
-    rel = i32(np.arange(8))
-    n_rel = int((ac.block_table[:8] >= 0).sum())
+    if "append" in parts:
+        # decode append for the 64-sequence batch: RoPE of K and q, page pops, K/V write
+        ac = W.llama_append()
+        dc = ac.decode
+        c = dc.cache
+        pool = device_pool(c)
+        bt = i32(ac.block_table)
+        free_np = np.full(c.n_pages, -1, np.int32)
+        free_np[:ac.top] = ac.free_pages
+        free = i32(free_np)
+        alloc = pa.new_alloc_state(ac.top, DEV)
+        cos_t = torch.from_numpy(ac.cos_t).to(DEV)
+        sin_t = torch.from_numpy(ac.sin_t).to(DEV)
+        nt = dc.new_tokens
+        nk, nv, npos, nsl = nt.k.to(DEV), nt.v.to(DEV), i32(nt.positions), i32(dc.slot_ids)
+        qa = dc.q.to(DEV)
+        q_out = torch.empty_like(qa)
+        t = kernel_time(lambda: pa.kv_append(nk, nv, npos, cos_t, sin_t, pool, bt, c.layer, free, alloc,
+                                             slot_ids=nsl, q=qa, q_out=q_out))
+        n_open = int(((nt.positions % 16) == 0).sum())
+        ab = (2 * nk.numel() + 2 * qa.numel()) * 2 * 2 + dc.B * ac.cos_t.shape[1] * 4 * 2 + n_open * 4
+        emit("kv_append B=64 (32/8/64): RoPE of K and q, page pops, K/V write", t * 1e6, ab / t / 1e9, "GB/s",
+             f"{n_open} of {dc.B} tokens open a page; {ab} bytes moved")
 
-    def restore():
-        bt.copy_(bt0)
-        alloc.copy_(alloc0)
+        # release of 8 of the 64 sequences (one workgroup, in order): graphs of
+        # (restore the table and the stack top, release) minus graphs of the restore alone
+        bt0, alloc0 = bt.clone(), alloc.clone()
+        rel = i32(np.arange(8))
+        n_rel = int((ac.block_table[:8] >= 0).sum())
 
-    def restore_release():
-        restore()
-        pa.kv_release(rel, bt, free, alloc)
+        def restore():
+            bt.copy_(bt0)
+            alloc.copy_(alloc0)
 
-    t_rr = kernel_time(restore_release)
-    t_r = kernel_time(restore)
-    us = (t_rr - t_r) * 1e6
-    emit("kv_release of 8 slots (1 layer x 128 blocks each)", us, n_rel / us, "pages/us",
-         f"{n_rel} pages pushed; graph of restore+release minus graph of restore")
-    del pool
+        def restore_release():
+            restore()
+            pa.kv_release(rel, bt, free, alloc)
+
+        t_rr = kernel_time(restore_release)
+        t_r = kernel_time(restore)
+        us = (t_rr - t_r) * 1e6
+        emit("kv_release of 8 slots (1 layer x 128 blocks each)", us, n_rel / us, "pages/us",
+             f"{n_rel} pages pushed; graph of restore+release minus graph of restore")
+        del pool
 
     print("\n| workload | time (us) | throughput | note |\n|---|---:|---:|---|")
     for name, us, metric, unit, extra in rows:
@@ -448,9 +478,9 @@ def main() -> int:
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--kernels-only", type=int, default=0, metavar="N",
                     help="launch each dominant kernel N times for a counter run; no JSON")
-    ap.add_argument("--sweep", action="store_true",
-                    help="measure the other configurations (17-token prompt, dense FA2 grid, "
-                         "long prefill, long decode); no JSON")
+    ap.add_argument("--sweep", nargs="*", default=None, metavar="PART",
+                    help="measure the other configurations instead of the JSON line; parts: "
+                         + ", ".join(SWEEP_PARTS) + " (default: all)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -461,8 +491,12 @@ def main() -> int:
     if args.kernels_only:
         kernels_only(args.kernels_only)
         return 0
-    if args.sweep:
-        sweep()
+    if args.sweep is not None:
+        bad = [x for x in args.sweep if x not in SWEEP_PARTS]
+        if bad:
+            print(f"unknown sweep part(s): {bad}", file=sys.stderr)
+            return 2
+        sweep(tuple(args.sweep) or SWEEP_PARTS)
         return 0
 
     p = bench_prefill(args.steps, args.warmup)

@@ -216,6 +216,25 @@ __global__ __launch_bounds__(64 * (kBlocks / BPW), OCC) void prefill_kernel(Pref
   const int wg_row_end = min(rb * BM + BM, qlen);
   const int kv_end = a.causal ? off + wg_row_end : len;   // keys past this are never visible here
   const int n_tiles = (kv_end > 0 && rb * BM < qlen) ? (kv_end + kBN - 1) / kBN : 0;
+  if (n_tiles == 0) {
+    // every row of this workgroup is padding (rows past the query length of a
+    // short sequence in a padded batch): O = 0, LSE = -inf, nothing else
+    if (err_bits && tid == 0) raise_err(a.err, err_bits);
+#pragma unroll
+    for (int i = 0; i < BPW; ++i) {
+      const int row = row0[i] + lr;
+      if (row < T) {
+        uint16_t *op = a.O + (((int64_t)b * T + row) * Hq + head[i]) * D;
+#pragma unroll
+        for (int mb = 0; mb < D / 32; ++mb)
+#pragma unroll
+          for (int g = 0; g < 4; ++g)
+            *reinterpret_cast<uint2 *>(op + mb * 32 + 8 * g + 4 * lh) = make_uint2(0u, 0u);
+        if (lh == 0) a.LSE[((int64_t)b * Hq + head[i]) * T + row] = -INFINITY;
+      }
+    }
+    return;
+  }
   const int nblk = (kv_end + kPageTokens - 1) / kPageTokens;   // blocks read (paged)
   // last key each of this lane's rows may see (-1: padding row, sees nothing)
   int lim[BPW];
