@@ -592,3 +592,110 @@ int oracle_kv_release(const int32_t *slots, int n, int32_t *block_table, int n_s
     }
     return errs;
 }
+
+/* ------------------------------------------------------------------------ */
+/* Backward of the dense attention (FlashAttention-2 explainer, "Results"   */
+/* and the MQA/GQA paragraph: gradients of the same exact attention; the     */
+/* key/value gradients of a GQA group are summed over its query heads).     */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * Gradients of loss = sum(O * dO) for O = softmax(scale * q K^T) V over the
+ * visible keys, written out from the derivative of that definition, row by
+ * row (i = query row, j = visible key):
+ *   P_ij  = exp(s_ij - LSE_i)                     (the forward's weights)
+ *   dV_j += P_ij dO_i
+ *   dP_ij = dO_i . V_j
+ *   D_i   = sum_j P_ij dP_ij
+ *   dS_ij = P_ij (dP_ij - D_i)
+ *   dQ_i  = scale * sum_j dS_ij K_j
+ *   dK_j += scale * dS_ij q_i
+ * Inputs as oracle_attn_dense plus dO [B][T][Hq][d] (bf16); outputs dQ
+ * [B][T][Hq][d], dK, dV [B][T][Hkv][d] in double.  aQ, aK, aV (nullable)
+ * receive the same sums taken over absolute values of every term
+ * (|dS_ij| |K_j| ...), the scale of each output's rounding error.
+ */
+void oracle_attn_dense_backward(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                                const uint16_t *dout, int B, int T, int Hq, int Hkv, int d,
+                                double scale, int causal, double *dQ, double *dK, double *dV,
+                                double *aQ, double *aK, double *aV)
+{
+    int g = Hq / Hkv;
+    int64_t nkv = (int64_t)B * T * Hkv * d;
+    memset(dK, 0, sizeof(double) * (size_t)nkv);
+    memset(dV, 0, sizeof(double) * (size_t)nkv);
+    if (aK)
+        memset(aK, 0, sizeof(double) * (size_t)nkv);
+    if (aV)
+        memset(aV, 0, sizeof(double) * (size_t)nkv);
+    /* one (sequence, kv head) per task: its dK, dV rows belong to it alone */
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t bk = 0; bk < (int64_t)B * Hkv; ++bk) {
+        int b = (int)(bk / Hkv), kvh = (int)(bk % Hkv);
+        double *s = malloc(sizeof(double) * (size_t)T);
+        double *dp = malloc(sizeof(double) * (size_t)T);
+        double *qd = malloc(sizeof(double) * (size_t)d);
+        double *od = malloc(sizeof(double) * (size_t)d);
+        for (int h = kvh * g; h < (kvh + 1) * g; ++h) {
+            for (int i = 0; i < T; ++i) {
+                int n = causal ? i + 1 : T;
+                const uint16_t *qr = q + (((int64_t)b * T + i) * Hq + h) * d;
+                const uint16_t *dor = dout + (((int64_t)b * T + i) * Hq + h) * d;
+                for (int c = 0; c < d; ++c) {
+                    qd[c] = bf16_to_double(qr[c]);
+                    od[c] = bf16_to_double(dor[c]);
+                }
+                double m = -INFINITY;
+                for (int j = 0; j < n; ++j) {
+                    const uint16_t *kr = k + (((int64_t)b * T + j) * Hkv + kvh) * d;
+                    const uint16_t *vr = v + (((int64_t)b * T + j) * Hkv + kvh) * d;
+                    double dot = 0.0, dv = 0.0;
+                    for (int c = 0; c < d; ++c) {
+                        dot += qd[c] * bf16_to_double(kr[c]);
+                        dv += od[c] * bf16_to_double(vr[c]);
+                    }
+                    s[j] = scale * dot;
+                    dp[j] = dv;
+                    if (s[j] > m)
+                        m = s[j];
+                }
+                double l = 0.0;
+                for (int j = 0; j < n; ++j)
+                    l += exp(s[j] - m);
+                double lse = m + log(l);
+                double D = 0.0;
+                for (int j = 0; j < n; ++j)
+                    D += exp(s[j] - lse) * dp[j];
+                double *dq = dQ + (((int64_t)b * T + i) * Hq + h) * d;
+                double *aq = aQ ? aQ + (((int64_t)b * T + i) * Hq + h) * d : NULL;
+                for (int c = 0; c < d; ++c) {
+                    dq[c] = 0.0;
+                    if (aq)
+                        aq[c] = 0.0;
+                }
+                for (int j = 0; j < n; ++j) {
+                    double p = exp(s[j] - lse);
+                    double ds = p * (dp[j] - D);
+                    int64_t kvo = (((int64_t)b * T + j) * Hkv + kvh) * d;
+                    const uint16_t *kr = k + kvo;
+                    for (int c = 0; c < d; ++c) {
+                        double kc = bf16_to_double(kr[c]);
+                        dq[c] += scale * ds * kc;
+                        dK[kvo + c] += scale * ds * qd[c];
+                        dV[kvo + c] += p * od[c];
+                        if (aq)
+                            aq[c] += scale * fabs(ds * kc);
+                        if (aK)
+                            aK[kvo + c] += scale * fabs(ds * qd[c]);
+                        if (aV)
+                            aV[kvo + c] += fabs(p * od[c]);
+                    }
+                }
+            }
+        }
+        free(s);
+        free(dp);
+        free(qd);
+        free(od);
+    }
+}

@@ -3,8 +3,8 @@
 Each mutant is a plausible slip in ``oracle/oracle.c`` (a dropped term, a
 wrong sign, a wrong index or stride, a transposed operand).  The copy is
 compiled on the CPU into a temporary library and the pins of
-``test_oracle.py``, ``test_oracle_append.py`` and ``test_oracle_chunk.py``
-run against it in a child process (a mutant may read out of
+``test_oracle.py``, ``test_oracle_append.py``, ``test_oracle_chunk.py`` and
+``test_oracle_backward.py`` run against it in a child process (a mutant may read out of
 bounds and crash, which also counts as caught).  The real oracle is never
 modified.
 """
@@ -58,12 +58,22 @@ MUTANTS = [
      "uint16_t vb = double_to_bf16(y[c]);"),
     ("release_descending", "for (int blk = 0; blk < mbps; ++blk) {", "for (int blk = mbps - 1; blk >= 0; --blk) {"),
     ("release_keeps_entry", "                *entry = -1;\n", "\n"),
+    # backward
+    ("bwd_drop_D", "double ds = p * (dp[j] - D);", "double ds = p * dp[j];"),
+    ("bwd_dq_no_scale", "dq[c] += scale * ds * kc;", "dq[c] += ds * kc;"),
+    ("bwd_dv_uses_ds", "dV[kvo + c] += p * od[c];", "dV[kvo + c] += ds * od[c];"),
+    ("bwd_dk_uses_p", "dK[kvo + c] += scale * ds * qd[c];", "dK[kvo + c] += scale * p * qd[c];"),
+    ("bwd_causal_off_by_one", "int n = causal ? i + 1 : T;", "int n = causal ? i : T;"),
+    ("bwd_dp_uses_k", "dv += od[c] * bf16_to_double(vr[c]);", "dv += od[c] * bf16_to_double(kr[c]);"),
+    ("bwd_gqa_interleaved", "for (int h = kvh * g; h < (kvh + 1) * g; ++h) {",
+     "for (int h = kvh; h < Hq; h += Hkv) {"),
 ]
 
 RUNNER = textwrap.dedent("""
     import sys, traceback
     sys.path.insert(0, {root!r}); sys.path.insert(0, {tests!r})
     import oracle, test_oracle as T, test_oracle_append as A, test_oracle_chunk as C
+    import test_oracle_backward as G
     import inspect
     failed = []
     pins = [
@@ -94,6 +104,11 @@ RUNNER = textwrap.dedent("""
         (C.test_chunk_single_row_is_decode, {{}}),
         (C.test_chunk_zero_query_closed_form, {{}}),
         (C.test_chunk_matches_numpy_direct, dict(causal=True)),
+        (G.test_backward_matches_autograd, dict(Hq=4, Hkv=1, d=64, causal=True)),
+        (G.test_backward_matches_autograd, dict(Hq=8, Hkv=2, d=128, causal=False)),
+        (G.test_backward_single_key, {{}}),
+        (G.test_backward_zero_query_dv_closed_form, {{}}),
+        (G.test_backward_key_gradients_sum_to_zero, dict(causal=True)),
     ]
     for fn, kw in pins:
         try:

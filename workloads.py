@@ -160,6 +160,7 @@ class DenseCase:
     v: torch.Tensor
     scale: float
     causal: bool
+    dout: torch.Tensor | None = None  # [B, T, Hq, d]: upstream gradient (backward cases)
 
 
 def _assign_pages(perm: np.ndarray, cursor: int, n_blocks: int) -> tuple[np.ndarray, int]:
@@ -325,13 +326,16 @@ def make_decode(name: str, *, B: int, Hq: int, Hkv: int, d: int, n_pages: int,
 
 
 def make_dense(name: str, *, B: int, T: int, Hq: int, Hkv: int, d: int, causal: bool,
-               seed: int = 0, scale: float | None = None) -> DenseCase:
+               seed: int = 0, scale: float | None = None, grad: bool = False) -> DenseCase:
+    """Contiguous Q, K, V [B, T, H, d]; with ``grad`` also the upstream gradient dO
+    (drawn after V from the same generator, so Q, K, V are those of the forward case)."""
     gen = torch.Generator().manual_seed(seed)
     q = _randn_bf16(gen, (B, T, Hq, d))
     k = _randn_bf16(gen, (B, T, Hkv, d))
     v = _randn_bf16(gen, (B, T, Hkv, d))
+    dout = _randn_bf16(gen, (B, T, Hq, d)) if grad else None
     scale = float(np.float32(1.0 / np.sqrt(d))) if scale is None else float(np.float32(scale))
-    return DenseCase(name=name, q=q, k=k, v=v, scale=scale, causal=causal)
+    return DenseCase(name=name, q=q, k=k, v=v, scale=scale, causal=causal, dout=dout)
 
 
 # ---------------------------------------------------------------------------
@@ -379,11 +383,12 @@ FA2_SEQLENS = (512, 1024, 2048, 4096, 8192, 16384)
 FA2_HEADS = ((64, 32), (128, 16))      # (head_dim, heads): hidden 2048
 
 
-def fa2_dense(T: int, d: int, causal: bool, seed: int = 0) -> DenseCase:
-    """FlashAttention-2 benchmark shape: hidden 2048, batch x seqlen = 16384 tokens, MHA."""
+def fa2_dense(T: int, d: int, causal: bool, seed: int = 0, grad: bool = False) -> DenseCase:
+    """FlashAttention-2 benchmark shape: hidden 2048, batch x seqlen = 16384 tokens, MHA
+    (with ``grad``: plus the upstream gradient, for the backward)."""
     H = 2048 // d
     return make_dense(f"dense_fa2_t{T}_d{d}_{'causal' if causal else 'full'}", B=16384 // T, T=T,
-                      Hq=H, Hkv=H, d=d, causal=causal, seed=seed)
+                      Hq=H, Hkv=H, d=d, causal=causal, seed=seed, grad=grad)
 
 
 # ---------------------------------------------------------------------------
