@@ -207,6 +207,33 @@ int attn_prefill_dense(const void *q, const void *k, const void *v, int B, int T
                        int head_dim, float scale, int causal, void *O, float *LSE, void *stream);
 
 /*
+ * attn_backward_dense -- gradients of exact attention on contiguous Q, K, V
+ * (FlashAttention-2 explainer, "Parallelise along the sequence length": P is
+ * recomputed from the stored log-sum-exp; MQA/GQA paragraph: dK, dV of a kv
+ * head are the sums over the q heads that share it).  With S = scale q K^T,
+ * P = exp(S - LSE) over the visible keys and D_i = sum_c dO_ic O_ic:
+ *   dV_j = sum_i P_ij dO_i,  dS_ij = P_ij (dO_i . V_j - D_i),
+ *   dQ_i = scale sum_j dS_ij K_j,  dK_j = scale sum_i dS_ij q_i.
+ *
+ *   q, o, dout   [B][T][Hq][head_dim] bf16 (o: the forward's output).
+ *   k, v         [B][T][Hkv][head_dim] bf16.
+ *   lse          [B][Hq][T] fp32, the forward's LSE (natural log).
+ *   dq           [B][T][Hq][head_dim] bf16 output; dk, dv [B][T][Hkv][head_dim]
+ *                bf16 outputs (every element written once: deterministic).
+ *   workspace    attn_backward_workspace_size(B, T, Hq) bytes, 16-byte
+ *                aligned (per-row D and LSE); contents on entry do not matter.
+ *   causal, scale as for attn_prefill_dense.  Supported: head_dim 64 or 128,
+ *   Hq/Hkv in {1, 2, 4, 8}.  Three launches on `stream`.
+ */
+int attn_backward_dense(const void *q, const void *k, const void *v, const void *o,
+                        const void *dout, const float *lse, int B, int T, int Hq, int Hkv,
+                        int head_dim, float scale, int causal, void *dq, void *dk, void *dv,
+                        void *workspace, size_t workspace_bytes, void *stream);
+
+/* Workspace bytes attn_backward_dense needs (0 on bad sizes). */
+size_t attn_backward_workspace_size(int B, int T, int Hq);
+
+/*
  * kv_append -- the cache writes of one decode step in one launch: for each of
  * B new tokens (one per sequence), in batch order,
  *   1. if its position opens a block (position % 16 == 0: tiny-vllm part 6,

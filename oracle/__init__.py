@@ -78,8 +78,8 @@ def _bind(lib):
     lib.oracle_kv_release.restype = _I
     lib.oracle_kv_release.argtypes = [_P, _I, _P, _I, _I, _I, _P, _P, _I]
     lib.oracle_attn_dense_backward.restype = None
-    lib.oracle_attn_dense_backward.argtypes = [_P, _P, _P, _P, _I, _I, _I, _I, _I, _D, _I, _P, _P, _P,
-                                               _P, _P, _P]
+    lib.oracle_attn_dense_backward.argtypes = [_P, _P, _P, _P, _I, _I, _I, _I, _I, _D, _I, _P, _I,
+                                               _P, _P, _P, _P, _P, _P, _P, _P]
     lib.oracle_attn_dense.restype = None
     lib.oracle_attn_dense.argtypes = [_P, _P, _P, _I, _I, _I, _I, _I, _D, _I, _P, _I64, _P, _P]
     return lib
@@ -182,21 +182,26 @@ def attn_dense(q, k, v, scale: float, causal: bool, rows=None):
     return O, L
 
 
-def attn_dense_backward(q, k, v, dout, scale: float, causal: bool, with_abs: bool = False):
+def attn_dense_backward(q, k, v, dout, scale: float, causal: bool, with_abs: bool = False,
+                        pairs=None):
     """Gradients of sum(O * dout) w.r.t. q, k, v (contiguous [B,T,H,d] bf16 inputs).
 
-    Returns (dQ, dK, dV) in float64, plus (aQ, aK, aV) -- the same sums over the
-    absolute values of their terms -- when with_abs."""
+    Returns (dQ, dK, dV) in float64; with with_abs also (aQ, aK, aV) -- the same sums
+    over the absolute values of their terms -- and (eQ, eK), the bounds on how far dQ,
+    dK move when D is computed from a bf16-rounded forward output.  pairs: evaluate only
+    these (b, kv head) pairs (the other outputs are 0)."""
     qb, kb, vb, ob = _bits(q), _bits(k), _bits(v), _bits(dout)
     B, T, Hq, d = qb.shape
     Hkv = kb.shape[2]
     dQ = np.empty((B, T, Hq, d), np.float64)
     dK = np.empty((B, T, Hkv, d), np.float64)
     dV = np.empty((B, T, Hkv, d), np.float64)
-    a = [np.empty_like(x) for x in (dQ, dK, dV)] if with_abs else [None, None, None]
+    a = [np.empty_like(x) for x in (dQ, dK, dV, dQ, dK)] if with_abs else [None] * 5
+    pr = None if pairs is None else _i32(pairs).reshape(-1, 2)
     load().oracle_attn_dense_backward(_ptr(qb), _ptr(kb), _ptr(vb), _ptr(ob), B, T, Hq, Hkv, d,
-                                      float(scale), int(bool(causal)), _ptr(dQ), _ptr(dK), _ptr(dV),
-                                      _ptr(a[0]), _ptr(a[1]), _ptr(a[2]))
+                                      float(scale), int(bool(causal)), _ptr(pr),
+                                      0 if pr is None else pr.shape[0], _ptr(dQ), _ptr(dK), _ptr(dV),
+                                      _ptr(a[0]), _ptr(a[1]), _ptr(a[2]), _ptr(a[3]), _ptr(a[4]))
     return (dQ, dK, dV, *a) if with_abs else (dQ, dK, dV)
 
 

@@ -614,13 +614,28 @@ int oracle_kv_release(const int32_t *slots, int n, int32_t *block_table, int n_s
  * [B][T][Hq][d], dK, dV [B][T][Hkv][d] in double.  aQ, aK, aV (nullable)
  * receive the same sums taken over absolute values of every term
  * (|dS_ij| |K_j| ...), the scale of each output's rounding error.
+ * pairs (nullable, n_pairs (b, kv head) pairs): evaluate only those.
+ * eQ, eK (nullable): how far dQ, dK move when D_i is taken from an output O
+ * that was rounded to bf16 after a product with bf16-rounded weights, as an
+ * implementation that reads the forward's O does: with
+ *   E_i = 2^-9 * sum_c |dO_ic| (|O_ic| + sum_j P_ij |V_jc|)     (bound on |dD_i|)
+ * eQ_ic = scale E_i sum_j P_ij |K_jc| and eK_jc = scale sum_i P_ij E_i |q_ic|.
  */
 void oracle_attn_dense_backward(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                                 const uint16_t *dout, int B, int T, int Hq, int Hkv, int d,
-                                double scale, int causal, double *dQ, double *dK, double *dV,
-                                double *aQ, double *aK, double *aV)
+                                double scale, int causal, const int32_t *pairs, int n_pairs,
+                                double *dQ, double *dK, double *dV, double *aQ, double *aK,
+                                double *aV, double *eQ, double *eK)
 {
     int g = Hq / Hkv;
+    int64_t nq = (int64_t)B * T * Hq * d;
+    memset(dQ, 0, sizeof(double) * (size_t)nq);
+    if (aQ)
+        memset(aQ, 0, sizeof(double) * (size_t)nq);
+    if (eQ)
+        memset(eQ, 0, sizeof(double) * (size_t)nq);
+    if (eK)
+        memset(eK, 0, sizeof(double) * (size_t)((int64_t)B * T * Hkv * d));
     int64_t nkv = (int64_t)B * T * Hkv * d;
     memset(dK, 0, sizeof(double) * (size_t)nkv);
     memset(dV, 0, sizeof(double) * (size_t)nkv);
@@ -628,14 +643,20 @@ void oracle_attn_dense_backward(const uint16_t *q, const uint16_t *k, const uint
         memset(aK, 0, sizeof(double) * (size_t)nkv);
     if (aV)
         memset(aV, 0, sizeof(double) * (size_t)nkv);
-    /* one (sequence, kv head) per task: its dK, dV rows belong to it alone */
+    /* one (sequence, kv head) per task: its dK, dV rows belong to it alone;
+       pairs (nullable): only the listed (b, kv head) pairs are evaluated, the
+       outputs of the others stay 0 */
+    int64_t n_tasks = pairs ? n_pairs : (int64_t)B * Hkv;
 #pragma omp parallel for schedule(dynamic, 1)
-    for (int64_t bk = 0; bk < (int64_t)B * Hkv; ++bk) {
+    for (int64_t task = 0; task < n_tasks; ++task) {
+        int64_t bk = pairs ? (int64_t)pairs[2 * task] * Hkv + pairs[2 * task + 1] : task;
         int b = (int)(bk / Hkv), kvh = (int)(bk % Hkv);
         double *s = malloc(sizeof(double) * (size_t)T);
         double *dp = malloc(sizeof(double) * (size_t)T);
         double *qd = malloc(sizeof(double) * (size_t)d);
         double *od = malloc(sizeof(double) * (size_t)d);
+        double *oex = malloc(sizeof(double) * (size_t)d);
+        double *pva = malloc(sizeof(double) * (size_t)d);
         for (int h = kvh * g; h < (kvh + 1) * g; ++h) {
             for (int i = 0; i < T; ++i) {
                 int n = causal ? i + 1 : T;
@@ -666,8 +687,26 @@ void oracle_attn_dense_backward(const uint16_t *q, const uint16_t *k, const uint
                 double D = 0.0;
                 for (int j = 0; j < n; ++j)
                     D += exp(s[j] - lse) * dp[j];
+                double E = 0.0;
+                if (eQ || eK) {
+                    for (int c = 0; c < d; ++c)
+                        oex[c] = pva[c] = 0.0;
+                    for (int j = 0; j < n; ++j) {
+                        double p = exp(s[j] - lse);
+                        const uint16_t *vr = v + (((int64_t)b * T + j) * Hkv + kvh) * d;
+                        for (int c = 0; c < d; ++c) {
+                            double vc = bf16_to_double(vr[c]);
+                            oex[c] += p * vc;
+                            pva[c] += p * fabs(vc);
+                        }
+                    }
+                    for (int c = 0; c < d; ++c)
+                        E += fabs(od[c]) * (fabs(oex[c]) + pva[c]);
+                    E *= ldexp(1.0, -9);
+                }
                 double *dq = dQ + (((int64_t)b * T + i) * Hq + h) * d;
                 double *aq = aQ ? aQ + (((int64_t)b * T + i) * Hq + h) * d : NULL;
+                double *eq = eQ ? eQ + (((int64_t)b * T + i) * Hq + h) * d : NULL;
                 for (int c = 0; c < d; ++c) {
                     dq[c] = 0.0;
                     if (aq)
@@ -689,6 +728,10 @@ void oracle_attn_dense_backward(const uint16_t *q, const uint16_t *k, const uint
                             aK[kvo + c] += scale * fabs(ds * qd[c]);
                         if (aV)
                             aV[kvo + c] += fabs(p * od[c]);
+                        if (eq)
+                            eq[c] += scale * E * p * fabs(kc);
+                        if (eK)
+                            eK[kvo + c] += scale * p * E * fabs(qd[c]);
                     }
                 }
             }
@@ -697,5 +740,7 @@ void oracle_attn_dense_backward(const uint16_t *q, const uint16_t *k, const uint
         free(dp);
         free(qd);
         free(od);
+        free(oex);
+        free(pva);
     }
 }

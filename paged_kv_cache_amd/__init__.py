@@ -68,6 +68,11 @@ def load():
                                   _I, _I, _P, _I, _P, _I, _I, _P, _P]
         lib.kv_release.restype = _I
         lib.kv_release.argtypes = [_P, _I, _P, _I, _I, _I, _P, _I, _P, _P, _P]
+        lib.attn_backward_dense.restype = _I
+        lib.attn_backward_dense.argtypes = [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P, _P,
+                                            _P, _P, _SZ, _P]
+        lib.attn_backward_workspace_size.restype = _SZ
+        lib.attn_backward_workspace_size.argtypes = [_I, _I, _I]
         lib.attn_prefill_dense.restype = _I
         lib.attn_prefill_dense.argtypes = [_P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P, _P, _P]
         _lib = lib
@@ -265,3 +270,28 @@ def kv_release(slots: torch.Tensor, block_table: torch.Tensor, free_pages: torch
 def new_alloc_state(top: int, device=None) -> torch.Tensor:
     """The int32 [2] allocator state for kv_append / kv_release: {top, 0}."""
     return torch.tensor([int(top), 0], dtype=torch.int32, device=device or torch.device("cuda"))
+
+
+def attn_backward_dense(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
+                        dout: torch.Tensor, lse: torch.Tensor, scale: float, causal: bool = True,
+                        dq: torch.Tensor | None = None, dk: torch.Tensor | None = None,
+                        dv: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                        stream=None):
+    """Gradients of exact attention on contiguous q [B, T, Hq, d], k, v [B, T, Hkv, d], given
+    the forward's o and lse [B, Hq, T] and the upstream gradient dout; returns (dq, dk, dv)."""
+    B, T, Hq, d = q.shape
+    Hkv = k.shape[2]
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    if workspace is None:
+        n = max(int(load().attn_backward_workspace_size(B, T, Hq)), 16)
+        workspace = torch.empty(n, dtype=torch.uint8, device=q.device)
+    rc = load().attn_backward_dense(
+        _dev(q, torch.bfloat16, "q"), _dev(k, torch.bfloat16, "k"), _dev(v, torch.bfloat16, "v"),
+        _dev(o, torch.bfloat16, "o"), _dev(dout, torch.bfloat16, "dout"), _dev(lse, torch.float32, "lse"),
+        B, T, Hq, Hkv, d, float(scale), int(bool(causal)), _dev(dq, torch.bfloat16, "dq"),
+        _dev(dk, torch.bfloat16, "dk"), _dev(dv, torch.bfloat16, "dv"), _dev(workspace, None, "workspace"),
+        workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(rc, "attn_backward_dense")
+    return dq, dk, dv

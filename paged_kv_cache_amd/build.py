@@ -20,7 +20,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libpagedattn.so")
-SOURCES = ["api.hip", "scatter.hip", "append.hip", "decode.hip", "prefill.hip"]
+SOURCES = ["api.hip", "scatter.hip", "append.hip", "decode.hip", "prefill.hip", "backward.hip"]
 ARCH = "gfx950"
 
 

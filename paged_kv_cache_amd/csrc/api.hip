@@ -197,4 +197,28 @@ int kv_release(const int32_t *slots, int n, int32_t *block_table, int n_slots, i
                                static_cast<hipStream_t>(stream));
 }
 
+size_t attn_backward_workspace_size(int B, int T, int Hq) {
+  if (B <= 0 || T <= 0 || Hq <= 0) return 0;
+  return pa::backward_workspace_bytes(B, T, Hq);
+}
+
+int attn_backward_dense(const void *q, const void *k, const void *v, const void *o,
+                        const void *dout, const float *lse, int B, int T, int Hq, int Hkv,
+                        int head_dim, float scale, int causal, void *dq, void *dk, void *dv,
+                        void *workspace, size_t workspace_bytes, void *stream) {
+  if (B < 0 || T < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0) return PA_ERR_SHAPE;
+  if (!supported_head_dim(head_dim)) return PA_ERR_UNSUPPORTED;
+  const int G = Hq / Hkv;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return PA_ERR_UNSUPPORTED;
+  if (B == 0 || T == 0) return PA_OK;
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !workspace) return PA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) ||
+      !aligned16(dq) || !aligned16(dk) || !aligned16(dv) || !aligned16(workspace) || !aligned16(lse))
+    return PA_ERR_ALIGN;
+  if ((int64_t)B * T * Hq > 0x7fffffffLL / 16) return PA_ERR_RANGE;
+  if (workspace_bytes < pa::backward_workspace_bytes(B, T, Hq)) return PA_ERR_WORKSPACE;
+  return pa::launch_backward_dense(q, k, v, o, dout, lse, B, T, Hq, Hkv, head_dim, scale, causal,
+                                   dq, dk, dv, workspace, static_cast<hipStream_t>(stream));
+}
+
 }  // extern "C"

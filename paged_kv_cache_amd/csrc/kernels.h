@@ -39,4 +39,11 @@ int launch_kv_release(const int32_t *slots, int n, int32_t *block_table, int n_s
                       int mbps, int32_t *free_pages, int capacity, int32_t *alloc_state,
                       int32_t *err, hipStream_t stream);
 
+size_t backward_workspace_bytes(int B, int T, int Hq);
+
+int launch_backward_dense(const void *q, const void *k, const void *v, const void *o,
+                          const void *dout, const float *lse, int B, int T, int Hq, int Hkv, int D,
+                          float scale, int causal, void *dq, void *dk, void *dv, void *workspace,
+                          hipStream_t stream);
+
 }  // namespace pa

@@ -23,7 +23,8 @@ def test_header_declares_the_path():
     names = declared_functions()
     for n in ["kv_scatter", "attn_prefill", "attn_decode", "attn_prefill_dense",
               "attn_decode_workspace_size", "pa_status_string", "pa_page_bytes", "kv_append",
-              "kv_release", "attn_prefill_chunk"]:
+              "kv_release", "attn_prefill_chunk", "attn_backward_dense",
+              "attn_backward_workspace_size"]:
         assert n in names
 
 

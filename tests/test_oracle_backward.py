@@ -72,7 +72,33 @@ def test_backward_key_gradients_sum_to_zero(oracle_lib, causal):
 
 def test_backward_abs_sums_bound_values(oracle_lib):
     case = W.make_dense("a", B=1, T=25, Hq=4, Hkv=1, d=64, causal=True, seed=5, grad=True)
-    dQ, dK, dV, aQ, aK, aV = oracle_lib.attn_dense_backward(case.q, case.k, case.v, case.dout,
-                                                            case.scale, True, with_abs=True)
+    dQ, dK, dV, aQ, aK, aV, eQ, eK = oracle_lib.attn_dense_backward(
+        case.q, case.k, case.v, case.dout, case.scale, True, with_abs=True)
     for x, a in ((dQ, aQ), (dK, aK), (dV, aV)):
         assert np.all(np.abs(x) <= a + 1e-12)
+    assert np.all(eQ >= 0) and np.all(eK >= 0) and eQ.max() > 0
+
+
+def test_backward_d_bound_covers_rounded_output(oracle_lib):
+    """eQ, eK bound the change of dQ, dK when D is taken from O rounded to bf16: checked
+    against a direct numpy evaluation with exactly that D."""
+    case = W.make_dense("e", B=1, T=17, Hq=2, Hkv=1, d=64, causal=True, seed=17, grad=True)
+    dQ, dK, _, _, _, _, eQ, eK = oracle_lib.attn_dense_backward(
+        case.q, case.k, case.v, case.dout, case.scale, True, with_abs=True)
+    q, k, v, do = (x.double().numpy()[0] for x in (case.q, case.k, case.v, case.dout))
+    sc = case.scale
+    gq = np.zeros_like(q)
+    gk = np.zeros_like(k)
+    for h in range(2):
+        for i in range(17):
+            s = sc * (k[:i + 1, 0] @ q[i, h])
+            p = np.exp(s - s.max())
+            p /= p.sum()
+            dp = v[:i + 1, 0] @ do[i, h]
+            o = torch.tensor(p @ v[:i + 1, 0], dtype=torch.float32).to(torch.bfloat16).double().numpy()
+            ds = p * (dp - (do[i, h] * o).sum())
+            gq[i, h] = sc * ds @ k[:i + 1, 0]
+            gk[:i + 1, 0] += sc * np.outer(ds, q[i, h])
+    assert np.all(np.abs(gq - dQ[0]) <= eQ[0] + 1e-12)
+    assert np.all(np.abs(gk - dK[0]) <= eK[0] + 1e-12)
+    assert np.abs(gq - dQ[0]).max() > 1e-4          # the effect is real at this size
