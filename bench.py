@@ -317,7 +317,7 @@ def kernels_only(n: int) -> None:
     print(f"kernels-only: {n} launches each", flush=True)
 
 
-SWEEP_PARTS = ("tiny", "dense", "long_prefill", "long_decode", "chunk", "append")
+SWEEP_PARTS = ("tiny", "dense", "long_prefill", "long_decode", "chunk", "append", "backward")
 
 
 def sweep(parts=SWEEP_PARTS) -> None:
@@ -326,7 +326,8 @@ def sweep(parts=SWEEP_PARTS) -> None:
     (MHA, d 64 / 128, T 512..16k, B*T = 16k, causal and full), the long dense
     prefill (B=1, T=16384, 16x128, causal), the long decode (4 x 16384), a
     prefix continuation and a mixed prefill + decode batch, the decode append
-    of the 64-sequence batch and a release of 8 of its slots.
+    of the 64-sequence batch, a release of 8 of its slots, and the backward
+    on the FA2 shapes.
     Kernel times are HIP-event averages over graph replays (kernel_time)."""
     rows = []
 
@@ -464,6 +465,30 @@ def sweep(parts=SWEEP_PARTS) -> None:
         emit("kv_release of 8 slots (1 layer x 128 blocks each)", us, n_rel / us, "pages/us",
              f"{n_rel} pages pushed; graph of restore+release minus graph of restore")
         del pool
+
+    if "backward" in parts:
+        # backward on the FA2 shapes: FLOPs = 2.5 x forward (the explainer's convention:
+        # 5 matrix products against 2); fwd+bwd = 3.5 x forward
+        for d, H in W.FA2_HEADS:
+            for T in W.FA2_SEQLENS:
+                for causal in (False, True):
+                    gc = W.fa2_dense(T, d, causal, grad=True)
+                    qd, kd, vd, dod = (x.to(DEV) for x in (gc.q, gc.k, gc.v, gc.dout))
+                    Od, Ld = pa.attn_prefill_dense(qd, kd, vd, gc.scale, causal)
+                    dq, dk, dv = torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd)
+                    B = 16384 // T
+                    ws = torch.empty(max(int(pa.load().attn_backward_workspace_size(B, T, H)), 16),
+                                     dtype=torch.uint8, device=DEV)
+                    tb = kernel_time(lambda: pa.attn_backward_dense(qd, kd, vd, Od, dod, Ld, gc.scale, causal,
+                                                                    dq=dq, dk=dk, dv=dv, workspace=ws),
+                                     reps=5, trials=3)
+                    tf = kernel_time(lambda: pa.attn_prefill_dense(qd, kd, vd, gc.scale, causal, out=Od, lse=Ld),
+                                     reps=5, trials=3)
+                    fwd = prefill_flops(B, T, H, d, causal)
+                    emit(f"backward d={d} H={H} T={T} B={B} {'causal' if causal else 'full'}", tb * 1e6,
+                         2.5 * fwd / tb / 1e12, "TFLOP/s",
+                         f"fwd+bwd {3.5 * fwd / (tf + tb) / 1e12:.1f} TFLOP/s")
+                    del qd, kd, vd, dod, Od, Ld, dq, dk, dv, ws
 
     print("\n| workload | time (us) | throughput | note |\n|---|---:|---:|---|")
     for name, us, metric, unit, extra in rows:
