@@ -221,9 +221,10 @@ int attn_prefill_dense(const void *q, const void *k, const void *v, int B, int T
  *   dq           [B][T][Hq][head_dim] bf16 output; dk, dv [B][T][Hkv][head_dim]
  *                bf16 outputs (every element written once: deterministic).
  *   workspace    attn_backward_workspace_size(B, T, Hq) bytes, 16-byte
- *                aligned (per-row D and LSE); contents on entry do not matter.
+ *                aligned (D of every row); contents on entry do not matter.
  *   causal, scale as for attn_prefill_dense.  Supported: head_dim 64 or 128,
- *   Hq/Hkv in {1, 2, 4, 8}.  Three launches on `stream`.
+ *   Hq/Hkv in {1, 2, 4, 8}.  Two launches on `stream` (dQ and the per-row D
+ *   first, then dK and dV).
  */
 int attn_backward_dense(const void *q, const void *k, const void *v, const void *o,
                         const void *dout, const float *lse, int B, int T, int Hq, int Hkv,

@@ -27,7 +27,8 @@
 // rounded to bf16 only as MFMA operands; in each kernel the lane layout of
 // the scores is already the B-operand layout of the next product, and the
 // transposed A operands (dO^T, Q^T, K^T) come from transposing LDS reads.
-// bwd_preprocess_kernel computes D_i and LSE_i * log2(e) once per row.
+// bwd_dq_kernel runs first and also computes D_i of its rows (it holds their
+// dO already) for bwd_dkdv_kernel.
 
 #include "device.h"
 #include "kernels.h"
@@ -41,8 +42,7 @@ constexpr int kBT = 64;   // rows (dK/dV kernel) or keys (dQ kernel) per staged 
 struct BwdArgs {
   const uint16_t *q, *k, *v, *o, *dout;   // [B][T][H][D] bf16
   const float *lse;                       // [B][Hq][T] natural log
-  float *dvec;                            // workspace [B][Hq][T]: D_i
-  float *lse2;                            // workspace [B][Hq][T]: LSE_i * log2(e)
+  float *dvec;                            // workspace [B][Hq][T]: D_i (written by bwd_dq_kernel)
   uint16_t *dq, *dk, *dv;
   int B, T, Hq, Hkv;
   float scale, scale_log2;
@@ -79,36 +79,6 @@ __device__ __forceinline__ bf16x8 tr_operand(const uint8_t *tile, const uint32_t
 }
 
 }  // namespace
-
-// ---- D_i = sum_c dO_ic O_ic and LSE_i * log2(e), one row per D/8 lanes
-template <int D>
-__global__ __launch_bounds__(256) void bwd_preprocess_kernel(BwdArgs a) {
-  constexpr int CH = D / 8;
-  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t row = gid / CH;                 // (b, t, h) in [B][T][Hq] order
-  const int c = (int)(gid % CH);
-  const int64_t n_rows = (int64_t)a.B * a.T * a.Hq;
-  const bool in = row < n_rows;
-  const int64_t rr = in ? row : 0;
-  const u32x4 ov = *reinterpret_cast<const u32x4 *>(a.o + rr * D + c * 8);
-  const u32x4 dv = *reinterpret_cast<const u32x4 *>(a.dout + rr * D + c * 8);
-  float s = 0.f;
-#pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    s += __uint_as_float(ov[w] << 16) * __uint_as_float(dv[w] << 16);
-    s += __uint_as_float(ov[w] & 0xffff0000u) * __uint_as_float(dv[w] & 0xffff0000u);
-  }
-#pragma unroll
-  for (int m = 1; m < CH; m <<= 1) s += __shfl_xor(s, m, 64);
-  if (in && c == 0) {
-    const int h = (int)(rr % a.Hq);
-    const int64_t bt = rr / a.Hq;
-    const int t = (int)(bt % a.T), b = (int)(bt / a.T);
-    const int64_t o = ((int64_t)b * a.Hq + h) * a.T + t;
-    a.dvec[o] = s;
-    a.lse2[o] = a.lse[o] * kLog2e;
-  }
-}
 
 // ---- dK, dV: one workgroup per (sequence, kv head, 128 keys)
 template <int D, int G>
@@ -205,7 +175,7 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdArgs 
     if (tid < kBT) {
       const int row = rt * kBT + tid;
       const int64_t o = ((int64_t)b * Hq + h) * T + (row < T ? row : 0);
-      pl = row < T ? a.lse2[o] : INFINITY;     // padding rows: P = 0
+      pl = row < T ? a.lse[o] * kLog2e : INFINITY;   // padding rows: P = 0
       pd = row < T ? a.dvec[o] : 0.f;
     }
   };
@@ -358,9 +328,29 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
       oreg[kk] = op[kk];
     }
   }
+  // D of the lane's row: its dO times the forward's O (each lane half holds
+  // half of the row), written for bwd_dkdv_kernel
   const int64_t so = ((int64_t)b * Hq + head) * T + rowc;
-  const float l2 = row < T ? a.lse2[so] : INFINITY;
-  const float dr = row < T ? a.dvec[so] : 0.f;
+  const float l2 = row < T ? a.lse[so] * kLog2e : INFINITY;
+  float dr;
+  {
+    const int64_t off = (((int64_t)b * T + rowc) * Hq + head) * D + lh * (D / 2);
+    const u32x4 *op = reinterpret_cast<const u32x4 *>(a.o + off);
+    float part = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+      const u32x4 ov = op[kk];
+      const u32x4 dv = __builtin_bit_cast(u32x4, oreg[kk]);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        part += __uint_as_float(ov[w] << 16) * __uint_as_float(dv[w] << 16);
+        part += __uint_as_float(ov[w] & 0xffff0000u) * __uint_as_float(dv[w] & 0xffff0000u);
+      }
+    }
+    dr = part + __shfl_xor(part, 32, 64);
+    if (row < T && lh == 0) a.dvec[so] = dr;
+    dr = row < T ? dr : 0.f;
+  }
 
   uint32_t raddr[CH / 2];
 #pragma unroll
@@ -483,20 +473,17 @@ template <int D, int G>
 int launch_bwd_t(const BwdArgs &a, hipStream_t stream) {
   constexpr int HW = G < 4 ? G : 4;
   constexpr int BM = 32 * (4 / HW);
-  const int64_t n_rows = (int64_t)a.B * a.T * a.Hq;
-  const int64_t pre_grid = (n_rows * (D / 8) + 255) / 256;
   const int64_t kv_grid = (int64_t)a.B * a.Hkv * ((a.T + 127) / 128);
   const int64_t q_grid = (int64_t)a.B * (a.Hq / HW) * ((a.T + BM - 1) / BM);
-  if (pre_grid > 0x7fffffff || kv_grid > 0x7fffffff || q_grid > 0x7fffffff) return PA_ERR_RANGE;
-  hipLaunchKernelGGL((bwd_preprocess_kernel<D>), dim3((unsigned)pre_grid), dim3(256), 0, stream, a);
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D, G>), dim3((unsigned)kv_grid), dim3(256), 0, stream, a);
+  if (kv_grid > 0x7fffffff || q_grid > 0x7fffffff) return PA_ERR_RANGE;
   hipLaunchKernelGGL((bwd_dq_kernel<D, G>), dim3((unsigned)q_grid), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, G>), dim3((unsigned)kv_grid), dim3(256), 0, stream, a);
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
 
 }  // namespace
 
-size_t backward_workspace_bytes(int B, int T, int Hq) { return 2 * (size_t)B * Hq * T * sizeof(float); }
+size_t backward_workspace_bytes(int B, int T, int Hq) { return (size_t)B * Hq * T * sizeof(float); }
 
 int launch_backward_dense(const void *q, const void *k, const void *v, const void *o,
                           const void *dout, const float *lse, int B, int T, int Hq, int Hkv, int D,
@@ -510,7 +497,6 @@ int launch_backward_dense(const void *q, const void *k, const void *v, const voi
   a.dout = static_cast<const uint16_t *>(dout);
   a.lse = lse;
   a.dvec = static_cast<float *>(workspace);
-  a.lse2 = a.dvec + (size_t)B * Hq * T;
   a.dq = static_cast<uint16_t *>(dq);
   a.dk = static_cast<uint16_t *>(dk);
   a.dv = static_cast<uint16_t *>(dv);
