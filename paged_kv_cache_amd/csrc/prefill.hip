@@ -9,8 +9,9 @@
 // pre-multiplied by scale*log2(e) (same values; v_exp_f32 is a base-2 unit).
 // m need not be the exact running max: any reference value works as long as
 // the exponentials neither overflow nor lose the row, so m is moved (and O, l
-// rescaled) only on a row's first tile or when some p of a tile would reach
-// 2^64; the others take p = 2^(s*c - m) against the old m, with no tile max.
+// rescaled) only on a row's first half tile or when some p of a half tile
+// would reach 2^64; the others take p = 2^(s*c - m) against the old m, with
+// no tile max.
 // Causal tiles wholly above the diagonal are never visited and the mask is
 // evaluated only on tiles that cross the diagonal or the sequence end
 // (explainer, "causal mask" paragraph).
@@ -21,9 +22,10 @@
 // query tile, all independent.  The wavefronts split the queries (split-Q):
 // with a group of four q heads the blocks are the four heads of the same 32
 // rows, so a K/V tile staged once in LDS serves 4 x 32 query rows; with
-// smaller groups they are more rows of fewer heads.  Each wavefront owns BPW
-// blocks (every operand it reads from LDS feeds BPW MFMAs).  No wavefront
-// ever reads another's results.
+// smaller groups they are more rows of fewer heads.  Each wavefront owns one
+// block and never reads another's results.  A tile is taken as two 32-key
+// halves one after the other, so that few registers are live: at d=64 the
+// kernel fits 128 registers and 4 workgroups share a CU.
 //
 // Tile products on gfx950 bf16 MFMA with fp32 accumulation, 32x32x16 shape:
 //   S^T[32 keys][32 rows] = K[32 keys][16 d] x Q^T[16 d][32 rows]
@@ -91,9 +93,9 @@ struct Swz {
   __device__ static int v(int key) { return 4 * ((key / (128 / D)) % (D / 32)); }
 };
 
-template <int D, int G, bool PAGED, int NS, int OCC, int BPW>
-__global__ __launch_bounds__(64 * (kBlocks / BPW), OCC) void prefill_kernel(PrefillArgs a) {
-  constexpr int NW = kBlocks / BPW;                // waves per workgroup
+template <int D, int G, bool PAGED, int NS, int OCC>
+__global__ __launch_bounds__(64 * kBlocks, OCC) void prefill_kernel(PrefillArgs a) {
+  constexpr int NW = kBlocks;                      // waves per workgroup, one block each
   constexpr int HW = G < kBlocks ? G : kBlocks;    // heads per workgroup
   constexpr int RW = kBlocks / HW;                 // 32-row blocks per workgroup
   constexpr int BM = 32 * RW;                      // query rows per workgroup
@@ -106,12 +108,14 @@ __global__ __launch_bounds__(64 * (kBlocks / BPW), OCC) void prefill_kernel(Pref
   constexpr int TPP = kPageTokens / KPI;           // transfers per page
   static_assert(PPW >= 1 && PPW * kPageTokens == NDMA * KPI, "each wave fetches whole pages of every key tile");
   static_assert(NS >= 2 && NS <= 4, "LDS ring depth");
-  // The running max m is only moved when some p = 2^(s*c - m) of a tile would
-  // reach 2^64 (or on a row's first tile): fp32 and bf16 hold such p exactly
-  // as well as p <= 1, and O, l stay far from overflow, so most tiles skip
-  // the tile max and the rescale altogether.
+  // The running max m is only moved when some p = 2^(s*c - m) of a half tile
+  // would reach 2^64: fp32 and bf16 hold such p exactly as well as p <= 1,
+  // and O, l stay far from overflow, so most tiles skip the tile max and the
+  // rescale altogether.  m starts at -1e30, so a row's first half tile with
+  // a visible key always moves it.
   constexpr float kSpecLimit = 0x1p64f;
   constexpr float kMaxFloor = -1e30f;              // finite start of the running max
+
 
   // Ring of NS stages, each a K tile and a V tile ([key][chunk], swizzled).
   // Tile u lives in stage u % NS; it is fetched NS-1 tiles ahead of use.
@@ -162,16 +166,10 @@ __global__ __launch_bounds__(64 * (kBlocks / BPW), OCC) void prefill_kernel(Pref
   const int Hq = a.Hkv * G;
   const int kvh = (hg * HW) / G;
   const int T = a.T;
-  // this wave's column blocks: block j = wave*BPW + i is head hg*HW + j%HW,
-  // rows rb*BM + 32*(j/HW) .. +31
-  int head[BPW], row0[BPW];
-#pragma unroll
-  for (int i = 0; i < BPW; ++i) {
-    const int j = wave * BPW + i;
-    head[i] = hg * HW + j % HW;
-    row0[i] = rb * BM + 32 * (j / HW);
-  }
-  const int wave_row_end = row0[BPW - 1] + 31;   // last row of this wave
+  // this wave's column block: head hg*HW + wave%HW, rows row0 .. row0+31
+  const int head = hg * HW + wave % HW;
+  const int row0 = rb * BM + 32 * (wave / HW);
+  const int wave_row_end = row0 + 31;
 
   int len = T;    // keys of this sequence (its cached tokens)
   int qlen = T;   // its query rows: the last qlen of its len tokens
@@ -220,49 +218,39 @@ __global__ __launch_bounds__(64 * (kBlocks / BPW), OCC) void prefill_kernel(Pref
     // every row of this workgroup is padding (rows past the query length of a
     // short sequence in a padded batch): O = 0, LSE = -inf, nothing else
     if (err_bits && tid == 0) raise_err(a.err, err_bits);
+    const int row = row0 + lr;
+    if (row < T) {
+      uint16_t *op = a.O + (((int64_t)b * T + row) * Hq + head) * D;
 #pragma unroll
-    for (int i = 0; i < BPW; ++i) {
-      const int row = row0[i] + lr;
-      if (row < T) {
-        uint16_t *op = a.O + (((int64_t)b * T + row) * Hq + head[i]) * D;
+      for (int mb = 0; mb < D / 32; ++mb)
 #pragma unroll
-        for (int mb = 0; mb < D / 32; ++mb)
-#pragma unroll
-          for (int g = 0; g < 4; ++g)
-            *reinterpret_cast<uint2 *>(op + mb * 32 + 8 * g + 4 * lh) = make_uint2(0u, 0u);
-        if (lh == 0) a.LSE[((int64_t)b * Hq + head[i]) * T + row] = -INFINITY;
-      }
+        for (int g = 0; g < 4; ++g)
+          *reinterpret_cast<uint2 *>(op + mb * 32 + 8 * g + 4 * lh) = make_uint2(0u, 0u);
+      if (lh == 0) a.LSE[((int64_t)b * Hq + head) * T + row] = -INFINITY;
     }
     return;
   }
   const int nblk = (kv_end + kPageTokens - 1) / kPageTokens;   // blocks read (paged)
-  // last key each of this lane's rows may see (-1: padding row, sees nothing)
-  int lim[BPW];
-#pragma unroll
-  for (int i = 0; i < BPW; ++i) {
-    const int row = row0[i] + lr;
-    lim[i] = row < qlen ? (a.causal ? off + row : len - 1) : -1;
-  }
+  // last key this lane's row may see (-1: padding row, sees nothing)
+  const int row = row0 + lr;
+  const int lim = row < qlen ? (a.causal ? off + row : len - 1) : -1;
 
-  // ---- Q^T as B operands: lane holds row row0[i] + lr, d = lh*(D/2) + k*8 + e
+  // ---- Q^T as B operands: lane holds row row0 + lr, d = lh*(D/2) + k*8 + e
   // A padding row (row >= qlen) takes the sequence's row 0 instead: its
   // results are never written (O = 0, LSE = -inf), and a real row keeps its
   // scores finite.  (Unconditional loads: no wait between them.)
-  bf16x8 qf[BPW][D / 16];
-#pragma unroll
-  for (int i = 0; i < BPW; ++i) {
-    const int row = row0[i] + lr;
+  bf16x8 qf[D / 16];
+  {
     const bf16x8 *qp = reinterpret_cast<const bf16x8 *>(
-        a.q + (((int64_t)b * T + (row < qlen ? row : 0)) * Hq + head[i]) * D + lh * (D / 2));
+        a.q + (((int64_t)b * T + (row < qlen ? row : 0)) * Hq + head) * D + lh * (D / 2));
 #pragma unroll
-    for (int k = 0; k < D / 16; ++k) qf[i][k] = qp[k];
+    for (int k = 0; k < D / 16; ++k) qf[k] = qp[k];
   }
 
   // ---- pages: validated once for the whole workgroup.  A key that must not
   // count (past kv_end, or on a missing page) is fetched from a safe token
   // instead (token 0 of the first valid block, or of pool page 0 if there is
-  // none) so that every tile moves the same bytes and its V rows stay finite;
-  // its score is masked.
+  // none) so that its V row stays finite; its score is masked.
   bool any_bad = false;
   int64_t safe_page = 0;
   int32_t raw0[PPW];   // first window of this wave's pages, read with the pass below
@@ -325,7 +313,9 @@ __global__ __launch_bounds__(64 * (kBlocks / BPW), OCC) void prefill_kernel(Pref
   // u holds the offset of its page of tile 64*win + u (the safe page's when
   // the page is missing or past the end); bit u of good_m / clean_m: the page
   // exists / every key on it counts.  One vector read of the block table per
-  // 64 tiles; a tile then costs two lane reads.
+  // 64 tiles; a tile then costs two lane reads.  V tiles are fetched one
+  // tile behind K tiles and before them in a step, so the window only moves
+  // forward.
   uint32_t off_lo[PPW], off_hi[PPW];
   uint64_t good_m[PPW], clean_m[PPW];
   int win = -1;
@@ -359,6 +349,8 @@ __global__ __launch_bounds__(64 * (kBlocks / BPW), OCC) void prefill_kernel(Pref
   };
   const uint8_t *safe_base = a.pool + safe_page * page_bytes;
 
+  // ---- fetch the K (IS_V = false) or V tile u into the stage at dst: NDMA
+  // transfers per wave
   // ---- fetch tile u into stage S: 2*NDMA transfers per wave, always
   auto fetch = [&](int u, auto S_) {
     uint8_t *kdst = kbuf(S_) + wave * NDMA * 1024;
@@ -436,53 +428,28 @@ __global__ __launch_bounds__(64 * (kBlocks / BPW), OCC) void prefill_kernel(Pref
     vaddr[mb] = key * ROWB + (uint32_t)((((dcol / 8) ^ Swz<D>::v(key)) * 16) + (dcol % 8) * 2);
   }
 
-  f32x16 acc[BPW][D / 32];
+  f32x16 acc[D / 32];
 #pragma unroll
-  for (int i = 0; i < BPW; ++i)
+  for (int mb = 0; mb < D / 32; ++mb)
 #pragma unroll
-    for (int mb = 0; mb < D / 32; ++mb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][mb][r] = 0.f;
-  float m_run[BPW], l_lane[BPW];   // reference max of the row (log2 units); this lane's half of l
-#pragma unroll
-  for (int i = 0; i < BPW; ++i) {
-    m_run[i] = kMaxFloor;
-    l_lane[i] = 0.f;
-  }
-  bool started = false;            // some tile processed (wave-uniform)
+    for (int r = 0; r < 16; ++r) acc[mb][r] = 0.f;
+  float m_run = kMaxFloor;   // reference max of the row (log2 units)
+  float l_lane = 0.f;        // this lane's half of l
   // first tile whose scores need the mask: the first tile holding a key past
   // the position of the block's first row (off + row0), or the tile that
   // crosses kv_end
-  int t_mask[BPW];
-#pragma unroll
-  for (int i = 0; i < BPW; ++i)
-    t_mask[i] = min(a.causal ? (off + row0[i] + 1) / kBN : 0x7fffffff, kv_end / kBN);
+  const int t_mask = min(a.causal ? (off + row0 + 1) / kBN : 0x7fffffff, kv_end / kBN);
   const float c = a.scale_log2;
 
-  // ---- one key tile: S = K Q^T, online softmax, O^T += V^T P^T.  Every
-  // operand read from LDS feeds the MFMAs of all BPW column blocks.
+
+  // ---- one key tile: S = K Q^T, online softmax, O^T += V^T P^T, as two
+  // 32-key halves one after the other (each an online-softmax step), so that
+  // only one half's scores and operands are live at a time.  The lane holds
+  // keys kv0 + 32h + 8*(r/4) + 4*lh + r%4 of its row in s[r].
   auto compute = [&](int t, auto S_) {
     const uint8_t *kt = kbuf(S_);
     const uint8_t *vt = vbuf(S_);
-    const int kv0 = t * kBN;
-
-    f32x16 s[BPW][2];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-#pragma unroll
-      for (int i = 0; i < BPW; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s[i][h][r] = 0.f;
-#pragma unroll
-      for (int k = 0; k < CH / 2; ++k) {
-        const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(kt + kaddr[k] + h * 32 * ROWB);
-#pragma unroll
-        for (int i = 0; i < BPW; ++i) s[i][h] = mfma32(kf, qf[i][k], s[i][h]);
-      }
-    }
-
-    // mask: only tiles that cross a diagonal, kv_end or a missing page.  The
-    // lane holds keys kv0 + h*32 + 8*(r/4) + 4*lh + r%4.
+    // mask: only tiles that cross a diagonal, kv_end or a missing page
     uint32_t bad_pages = 0;
     if constexpr (PAGED) {
       if (any_bad) {
@@ -493,68 +460,36 @@ __global__ __launch_bounds__(64 * (kBlocks / BPW), OCC) void prefill_kernel(Pref
         }
       }
     }
-#pragma unroll
-    for (int i = 0; i < BPW; ++i) {
-      const bool need_mask = (t >= t_mask[i]) | (bad_pages != 0);
-      if (need_mask) {
-        const int rel = lim[i] - (kv0 + 4 * lh);      // visible iff key offset <= rel
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int off = h * 32 + 8 * (r / 4) + (r % 4);
-            s[i][h][r] = off <= rel ? s[i][h][r] : -INFINITY;
-          }
-        if (bad_pages) {
-#pragma unroll
-          for (int h = 0; h < 2; ++h)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int pidx = (h * 32 + 8 * (r / 4) + 4 * lh) / kPageTokens;
-              s[i][h][r] = ((bad_pages >> pidx) & 1u) ? -INFINITY : s[i][h][r];
-            }
-        }
-      }
-    }
-
-    // The two 32-key halves of the tile are two online-softmax steps.  The PV
-    // products of a half are issued as soon as its P is ready, so they run
-    // while the exponentials of the next half are computed.
-    // P = 2^(s*c - m) (bf16) of half h, the B operands of its PV products:
-    // pb[i][q] covers keys 32h + 16q .. +15.
-    bf16x8 pb[BPW][2];
-    float psum[BPW];
-    auto exps = [&](int i, int h) {
-      float sum = 0.f;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = fast_exp2(__builtin_fmaf(s[i][h][r], c, -m_run[i]));
-        sum += p;
-        pb[i][r / 8][r % 8] = (__bf16)p;
-      }
-      psum[i] = sum;
-    };
-    // move the running max to the half's max (row max of the raw scores;
-    // scale >= 0 keeps the order) and rescale what is accumulated
-    auto remax = [&](int i, int h) {
-      float rmax = -INFINITY;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) rmax = fmaxf(rmax, s[i][h][r]);
-      auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(rmax), __float_as_uint(rmax), false, false);
-      rmax = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-      const float m_new = fmaxf(m_run[i], rmax * c);
-      const float corr = fast_exp2(m_run[i] - m_new);
-      m_run[i] = m_new;
-      l_lane[i] *= corr;
-#pragma unroll
-      for (int mb = 0; mb < D / 32; ++mb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[i][mb][r] *= corr;
-    };
+    const bool need_mask = (t >= t_mask) | (bad_pages != 0);
+    const int rel = lim - (t * kBN + 4 * lh);   // key offset o is visible iff o <= rel
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      // V^T operands of this half, read before the exponentials so that their
-      // LDS latency is hidden behind them
+      // S^T = K Q^T of the half (CH/2 MFMAs, K from LDS)
+      bf16x8 kf[CH / 2];
+#pragma unroll
+      for (int k = 0; k < CH / 2; ++k) kf[k] = *reinterpret_cast<const bf16x8 *>(kt + kaddr[k] + h * 32 * ROWB);
+      f32x16 s;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[r] = 0.f;
+#pragma unroll
+      for (int k = 0; k < CH / 2; ++k) s = mfma32(kf[k], qf[k], s);
+      if (need_mask) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int o = h * 32 + 8 * (r / 4) + (r % 4);
+          s[r] = o <= rel ? s[r] : -INFINITY;
+        }
+        if (bad_pages) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int pidx = (h * 32 + 8 * (r / 4) + 4 * lh) / kPageTokens;
+            s[r] = ((bad_pages >> pidx) & 1u) ? -INFINITY : s[r];
+          }
+        }
+      }
+      // V^T operands of the half, read before the exponentials so that their
+      // LDS latency is hidden behind them: vop[mb][q] covers keys
+      // 32h + 16q .. +15 and columns 32mb .. +31
       bf16x8 vop[D / 32][2];
 #pragma unroll
       for (int mb = 0; mb < D / 32; ++mb)
@@ -569,27 +504,46 @@ __global__ __launch_bounds__(64 * (kBlocks / BPW), OCC) void prefill_kernel(Pref
           }
           vop[mb][q] = __builtin_bit_cast(bf16x8, u32x4{part[0].x, part[0].y, part[1].x, part[1].y});
         }
+      // P = 2^(s*c - m) (bf16), the B operands of the PV products: pb[q]
+      // covers keys 32h + 16q .. +15; the row sum takes the fp32 p
+      bf16x8 pb[2];
+      auto exps = [&]() -> float {
+        float sum = 0.f;
 #pragma unroll
-      for (int i = 0; i < BPW; ++i) {
-        if (!started) {
-          remax(i, h);
-          exps(i, h);
-        } else {
-          exps(i, h);
-          if (__any(!(psum[i] < kSpecLimit))) {   // some p would be too large: redo with the half's max
-            remax(i, h);
-            exps(i, h);
-          }
+        for (int r = 0; r < 16; ++r) {
+          const float p = fast_exp2(__builtin_fmaf(s[r], c, -m_run));
+          sum += p;
+          pb[r / 8][r % 8] = (__bf16)p;
         }
-        l_lane[i] += psum[i];
+        return sum;
+      };
+      float ps = exps();
+      if (__any(!(ps < kSpecLimit))) {
+        // some p would be too large (or this is the row's first visible
+        // half): move the running max to the half's max (row max of the raw
+        // scores; scale >= 0 keeps the order), rescale what is accumulated,
+        // and redo the exponentials
+        float rmax = -INFINITY;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) rmax = fmaxf(rmax, s[r]);
+        auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(rmax), __float_as_uint(rmax), false, false);
+        rmax = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+        const float m_new = fmaxf(m_run, rmax * c);
+        const float corr = fast_exp2(m_run - m_new);
+        m_run = m_new;
+        l_lane *= corr;
+#pragma unroll
+        for (int mb = 0; mb < D / 32; ++mb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[mb][r] *= corr;
+        ps = exps();
       }
-      started = true;
+      l_lane += ps;
+      // O^T += V^T P^T
 #pragma unroll
-      for (int mb = 0; mb < D / 32; ++mb)
+      for (int q = 0; q < 2; ++q)
 #pragma unroll
-        for (int q = 0; q < 2; ++q)
-#pragma unroll
-          for (int i = 0; i < BPW; ++i) acc[i][mb] = mfma32(vop[mb][q], pb[i][q], acc[i][mb]);
+        for (int mb = 0; mb < D / 32; ++mb) acc[mb] = mfma32(vop[mb][q], pb[q], acc[mb]);
     }
   };
 
@@ -616,9 +570,7 @@ __global__ __launch_bounds__(64 * (kBlocks / BPW), OCC) void prefill_kernel(Pref
   // empty asm that takes the Q registers forces the wait; the Q loads and the
   // block-table reads above are in flight together until here.)
 #pragma unroll
-  for (int i = 0; i < BPW; ++i)
-#pragma unroll
-    for (int k = 0; k < D / 16; ++k) asm("" : "+v"(qf[i][k]));
+  for (int k = 0; k < D / 16; ++k) asm("" : "+v"(qf[k]));
   if (n_tiles > 0) {
     if constexpr (PAGED) window_set(0, raw0);
     fetch(0, std::integral_constant<int, 0>{});
@@ -645,48 +597,36 @@ __global__ __launch_bounds__(64 * (kBlocks / BPW), OCC) void prefill_kernel(Pref
   if (err_bits && tid == 0) raise_err(a.err, err_bits);
 
   // ---- epilogue: one divide per row, LSE in natural-log units
-#pragma unroll
-  for (int i = 0; i < BPW; ++i) {
-    const int row = row0[i] + lr;
-    auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_lane[i]), __float_as_uint(l_lane[i]), false, false);
+  {
+    auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_lane), __float_as_uint(l_lane), false, false);
     const float l_row = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
     const bool has = row < qlen && l_row > 0.f;
     const float inv_l = has ? 1.f / l_row : 0.f;
     if (row < T) {
-      uint16_t *op = a.O + (((int64_t)b * T + row) * Hq + head[i]) * D;
+      uint16_t *op = a.O + (((int64_t)b * T + row) * Hq + head) * D;
 #pragma unroll
       for (int mb = 0; mb < D / 32; ++mb)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           uint2 w;
-          w.x = has ? pack_bf16x2(acc[i][mb][4 * g + 0] * inv_l, acc[i][mb][4 * g + 1] * inv_l) : 0u;
-          w.y = has ? pack_bf16x2(acc[i][mb][4 * g + 2] * inv_l, acc[i][mb][4 * g + 3] * inv_l) : 0u;
+          w.x = has ? pack_bf16x2(acc[mb][4 * g + 0] * inv_l, acc[mb][4 * g + 1] * inv_l) : 0u;
+          w.y = has ? pack_bf16x2(acc[mb][4 * g + 2] * inv_l, acc[mb][4 * g + 3] * inv_l) : 0u;
           *reinterpret_cast<uint2 *>(op + mb * 32 + 8 * g + 4 * lh) = w;
         }
       if (lh == 0)
-        a.LSE[((int64_t)b * Hq + head[i]) * T + row] = has ? (m_run[i] + fast_log2(l_row)) * kLn2 : -INFINITY;
+        a.LSE[((int64_t)b * Hq + head) * T + row] = has ? (m_run + fast_log2(l_row)) * kLn2 : -INFINITY;
     }
   }
 }
 
-#ifndef PA_PREFILL_NS64
-#define PA_PREFILL_NS64 3
-#endif
-#ifndef PA_PREFILL_OCC64
-#define PA_PREFILL_OCC64 3
-#endif
-// Per head size: 32-column blocks per wave (two: every K/V operand read from
-// LDS feeds two MFMAs, at 2 waves per SIMD; one: 3 waves per SIMD, measured
-// faster for d=64), ring depth, and target waves per SIMD.  d=128 keeps one
-// block and a 2-deep ring (64 KB of LDS, 2 workgroups per CU).
-#ifndef PA_PREFILL_BPW64
-#define PA_PREFILL_BPW64 1
-#endif
+
+// Per head size: LDS ring depth and target workgroups per CU.  d=64 takes a
+// 2-stage ring (32 KB of LDS) and fits 128 registers, so that 4 workgroups
+// share a CU; d=128 keeps a 2-stage ring (64 KB) at 2 workgroups per CU.
 template <int D>
 struct PrefillCfg {
-  static constexpr int BPW = D == 64 ? PA_PREFILL_BPW64 : 1;
-  static constexpr int NS = D == 64 ? PA_PREFILL_NS64 : 2;
-  static constexpr int OCC = D == 64 ? PA_PREFILL_OCC64 : 2;
+  static constexpr int NS = 2;
+  static constexpr int OCC = D == 64 ? 4 : 2;
 };
 
 template <int D, int G, bool PAGED>
@@ -701,8 +641,8 @@ static int launch_prefill_t(PrefillArgs a, hipStream_t stream) {
   const int64_t grid = (int64_t)a.B * a.n_hgroups * a.n_rowblocks;
   if (grid == 0) return PA_OK;
   if (grid > 0x7fffffff) return PA_ERR_RANGE;
-  hipLaunchKernelGGL((prefill_kernel<D, G, PAGED, C::NS, C::OCC, C::BPW>), dim3((unsigned)grid),
-                     dim3(64 * (kBlocks / C::BPW)), 0, stream, a);
+  hipLaunchKernelGGL((prefill_kernel<D, G, PAGED, C::NS, C::OCC>), dim3((unsigned)grid), dim3(64 * kBlocks), 0,
+                     stream, a);
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
 
