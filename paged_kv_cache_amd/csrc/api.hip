@@ -7,6 +7,23 @@
 #include "kernels.h"
 #include "pagedattn.h"
 
+namespace pa {
+
+int device_cu_count() {
+  static int count[64];   // per device; written once with the same value by any thread
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (count[dev] <= 0) {
+    hipDeviceProp_t prop;
+    count[dev] = (hipGetDeviceProperties(&prop, dev) == hipSuccess && prop.multiProcessorCount > 0)
+                     ? prop.multiProcessorCount
+                     : 256;
+  }
+  return count[dev];
+}
+
+}  // namespace pa
+
 namespace {
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }

@@ -41,6 +41,10 @@ int launch_kv_release(const int32_t *slots, int n, int32_t *block_table, int n_s
 
 size_t backward_workspace_bytes(int B, int T, int Hq);
 
+// Compute units of the current device (queried once per device; 256 if the
+// query fails).  Launchers use it to lay workgroups out in layers of one per CU.
+int device_cu_count();
+
 int launch_backward_dense(const void *q, const void *k, const void *v, const void *o,
                           const void *dout, const float *lse, int B, int T, int Hq, int Hkv, int D,
                           float scale, int causal, void *dq, void *dk, void *dv, void *workspace,

@@ -74,6 +74,7 @@ struct PrefillArgs {
   int causal;
   int n_hgroups;               // head groups per sequence
   int n_rowblocks;             // query tiles per sequence
+  int layer_ranks;             // query-tile ranks per layer of one workgroup per CU
   uint16_t *O;                 // [B][T][Hq][D]
   float *LSE;                  // [B][Hq][T]
   int32_t *err;
@@ -159,6 +160,15 @@ __global__ __launch_bounds__(64 * kBlocks, OCC) void prefill_kernel(PrefillArgs 
   } else {
     rank = wg / n_pairs;
     pair = wg % n_pairs;
+  }
+  if (a.causal && a.layer_ranks > 1) {
+    // Workgroups are dispatched in id order, one per CU at a time, so the
+    // ids fill the CUs in layers.  Causal tiles are taken longest first,
+    // snaking over the layers (odd layers in reverse), so that the tiles
+    // sharing a CU add up to about the same number of key tiles.
+    const int L = a.layer_ranks;
+    const int layer = rank / L, pos = rank % L;
+    if (layer & 1) rank = layer * L + (min(L, a.n_rowblocks - layer * L) - 1 - pos);
   }
   const int rb = a.causal ? a.n_rowblocks - 1 - rank : rank;
   const int b = pair / a.n_hgroups;
@@ -638,6 +648,8 @@ static int launch_prefill_t(PrefillArgs a, hipStream_t stream) {
   const int Hq = a.Hkv * G;
   a.n_hgroups = Hq / HW;
   a.n_rowblocks = (a.T + BM - 1) / BM;
+  const int64_t n_pairs = (int64_t)a.B * a.n_hgroups;
+  a.layer_ranks = n_pairs > 0 ? (int)(device_cu_count() / n_pairs) : 0;
   const int64_t grid = (int64_t)a.B * a.n_hgroups * a.n_rowblocks;
   if (grid == 0) return PA_OK;
   if (grid > 0x7fffffff) return PA_ERR_RANGE;
