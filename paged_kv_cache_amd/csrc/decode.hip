@@ -150,15 +150,30 @@ __global__ __launch_bounds__(64 * kWaves, PA_DECODE_MIN_WAVES_PER_SIMD) void dec
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lrow = lane & 15;        // MFMA row/column lane index
   const int lgrp = lane >> 4;        // MFMA k-group / output row group
-  // ---- workgroup -> (sequence, kv head, split).  Sequences are taken
-  // longest context first (the r-th workgroup row gets the r-th longest
-  // sequence, ties by index): workgroups are launched in id order into free
-  // slots, so this schedules the longest work first and the CUs finish
-  // together.  Batches above kSortMax keep the identity order.
-  const int xs = blockIdx.x % a.n_xsplits;
-  const int rest = blockIdx.x / a.n_xsplits;
-  const int kvh = rest % a.Hkv;
-  int b = rest / a.Hkv;
+  // ---- workgroup -> (sequence rank, kv head, split).  Sequences are taken
+  // longest context first (rank r is the r-th longest sequence, ties by
+  // index): workgroups are launched in id order into free slots, so this
+  // schedules the longest work first and the CUs finish together.  Batches
+  // above kSortMax keep the identity order.
+  int xs, kvh, b;
+  {
+    const int per = a.Hkv * a.n_xsplits;   // workgroups of one sequence
+    const int w = blockIdx.x;
+    if ((a.B & 7) == 0) {
+      // consecutive ids go to the 8 XCDs in turn: keep all the workgroups of
+      // a sequence on one XCD (its pages are then read whole, every kv head
+      // at about the same time, by that XCD)
+      const int j = w >> 3;
+      b = (j / per) * 8 + (w & 7);
+      const int within = j % per;
+      kvh = within / a.n_xsplits;
+      xs = within % a.n_xsplits;
+    } else {
+      xs = w % a.n_xsplits;
+      kvh = (w / a.n_xsplits) % a.Hkv;
+      b = w / per;
+    }
+  }
   if (a.B <= kSortMax) {
     __shared__ int lens_s[kSortMax];
     __shared__ int sorted_b;
