@@ -481,8 +481,12 @@ __global__ __launch_bounds__(64 * kBlocks, OCC) void prefill_kernel(PrefillArgs 
       f32x16 s;
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[r] = 0.f;
+      // the matrix phases of a wave run at raised priority: a wave about to
+      // feed the MFMA unit issues ahead of the waves in their vector phase
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int k = 0; k < CH / 2; ++k) s = mfma32(kf[k], qf[k], s);
+      __builtin_amdgcn_s_setprio(0);
       if (need_mask) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
@@ -550,10 +554,12 @@ __global__ __launch_bounds__(64 * kBlocks, OCC) void prefill_kernel(PrefillArgs 
       }
       l_lane += ps;
       // O^T += V^T P^T
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int q = 0; q < 2; ++q)
 #pragma unroll
         for (int mb = 0; mb < D / 32; ++mb) acc[mb] = mfma32(vop[mb][q], pb[q], acc[mb]);
+      __builtin_amdgcn_s_setprio(0);
     }
   };
 
