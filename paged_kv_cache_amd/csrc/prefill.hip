@@ -323,9 +323,8 @@ __global__ __launch_bounds__(64 * kBlocks, OCC) void prefill_kernel(PrefillArgs 
   // u holds the offset of its page of tile 64*win + u (the safe page's when
   // the page is missing or past the end); bit u of good_m / clean_m: the page
   // exists / every key on it counts.  One vector read of the block table per
-  // 64 tiles; a tile then costs two lane reads.  V tiles are fetched one
-  // tile behind K tiles and before them in a step, so the window only moves
-  // forward.
+  // 64 tiles; a tile then costs two lane reads.  Tiles are fetched in order,
+  // so the window only moves forward.
   uint32_t off_lo[PPW], off_hi[PPW];
   uint64_t good_m[PPW], clean_m[PPW];
   int win = -1;
@@ -359,9 +358,7 @@ __global__ __launch_bounds__(64 * kBlocks, OCC) void prefill_kernel(PrefillArgs 
   };
   const uint8_t *safe_base = a.pool + safe_page * page_bytes;
 
-  // ---- fetch the K (IS_V = false) or V tile u into the stage at dst: NDMA
-  // transfers per wave
-  // ---- fetch tile u into stage S: 2*NDMA transfers per wave, always
+  // ---- fetch tile u (K and V) into stage S: 2*NDMA transfers per wave, always
   auto fetch = [&](int u, auto S_) {
     uint8_t *kdst = kbuf(S_) + wave * NDMA * 1024;
     uint8_t *vdst = vbuf(S_) + wave * NDMA * 1024;
