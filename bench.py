@@ -89,6 +89,26 @@ def kernel_time(fn, reps: int = 20, trials: int = 5) -> float:
     return s.elapsed_time(e) / 1e3 / (reps * trials)
 
 
+def launch_spread(fns, n: int = 50, warmup: int = 10) -> dict:
+    """Median, p10 and p90 (us) of single launches, each between two HIP
+    events on the launching stream, after `warmup` untimed ones; launch i runs
+    fns[i % len(fns)].  A single-launch time also holds the gap between the
+    event and the kernel (about a microsecond), which the graph averages of
+    kernel_time do not."""
+    for i in range(warmup):
+        fns[i % len(fns)]()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for i, (s, e) in enumerate(ev):
+        s.record()
+        fns[i % len(fns)]()
+        e.record()
+    torch.cuda.synchronize()
+    t = np.array([s.elapsed_time(e) * 1e3 for s, e in ev])
+    return {"n": n, "median_us": round(float(np.median(t)), 2),
+            "p10_us": round(float(np.percentile(t, 10)), 2), "p90_us": round(float(np.percentile(t, 90)), 2)}
+
+
 def timed_steps(step_fns, steps: int, warmup: int, per_graph: int = 8) -> float:
     """Wall time (s) of exactly `steps` steps after `warmup`, bracketed by device
     syncs.  Step i runs step_fns[i % n]; the steps are replayed from HIP graphs
@@ -178,7 +198,7 @@ def bench_prefill(steps: int, warmup: int):
     flops = prefill_flops(case.B, case.T, case.Hq, case.d, True)
     alg_bytes = (q.numel() + O.numel()) * 2 + L.numel() * 4 + 2 * k.numel() * 2
     return dict(case=case, wall=wall, flops=flops, t_kernel=kernel_time(prefill),
-                t_scatter=kernel_time(scatter), alg_bytes=alg_bytes)
+                t_scatter=kernel_time(scatter), alg_bytes=alg_bytes, spread=launch_spread([prefill]))
 
 
 # ------------------------------------------------------------------ decode
@@ -237,8 +257,11 @@ def bench_decode(steps: int, warmup: int, replicas: int = 8):
     io_bytes = q.numel() * 2 + O.numel() * 2 + L.numel() * 4 + int(np.ceil(case.ctx_lens / 16).sum()) * 4
     # one launch per replica in turn: the KV of a launch is never the previous one's
     t_kernel = kernel_time(lambda: [decode(r) for r in range(replicas)], reps=4) / replicas
+    # whole pages touched: ceil(ctx/16) pages of 16 tokens x all kv heads x (K, V)
+    page_bytes = int(np.ceil(case.ctx_lens / 16).sum()) * 16 * c.n_kv_heads * case.d * 2 * 2
+    spread = launch_spread([lambda r=r: decode(r) for r in range(replicas)])
     return dict(case=case, wall=wall, kv_bytes=kv_bytes, io_bytes=io_bytes, t_kernel=t_kernel,
-                replicas=replicas, n_ctx=n_ctx)
+                replicas=replicas, n_ctx=n_ctx, page_bytes=page_bytes, spread=spread)
 
 
 # -------------------------------------------------------------- CPU oracle
@@ -561,7 +584,7 @@ def main() -> int:
                      "frac": round(kern_tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic_of("prefill", prefill_digest),
                      "avg_us": round(p["t_kernel"] * 1e6, 3), "alg_bytes": p["alg_bytes"],
-                     "source_digest": prefill_digest},
+                     "single_launch": p["spread"], "source_digest": prefill_digest},
         "scatter_us": round(p["t_scatter"] * 1e6, 3),
         "decode": {
             "metric": "decode KV-read GB/s", "unit": "GB/s",
@@ -576,7 +599,9 @@ def main() -> int:
                          "frac": round(d_kern / PEAK_HBM_GBS, 4),
                          "traffic": traffic_of("decode", decode_digest),
                          "avg_us": round(d["t_kernel"] * 1e6, 3), "alg_bytes": d_alg,
-                         "source_digest": decode_digest},
+                         "page_granular_bytes": d["page_bytes"],
+                         "page_granular_GBs": round(d["page_bytes"] / d["t_kernel"] / 1e9, 2),
+                         "single_launch": d["spread"], "source_digest": decode_digest},
         },
     }
     if not args.no_cpu:
