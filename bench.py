@@ -149,8 +149,8 @@ def source_digest(*names: str) -> str:
 # was taken on (digest of the .hip files), null otherwise.
 TRAFFIC = {
     # kernel: (source digest, fetched bytes, written bytes)
-    "prefill": ("d3d793fe964a7223", 25382733, 17301504),
-    "decode": ("a9e1890abff7b6e1", 152900377, 272928),
+    "prefill": ("dbc6d761975fe88e", 25385933, 17301504),
+    "decode": ("7c0357daf7ffba2e", 152911640, 273088),
 }
 
 

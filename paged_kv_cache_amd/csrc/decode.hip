@@ -180,15 +180,21 @@ __global__ __launch_bounds__(64 * kWaves, PA_DECODE_MIN_WAVES_PER_SIMD) void dec
     auto key = [&](int x) { return x < 0 ? 0 : min(x, a.max_ctx); };
     for (int i = tid; i < a.B; i += 64 * kWaves) lens_s[i] = key(a.ctx_lens[i]);
     __syncthreads();
-    for (int i = tid; i < a.B; i += 64 * kWaves) {
-      const int li = lens_s[i];
-      int rank = 0;
-      for (int j = 0; j < a.B; ++j) {
+    // rank of sequence i = number of sequences ahead of it; S adjacent lanes
+    // share one i, each counting every S-th j, and add up their counts
+    constexpr int kT = 64 * kWaves;
+    int S = 64;
+    while (S > 1 && S * a.B > kT) S >>= 1;
+    const int i = tid / S, s = tid % S;
+    const int li = i < a.B ? lens_s[i] : 0;
+    int rank = 0;
+    if (i < a.B)
+      for (int j = s; j < a.B; j += S) {
         const int lj = lens_s[j];
         rank += (lj > li) | ((lj == li) & (j < i));
       }
-      if (rank == b) sorted_b = i;
-    }
+    for (int o = 1; o < S; o <<= 1) rank += __shfl_xor(rank, o);
+    if (i < a.B && s == 0 && rank == b) sorted_b = i;
     __syncthreads();
     b = uniform(sorted_b);
   }

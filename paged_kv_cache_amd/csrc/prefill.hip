@@ -116,6 +116,7 @@ __global__ __launch_bounds__(64 * kBlocks, OCC) void prefill_kernel(PrefillArgs 
   // a visible key always moves it.
   constexpr float kSpecLimit = 0x1p64f;
   constexpr float kMaxFloor = -1e30f;              // finite start of the running max
+  constexpr int kStoreDevice = 16;                 // buffer-store cache policy: sc1 (device scope)
 
 
   // Ring of NS stages, each a K tile and a V tile ([key][chunk], swizzled).
@@ -609,25 +610,49 @@ __global__ __launch_bounds__(64 * kBlocks, OCC) void prefill_kernel(PrefillArgs 
 
   if (err_bits && tid == 0) raise_err(a.err, err_bits);
 
-  // ---- epilogue: one divide per row, LSE in natural-log units
+  // ---- epilogue: one divide per row, LSE in natural-log units.  O leaves
+  // through LDS: the workgroup's tile (BM rows x HW heads x D, bf16; the HW
+  // heads of a row are adjacent in O) is staged row by row in the ring's
+  // first stage and stored with 16-byte writes covering whole rows, at device
+  // scope (sc1), so the lines go out while other workgroups still compute
+  // instead of staying dirty in L2 until the kernel ends.
   {
     auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_lane), __float_as_uint(l_lane), false, false);
     const float l_row = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
     const bool has = row < qlen && l_row > 0.f;
     const float inv_l = has ? 1.f / l_row : 0.f;
-    if (row < T) {
-      uint16_t *op = a.O + (((int64_t)b * T + row) * Hq + head) * D;
+    if (row < T && lh == 0)
+      a.LSE[((int64_t)b * Hq + head) * T + row] = has ? (m_run + fast_log2(l_row)) * kLn2 : -INFINITY;
+    constexpr int RB = HW * ROWB;   // bytes of one staged row
+    constexpr int RC = RB / 16;     // its 16-byte chunks (chunk c sits at c ^ (row % 8))
+    static_assert(RC % 8 == 0 && BM * RB == 2 * TILEB, "O tile = one ring stage");
+    auto srow = [&](int r) -> uint8_t * { return r < BM / 2 ? lk0 + r * RB : lv0 + (r - BM / 2) * RB; };
+    __syncthreads();   // every wave is done with the ring (its transfers have landed)
+    {
+      const int r = 32 * (wave / HW) + lr;
+      uint8_t *dst = srow(r);
 #pragma unroll
       for (int mb = 0; mb < D / 32; ++mb)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
+          const int c = ((wave % HW) * D + mb * 32 + 8 * g) / 8;
           uint2 w;
           w.x = has ? pack_bf16x2(acc[mb][4 * g + 0] * inv_l, acc[mb][4 * g + 1] * inv_l) : 0u;
           w.y = has ? pack_bf16x2(acc[mb][4 * g + 2] * inv_l, acc[mb][4 * g + 3] * inv_l) : 0u;
-          *reinterpret_cast<uint2 *>(op + mb * 32 + 8 * g + 4 * lh) = w;
+          *reinterpret_cast<uint2 *>(dst + (c ^ (r & 7)) * 16 + 8 * lh) = w;
         }
-      if (lh == 0)
-        a.LSE[((int64_t)b * Hq + head) * T + row] = has ? (m_run + fast_log2(l_row)) * kLn2 : -INFINITY;
+    }
+    __syncthreads();
+    const int rows = min(BM, T - rb * BM);   // staged rows inside O
+    const int64_t row_stride = (int64_t)Hq * ROWB;
+    uint8_t *obase = reinterpret_cast<uint8_t *>(a.O) + (((int64_t)b * T + rb * BM) * Hq + hg * HW) * ROWB;
+    const int64_t span = (int64_t)(rows - 1) * row_stride + RB;
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(obase, (short)0, (int)min(span, (int64_t)0x7fffffff), 0x00020000);
+    for (int ci = tid; ci < rows * RC; ci += 64 * NW) {
+      const int r = ci / RC, cc = ci % RC;
+      const u32x4 v = *reinterpret_cast<const u32x4 *>(srow(r) + (cc ^ (r & 7)) * 16);
+      __builtin_amdgcn_raw_buffer_store_b128(v, rs, (int)(r * row_stride) + cc * 16, 0, kStoreDevice);
     }
   }
 }
