@@ -43,6 +43,32 @@ def test_prefill_ragged(Hq, Hkv, d, causal):
     assert torch.all(O[4] == 0) and torch.all(torch.isneginf(L[4]))
 
 
+@pytest.mark.parametrize("Hq,Hkv,d", [(32, 8, 64), (8, 8, 128), (16, 8, 64)])
+def test_prefill_writes_every_output(Hq, Hkv, d):
+    # O and LSE start as NaN: every element, padding rows (past a sequence's
+    # length) and rows of the last partial query tile included, is written
+    lens = [77, 3, 0, 100]
+    case = W.make_prefill("poisoned", B=len(lens), T=100, Hq=Hq, Hkv=Hkv, d=d, n_pages=40,
+                          seed=7 * Hq + d, seq_lens=lens, causal=True)
+    c = case.cache
+    bt = i32(c.block_table)
+    pool = device_pool(c)
+    scatter(pool, c, case.tokens, bt)
+    q = case.q.to(DEV)
+    O = torch.full_like(q, float("nan"))
+    L = torch.full((case.B, case.Hq, case.T), float("nan"), dtype=torch.float32, device=DEV)
+    pa.attn_prefill(q, pool, bt, c.layer, i32(case.seq_lens), c.n_kv_heads, case.scale, True,
+                    slot_ids=i32(case.slot_ids), out=O, lse=L)
+    torch.cuda.synchronize()
+    assert not torch.isnan(O).any() and not torch.isnan(L).any()
+    Oref, Lref, _ = oracle.prefill_case(case)
+    B, T = case.B, case.T
+    assert_attn_close(O.reshape(B * T, Hq, d), L.permute(0, 2, 1).reshape(B * T, Hq), Oref, Lref,
+                      what=case.name)
+    for b, n in enumerate(lens):   # padding rows: O = 0, LSE = -inf
+        assert torch.all(O[b, n:] == 0) and torch.all(torch.isneginf(L[b, :, n:]))
+
+
 def _ramped(k: torch.Tensor, pos: torch.Tensor, top: float) -> torch.Tensor:
     """|k| scaled by 1 + top*pos/max(pos): with |q| the scores climb along the keys."""
     ramp = 1.0 + top * pos.float() / max(1, int(pos.max()))
