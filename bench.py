@@ -149,8 +149,8 @@ def source_digest(*names: str) -> str:
 # was taken on (digest of the .hip files), null otherwise.
 TRAFFIC = {
     # kernel: (source digest, fetched bytes, written bytes)
-    "prefill": ("dbc6d761975fe88e", 25385933, 17301504),
-    "decode": ("7c0357daf7ffba2e", 152911640, 273088),
+    "prefill": ("dbc6d761975fe88e", 25385805, 17301504),
+    "decode": ("c3e697a2eb38e9d8", 152921751, 272864),
 }
 
 
@@ -340,7 +340,7 @@ def kernels_only(n: int) -> None:
     print(f"kernels-only: {n} launches each", flush=True)
 
 
-SWEEP_PARTS = ("tiny", "dense", "long_prefill", "long_decode", "chunk", "append", "backward")
+SWEEP_PARTS = ("tiny", "dense", "long_prefill", "long_decode", "decode_d128", "chunk", "append", "backward")
 
 
 def sweep(parts=SWEEP_PARTS) -> None:
@@ -422,6 +422,27 @@ def sweep(parts=SWEEP_PARTS) -> None:
         n_splits = pa.decode_splits(dcase.B, dcase.Hq, c.n_kv_heads, dcase.d, dcase.max_ctx)
         emit("long decode 4 x 16384 (32/8/64, paged)", t * 1e6, kvb / t / 1e9, "GB/s",
              f"{n_splits} workgroup splits per context (+ combine kernel)")
+
+    if "decode_d128" in parts:
+        # the decode batch with head_dim 128: 64 sequences, ctx ~ U[1, 2048], 32/8 heads,
+        # 4 page-disjoint replicas cycled (1.1 GB of K/V, past the MALL)
+        dcase = W.make_decode("decode_d128", B=64, Hq=32, Hkv=8, d=128, n_pages=20000, seed=0)
+        c = dcase.cache
+        pool = device_pool(c)
+        tables = [i32(tb) for tb in decode_replicas(dcase, 4)]
+        for tb in tables:
+            for tok in (dcase.context, dcase.new_tokens):
+                pa.kv_scatter(tok.k.to(DEV), tok.v.to(DEV), i32(tok.slot_ids), i32(tok.positions), pool, tb,
+                              c.layer)
+        qd, lens, sid = dcase.q.to(DEV), i32(dcase.ctx_lens), i32(dcase.slot_ids)
+        ws = pa.decode_workspace(dcase.B, dcase.Hq, c.n_kv_heads, dcase.d, dcase.max_ctx, DEV)
+        t = kernel_time(lambda: [pa.attn_decode(qd, pool, tb, c.layer, lens, c.n_kv_heads, dcase.scale,
+                                                dcase.max_ctx, slot_ids=sid, workspace=ws) for tb in tables],
+                        reps=4) / len(tables)
+        kvb = int(dcase.ctx_lens.sum()) * c.n_kv_heads * dcase.d * 2 * 2
+        emit("decode B=64, ctx ~ U[1, 2048] (32/8/128, paged)", t * 1e6, kvb / t / 1e9, "GB/s",
+             f"{int(dcase.ctx_lens.sum())} context tokens")
+        del pool
 
     if "chunk" in parts:
         # prefix continuation and a mixed prefill + decode batch (attn_prefill_chunk);

@@ -354,59 +354,130 @@ __global__ __launch_bounds__(64 * kWaves, PA_DECODE_MIN_WAVES_PER_SIMD) void dec
     }
   };
 
-  // ---- ring of register steps: step i is processed while step i+1 is in
-  // flight.  A step is kSub chunks (kSub*32 tokens): the more bytes a step
-  // moves, the fewer latency-bound steps a workgroup takes.
-  struct Step {
-    Chunk<D> c[kSub];
-  };
-  Step r0, r1;
-  auto issue_step = [&](Step &st, int i) {
-#pragma unroll
-    for (int j = 0; j < kSub; ++j) issue(st.c[j], t_begin + ((w + kWaves * i) * kSub + j) * kChunk);
-  };
-  auto process_step = [&](Step &st, int i) {
-#pragma unroll
-    for (int j = 0; j < kSub; ++j) {
-      const int c0 = t_begin + ((w + kWaves * i) * kSub + j) * kChunk;
-      if (c0 < t_end) process(st.c[j], c0);
+  if constexpr (D == 128) {
+    // d=128: a chunk loop driven by the next chunk's index, the partial saved
+    // inside it (fewer registers live at once than the loop below)
+    // a partial result (unnormalised output, reference max, exp-sum) into LDS,
+    // then start afresh
+    auto save = [&](float (*o)[D], float *m, float *l) {
+      const float l_tot = rows_sum(l_lane);
+      if (lrow < G) {
+  #pragma unroll
+        for (int mb = 0; mb < D / 16; ++mb)
+  #pragma unroll
+          for (int i = 0; i < 4; ++i) o[lrow][mb * 16 + 4 * lgrp + i] = acc[mb][i];
+        if (lgrp == 0) {
+          m[lrow] = m_run;
+          l[lrow] = l_tot;
+        }
+      }
+  #pragma unroll
+      for (int mb = 0; mb < D / 16; ++mb) acc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      m_run = kMaxFloor;
+      l_lane = 0.f;
+    };
+    // this wavefront's next chunk (-1: none left)
+    int taken = 0;
+    auto next = [&]() -> int {
+      if (taken < n_my) return w + kWaves * taken++;
+      return -1;
+    };
+    // the partial goes out after the wavefront's last chunk
+    const int last_static = w + kWaves * (n_my - 1);
+    auto after = [&](int k) {
+      if (k == last_static) save(red_o[w], red_m[w], red_l[w]);
+    };
+    if (n_my == 0) save(red_o[w], red_m[w], red_l[w]);   // no static chunk: an empty partial
+
+    // ---- ring of register chunks: chunk k is processed while the next one is
+    // in flight.  Exactly one chunk is in flight at the top of every iteration,
+    // on every path; the last chunk is processed in a branch of its own, with
+    // nothing issued after it, so no load is made past the end.
+    auto tok = [&](int k) { return t_begin + k * kChunk; };
+    int cur = next();
+    if (cur >= 0) {
+      Chunk<D> r0, r1;
+      issue(r0, tok(cur));
+      for (;;) {
+        int nx = next();
+        if (nx < 0) {
+          process(r0, tok(cur));
+          after(cur);
+          break;
+        }
+        issue(r1, tok(nx));
+        process(r0, tok(cur));
+        after(cur);
+        cur = nx;
+        nx = next();
+        if (nx < 0) {
+          process(r1, tok(cur));
+          after(cur);
+          break;
+        }
+        issue(r0, tok(nx));
+        process(r1, tok(cur));
+        after(cur);
+        cur = nx;
+      }
     }
-  };
-  // Exactly one step is in flight at the top of every iteration, on every
-  // path; the last step is processed in a branch of its own, with nothing
-  // issued after it, so no load is made past the end.
-  if (n_my > 0) {
-    issue_step(r0, 0);
-    for (int i = 0;;) {
-      if (i + 1 >= n_my) {
+  } else {
+    // ---- ring of register steps: step i is processed while step i+1 is in
+    // flight.  A step is kSub chunks (kSub*32 tokens): the more bytes a step
+    // moves, the fewer latency-bound steps a workgroup takes.
+    struct Step {
+      Chunk<D> c[kSub];
+    };
+    Step r0, r1;
+    auto issue_step = [&](Step &st, int i) {
+  #pragma unroll
+      for (int j = 0; j < kSub; ++j) issue(st.c[j], t_begin + ((w + kWaves * i) * kSub + j) * kChunk);
+    };
+    auto process_step = [&](Step &st, int i) {
+  #pragma unroll
+      for (int j = 0; j < kSub; ++j) {
+        const int c0 = t_begin + ((w + kWaves * i) * kSub + j) * kChunk;
+        if (c0 < t_end) process(st.c[j], c0);
+      }
+    };
+    // Exactly one step is in flight at the top of every iteration, on every
+    // path; the last step is processed in a branch of its own, with nothing
+    // issued after it, so no load is made past the end.
+    if (n_my > 0) {
+      issue_step(r0, 0);
+      for (int i = 0;;) {
+        if (i + 1 >= n_my) {
+          process_step(r0, i);
+          break;
+        }
+        issue_step(r1, i + 1);
         process_step(r0, i);
-        break;
-      }
-      issue_step(r1, i + 1);
-      process_step(r0, i);
-      ++i;
-      if (i + 1 >= n_my) {
+        ++i;
+        if (i + 1 >= n_my) {
+          process_step(r1, i);
+          break;
+        }
+        issue_step(r0, i + 1);
         process_step(r1, i);
-        break;
+        ++i;
       }
-      issue_step(r0, i + 1);
-      process_step(r1, i);
-      ++i;
     }
   }
 
   if (err_bits && lane == 0) raise_err(a.err, err_bits);
 
   // ---- merge the wavefronts: unnormalised outputs, maxima and sums via LDS
-  const float l_tot = rows_sum(l_lane);
-  if (lrow < G) {
+  if constexpr (D != 128) {
+    const float l_tot = rows_sum(l_lane);
+    if (lrow < G) {
 #pragma unroll
-    for (int mb = 0; mb < D / 16; ++mb)
+      for (int mb = 0; mb < D / 16; ++mb)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) red_o[w][lrow][mb * 16 + 4 * lgrp + i] = acc[mb][i];
-    if (lgrp == 0) {
-      red_m[w][lrow] = m_run;
-      red_l[w][lrow] = l_tot;
+        for (int i = 0; i < 4; ++i) red_o[w][lrow][mb * 16 + 4 * lgrp + i] = acc[mb][i];
+      if (lgrp == 0) {
+        red_m[w][lrow] = m_run;
+        red_l[w][lrow] = l_tot;
+      }
     }
   }
   __syncthreads();
