@@ -150,7 +150,7 @@ def source_digest(*names: str) -> str:
 TRAFFIC = {
     # kernel: (source digest, fetched bytes, written bytes)
     "prefill": ("dbc6d761975fe88e", 25385805, 17301504),
-    "decode": ("c3e697a2eb38e9d8", 152921751, 272864),
+    "decode": ("6ad1bd1579d005d6", 152890778, 273088),
 }
 
 
