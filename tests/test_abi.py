@@ -53,6 +53,17 @@ def test_decode_workspace_size():
     assert pa.decode_splits(4, 32, 8, 64, 16384) >= 2
 
 
+def test_decode_split_policy_one_workgroup_per_cu():
+    # splits give every CU (256 on this part, also the count assumed without a
+    # device) one workgroup: B * Hkv * splits = 256, never below 2 chunks of 32
+    # tokens per wavefront (512 tokens per split)
+    assert pa.decode_splits(4, 32, 8, 64, 16384) == 8      # 32 groups x 8
+    assert pa.decode_splits(16, 32, 8, 64, 2048) == 2      # 128 groups x 2
+    assert pa.decode_splits(1, 32, 8, 64, 3000) == 6       # 32 wanted, 3000 / 512 allowed
+    assert pa.decode_splits(1, 32, 8, 64, 100) == 1
+    assert pa.decode_splits(32, 32, 8, 64, 2048) == 1      # 256 groups already
+
+
 P = ctypes.c_void_p
 
 
