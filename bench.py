@@ -73,13 +73,24 @@ def capture(fn, reps: int = 1) -> torch.cuda.CUDAGraph:
     return g
 
 
-def kernel_time(fn, reps: int = 20, trials: int = 5) -> float:
+def warm(g, seconds: float) -> None:
+    """Replay graph g until `seconds` have passed.  Under a fresh load the GPU's
+    clocks take about 0.1 s to ramp up (the Llama prefill kernel runs ~52 us in
+    the first launches and ~42 us once the GPU is busy), so every measurement
+    here is taken after such a warm-up: the steady state is what is reported."""
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(4):
+            g.replay()
+        torch.cuda.synchronize()
+
+
+def kernel_time(fn, reps: int = 20, trials: int = 5, warm_s: float = 0.1) -> float:
     """Average device time (s) of one call of fn: a graph of `reps` back-to-back
     calls is replayed `trials` times between two HIP events on the launching
-    stream (after one untimed replay); total time / (reps * trials)."""
+    stream (after `warm_s` seconds of untimed replays); total time / (reps * trials)."""
     g = capture(fn, reps)
-    g.replay()
-    torch.cuda.synchronize()
+    warm(g, warm_s)
     s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     s.record()
     for _ in range(trials):
@@ -95,6 +106,7 @@ def launch_spread(fns, n: int = 50, warmup: int = 10) -> dict:
     fns[i % len(fns)].  A single-launch time also holds the gap between the
     event and the kernel (about a microsecond), which the graph averages of
     kernel_time do not."""
+    warm(capture(lambda: [fn() for fn in fns]), 0.1)
     for i in range(warmup):
         fns[i % len(fns)]()
     torch.cuda.synchronize()
@@ -110,8 +122,8 @@ def launch_spread(fns, n: int = 50, warmup: int = 10) -> dict:
 
 
 def timed_steps(step_fns, steps: int, warmup: int, per_graph: int = 8) -> float:
-    """Wall time (s) of exactly `steps` steps after `warmup`, bracketed by device
-    syncs.  Step i runs step_fns[i % n]; the steps are replayed from HIP graphs
+    """Wall time (s) of exactly `steps` steps after 0.2 s of untimed replays
+    (the clocks' ramp, see warm) and `warmup` steps, bracketed by device syncs.  Step i runs step_fns[i % n]; the steps are replayed from HIP graphs
     of `per_graph` consecutive steps (a multiple of n) plus one graph of the
     remainder, so the host launches one graph per `per_graph` steps."""
     n = len(step_fns)
@@ -123,6 +135,7 @@ def timed_steps(step_fns, steps: int, warmup: int, per_graph: int = 8) -> float:
     full = steps_graph(per_graph)
     rem = steps % per_graph
     tail = steps_graph(rem) if rem else None
+    warm(full, 0.2)   # clocks up before the warm-up steps proper
     for _ in range(-(-warmup // per_graph)):
         full.replay()
     torch.cuda.synchronize()
@@ -150,7 +163,7 @@ def source_digest(*names: str) -> str:
 TRAFFIC = {
     # kernel: (source digest, fetched bytes, written bytes)
     "prefill": ("dbc6d761975fe88e", 25385805, 17301504),
-    "decode": ("6ad1bd1579d005d6", 152890778, 273088),
+    "decode": ("6ad1bd1579d005d6", 152918807, 272992),
 }
 
 
