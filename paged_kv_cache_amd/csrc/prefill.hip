@@ -470,9 +470,8 @@ __global__ __launch_bounds__(64 * kBlocks, OCC) void prefill_kernel(PrefillArgs 
     }
     const bool need_mask = (t >= t_mask) | (bad_pages != 0);
     const int rel = lim - (t * kBN + 4 * lh);   // key offset o is visible iff o <= rel
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      // S^T = K Q^T of the half (CH/2 MFMAs, K from LDS)
+    // S^T = K Q^T of half h (CH/2 MFMAs, K from LDS)
+    auto qk = [&](int h) {
       bf16x8 kf[CH / 2];
 #pragma unroll
       for (int k = 0; k < CH / 2; ++k) kf[k] = *reinterpret_cast<const bf16x8 *>(kt + kaddr[k] + h * 32 * ROWB);
@@ -485,6 +484,25 @@ __global__ __launch_bounds__(64 * kBlocks, OCC) void prefill_kernel(PrefillArgs 
 #pragma unroll
       for (int k = 0; k < CH / 2; ++k) s = mfma32(kf[k], qf[k], s);
       __builtin_amdgcn_s_setprio(0);
+      return s;
+    };
+    auto vread = [&](int h, bf16x8 (&vop)[D / 32][2]) {
+#pragma unroll
+      for (int mb = 0; mb < D / 32; ++mb)
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          uint2 part[2];
+#pragma unroll
+          for (int half = 0; half < 2; ++half) {
+            const uint8_t *src = vt + vaddr[mb] + (32 * h + 16 * q + 8 * half) * ROWB;
+            part[half] = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                                       (__attribute__((address_space(3))) i16x4 *)(src)));
+          }
+          vop[mb][q] = __builtin_bit_cast(bf16x8, u32x4{part[0].x, part[0].y, part[1].x, part[1].y});
+        }
+    };
+    // mask, exponentials and PV of half h
+    auto soft_pv = [&](f32x16 &s, int h) {
       if (need_mask) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
@@ -499,25 +517,7 @@ __global__ __launch_bounds__(64 * kBlocks, OCC) void prefill_kernel(PrefillArgs 
           }
         }
       }
-      // V^T operands of the half, read before the exponentials so that their
-      // LDS latency is hidden behind them: vop[mb][q] covers keys
-      // 32h + 16q .. +15 and columns 32mb .. +31
       bf16x8 vop[D / 32][2];
-#pragma unroll
-      for (int mb = 0; mb < D / 32; ++mb)
-#pragma unroll
-        for (int q = 0; q < 2; ++q) {
-          uint2 part[2];
-#pragma unroll
-          for (int half = 0; half < 2; ++half) {
-            const uint8_t *src = vt + vaddr[mb] + (32 * h + 16 * q + 8 * half) * ROWB;
-            part[half] = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                                                       (__attribute__((address_space(3))) i16x4 *)(src)));
-          }
-          vop[mb][q] = __builtin_bit_cast(bf16x8, u32x4{part[0].x, part[0].y, part[1].x, part[1].y});
-        }
-      // P = 2^(s*c - m) (bf16), the B operands of the PV products: pb[q]
-      // covers keys 32h + 16q .. +15; the row sum takes the fp32 p
       bf16x8 pb[2];
       auto exps = [&]() -> float {
         float sum = 0.f;
@@ -531,10 +531,6 @@ __global__ __launch_bounds__(64 * kBlocks, OCC) void prefill_kernel(PrefillArgs 
       };
       float ps = exps();
       if (__any(!(ps < kSpecLimit))) {
-        // some p would be too large (or this is the row's first visible
-        // half): move the running max to the half's max (row max of the raw
-        // scores; scale >= 0 keeps the order), rescale what is accumulated,
-        // and redo the exponentials
         float rmax = -INFINITY;
 #pragma unroll
         for (int r = 0; r < 16; ++r) rmax = fmaxf(rmax, s[r]);
@@ -551,14 +547,22 @@ __global__ __launch_bounds__(64 * kBlocks, OCC) void prefill_kernel(PrefillArgs 
         ps = exps();
       }
       l_lane += ps;
-      // O^T += V^T P^T
+      vread(h, vop);
       __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int q = 0; q < 2; ++q)
 #pragma unroll
         for (int mb = 0; mb < D / 32; ++mb) acc[mb] = mfma32(vop[mb][q], pb[q], acc[mb]);
       __builtin_amdgcn_s_setprio(0);
-    }
+    };
+    // both halves' QK products are issued first, so the second half's run on
+    // the matrix unit while the first half's exponentials run; each half's V
+    // operands are read after its exponentials (read before them, they would
+    // push the wave past the 128 registers of four workgroups per CU)
+    f32x16 s0 = qk(0);
+    f32x16 s1 = qk(1);
+    soft_pv(s0, 0);
+    soft_pv(s1, 1);
   };
 
   // ---- the ring.  Step t: wait for this wave's transfers of tile t, barrier
