@@ -67,7 +67,8 @@ typedef enum pa_status {
     PA_ERR_ALIGN = -4,       /* a tensor pointer is not 16-byte aligned              */
     PA_ERR_WORKSPACE = -5,   /* decode workspace smaller than the size it needs      */
     PA_ERR_RANGE = -6,       /* an index or byte offset would overflow its type      */
-    PA_ERR_LAUNCH = -7       /* the HIP runtime refused the launch                   */
+    PA_ERR_LAUNCH = -7,      /* the HIP runtime refused the launch                   */
+    PA_ERR_VALUE = -8        /* a scalar argument is outside its domain (scale)      */
 } pa_status;
 
 /* Bits OR-ed into the optional device flag `err`. */
@@ -125,6 +126,9 @@ int kv_scatter(const void *k, const void *v, int64_t n_tokens, const int32_t *sl
  *   seq_lens     [B] int32, 0 <= seq_lens[b] <= T: the prompt length.
  *   causal       nonzero: query t sees keys 0..t; zero: keys 0..seq_len-1.
  *   scale        multiplies q.k (pass 1/sqrt(head_dim) for the usual scaling).
+ *                It must be finite and > 0 (the pages scale by 1/sqrt(d));
+ *                anything else returns PA_ERR_VALUE.  The same holds for the
+ *                scale of every attention call below.
  *   O            [B][T][Hq][head_dim] bf16 output.
  *   LSE          [B][Hq][T] fp32 output (natural log, scaled scores).
  *   Rows t >= seq_lens[b] are written as O = 0, LSE = -INFINITY.

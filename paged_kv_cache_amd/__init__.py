@@ -16,8 +16,8 @@ import os
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-# PAGED_KV_LIB may name another build of the same library (e.g. a tuning variant).
-LIB_PATH = os.environ.get("PAGED_KV_LIB") or os.path.join(_HERE, "libpagedattn.so")
+# The in-tree build; nothing in the environment redirects it.
+LIB_PATH = os.path.join(_HERE, "libpagedattn.so")
 _lib = None
 
 PA_DEVERR_BAD_PAGE = 1

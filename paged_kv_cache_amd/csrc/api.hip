@@ -30,6 +30,10 @@ bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 bool supported_head_dim(int d) { return d == 64 || d == 128; }
 
+// The kernels fold the scale into the exponent (exp2(s*scale*log2e - m)) and
+// mask keys with -inf scores, which only works for a finite positive scale.
+bool valid_scale(float s) { return s > 0.f && s <= 3.402823466e38f; }
+
 // Common checks of the paged-cache description.
 int check_cache(const void *kv_cache, int64_t n_pages, const int32_t *block_table, int n_slots,
                 int n_layers, int mbps, int layer, int n_kv_heads, int head_dim) {
@@ -55,6 +59,7 @@ int prefill_common(const void *q, const void *kv_cache, int64_t n_pages, const i
                    float *LSE, int32_t *err, void *stream) {
   if (B < 0 || T < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0) return PA_ERR_SHAPE;
   if (!supported_head_dim(head_dim)) return PA_ERR_UNSUPPORTED;
+  if (!valid_scale(scale)) return PA_ERR_VALUE;
   int rc = check_cache(kv_cache, n_pages, block_table, n_slots, n_layers, max_blocks_per_seq, layer,
                        Hkv, head_dim);
   if (rc != PA_OK) return rc;
@@ -82,6 +87,7 @@ const char *pa_status_string(int status) {
     case PA_ERR_WORKSPACE: return "workspace too small";
     case PA_ERR_RANGE: return "index or byte offset overflow";
     case PA_ERR_LAUNCH: return "kernel launch failed";
+    case PA_ERR_VALUE: return "scale must be finite and > 0";
     default: return "unknown status";
   }
 }
@@ -144,6 +150,7 @@ int attn_decode(const void *q, const void *kv_cache, int64_t n_pages, const int3
   if (!supported_head_dim(head_dim)) return PA_ERR_UNSUPPORTED;
   const int G = Hq / Hkv;
   if (G != 1 && G != 2 && G != 4 && G != 8 && G != 16) return PA_ERR_UNSUPPORTED;
+  if (!valid_scale(scale)) return PA_ERR_VALUE;
   int rc = check_cache(kv_cache, n_pages, block_table, n_slots, n_layers, max_blocks_per_seq, layer,
                        Hkv, head_dim);
   if (rc != PA_OK) return rc;
@@ -166,6 +173,7 @@ int attn_prefill_dense(const void *q, const void *k, const void *v, int B, int T
   if (!supported_head_dim(head_dim)) return PA_ERR_UNSUPPORTED;
   const int G = Hq / Hkv;
   if (G != 1 && G != 2 && G != 4 && G != 8) return PA_ERR_UNSUPPORTED;
+  if (!valid_scale(scale)) return PA_ERR_VALUE;
   if (B == 0 || T == 0) return PA_OK;
   if (!q || !k || !v || !O || !LSE) return PA_ERR_NULL;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(O)) return PA_ERR_ALIGN;
@@ -227,6 +235,7 @@ int attn_backward_dense(const void *q, const void *k, const void *v, const void 
   if (!supported_head_dim(head_dim)) return PA_ERR_UNSUPPORTED;
   const int G = Hq / Hkv;
   if (G != 1 && G != 2 && G != 4 && G != 8) return PA_ERR_UNSUPPORTED;
+  if (!valid_scale(scale)) return PA_ERR_VALUE;
   if (B == 0 || T == 0) return PA_OK;
   if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !workspace) return PA_ERR_NULL;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) ||

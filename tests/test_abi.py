@@ -38,7 +38,7 @@ def test_page_bytes_and_status_strings():
     assert pa.page_bytes(8, 64) == 32768
     assert pa.page_bytes(2, 128) == 2 * 16 * 2 * 128 * 2
     lib = pa.load()
-    for s in range(0, -8, -1):
+    for s in range(0, -9, -1):
         assert lib.pa_status_string(s).decode() not in ("", "unknown status")
     assert lib.pa_status_string(5).decode() == "unknown status"
 
@@ -106,6 +106,27 @@ def test_host_checks_reject_bad_arguments():
                                   64, 0.125, 1, good, good, None, None) == -1
     assert lib.attn_prefill_chunk(good, good, 64, good, 1, 1, 128, 0, None, None, None, 0, 17, 32, 8,
                                   64, 0.125, 1, good, good, None, None) == 0
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.125, float("inf"), float("nan")])
+def test_scale_outside_its_domain_is_rejected(scale):
+    """The kernels take exp2(s * scale * log2 e - m) with -inf masks, which holds
+    for a finite positive scale only: every attention call rejects any other
+    value (PA_ERR_VALUE) before launching anything."""
+    lib = pa.load()
+    good = _fake()
+    assert lib.attn_prefill(good, good, 64, good, 1, 1, 128, 0, None, good, 1, 17, 32, 8, 64,
+                            scale, 1, good, good, None, None) == -8
+    assert lib.attn_prefill_chunk(good, good, 64, good, 1, 1, 128, 0, None, good, good, 1, 17, 32, 8,
+                                  64, scale, 1, good, good, None, None) == -8
+    assert lib.attn_decode(good, good, 64, good, 1, 1, 128, 0, None, good, 1, 32, 8, 64, scale,
+                           64, good, 1 << 20, good, good, None, None) == -8
+    assert lib.attn_prefill_dense(good, good, good, 1, 16, 4, 4, 64, scale, 1, good, good, None) == -8
+    assert lib.attn_backward_dense(good, good, good, good, good, good, 1, 16, 4, 4, 64, scale, 1,
+                                   good, good, good, good, 1 << 20, None) == -8
+    # the smallest and largest finite positive scales are accepted (zero-size no-op calls)
+    for ok in (1e-30, 3.0e38):
+        assert lib.attn_prefill_dense(None, None, None, 0, 16, 4, 4, 64, ok, 1, None, None, None) == 0
 
 
 def _append(lib, **kw):

@@ -66,6 +66,16 @@ def test_mixed_prefill_and_decode_batch():
     assert dO <= 2e-2 and dL <= 1e-3, (dO, dL)
 
 
+@pytest.mark.parametrize("causal", [True, False])
+def test_chunk_after_long_prefix(causal):
+    """300-token chunks after 9000 and 13000 cached tokens (keys in windows 0-3 of
+    the kernel's page offsets, 4096 keys each), 1024 blocks per sequence in the
+    table: every chunk row against the oracle."""
+    case = W.make_chunk("chunk_long", B=2, Hq=32, Hkv=8, d=64, n_pages=2048, kv_lens=[9300, 13300],
+                        q_lens=[300, 300], seed=41, causal=causal, mbps=1024)
+    _parity(case)
+
+
 def test_chunk_whole_prompt_equals_attn_prefill():
     """q_len = kv_len for every sequence: attn_prefill_chunk gives attn_prefill's output bit for bit."""
     case = W.make_chunk("whole", B=3, Hq=32, Hkv=8, d=64, n_pages=80, kv_lens=[200, 77, 128],

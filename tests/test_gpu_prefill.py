@@ -115,14 +115,67 @@ def test_prefill_llama_sampled_rows():
     assert_attn_close(Og, Lg, Oref, Lref, what="llama prefill")
 
 
-def test_prefill_llama_properties_all_rows():
-    """Every row of the full-size prefill: finite, and O within the convex hull
-    bound |O| <= max|V| of the visible keys; LSE >= max visible score."""
+def test_prefill_llama_all_rows():
+    """Every row of the full-size prefill (2 x 2048 rows x 32 heads) element by element."""
     case = W.llama_prefill()
+    _full_parity(case)
+
+
+# Rows around the page-offset windows of the paged kernel (a window holds the
+# pages of 64 key tiles = 4096 keys): the first and last rows of each window,
+# the tile and page edges next to them, and the last rows of the prompt.
+_WINDOW_ROWS = [0, 1, 63, 64, 1000, 4094, 4095, 4096, 4097, 4111, 4112, 4159, 4160, 6000, 8190,
+                8191, 8192, 8193, 8255, 8256, 8500]
+
+
+def _long_rows(case, extra=()):
+    rows = []
+    for b in range(case.B):
+        n = int(case.seq_lens[b]) if case.q_lens is None else int(case.q_lens[b])
+        ts = {t for t in _WINDOW_ROWS + list(extra) if t < n} | {n - 2, n - 1}
+        ts |= set(np.random.default_rng(b).integers(0, n, 12).tolist())
+        rows += [(b, t) for t in sorted(t for t in ts if t >= 0)]
+    return np.array(rows, np.int32)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_prefill_past_one_page_window(causal):
+    """Prompts of 9000 and 8500 tokens (141 and 133 key tiles: windows 0-2 of the
+    kernel's page offsets), 1024 blocks per sequence in the table, against the
+    oracle on rows whose keys reach into each window."""
+    case = W.make_prefill("long_paged", B=2, T=9000, Hq=32, Hkv=8, d=64, n_pages=2048, seed=31,
+                          seq_lens=[9000, 8500], causal=causal, mbps=1024)
     O, L, _ = run_prefill(case)
-    assert torch.isfinite(O.float()).all() and torch.isfinite(L).all()
-    vmax = float(case.tokens.v.float().abs().max())
-    assert float(O.float().abs().max()) <= vmax + 2e-2
+    rows = _long_rows(case)
+    Oref, Lref, _ = oracle.prefill_case(case, rows=rows)
+    Og, Lg = prefill_rows_layout(O, L, rows)
+    assert_attn_close(Og, Lg, Oref, Lref, what=case.name)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_prefill_missing_page_in_second_window(causal):
+    """A missing page among the keys of window 1 (keys 4096-8191) and one in
+    window 2: its keys are left out and flagged; rows before, across and after
+    it match the oracle, which leaves out the same keys."""
+    case = W.make_prefill("hole", B=1, T=9000, Hq=32, Hkv=8, d=64, n_pages=1024, seed=32,
+                          causal=causal, mbps=1024)
+    _, _, pool = run_prefill(case)
+    bt = case.cache.block_table.copy()
+    bt[0, 0, 300] = -1        # keys 4800..4815, tile 75
+    bt[0, 0, 530] = -1        # keys 8480..8495, tile 132
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    O, L = pa.attn_prefill(case.q.to(DEV), pool, i32(bt), 0, i32(case.seq_lens), 8, case.scale,
+                           causal, err=err)
+    rows = _long_rows(case, extra=(4799, 4800, 4815, 4816, 4830, 8479, 8480, 8496, 8990))
+    pool_h = oracle.pool_for(case)
+    oracle.scatter_tokens(pool_h, case.cache, case.tokens)
+    Oref, Lref, bad = oracle.attn_prefill(case.q, pool_h, case.cache.n_pages, bt, 0, None,
+                                          case.seq_lens, 8, case.scale, causal, rows=rows)
+    assert bad > 0
+    torch.cuda.synchronize()
+    assert int(err.item()) == pa.PA_DEVERR_BAD_PAGE
+    Og, Lg = prefill_rows_layout(O, L, rows)
+    assert_attn_close(Og, Lg, Oref, Lref, what="missing pages in windows 1 and 2")
 
 
 def test_prefill_deterministic_and_permutation_bitwise():
@@ -204,7 +257,7 @@ def test_dense_small(d, H, Hkv, causal):
     _dense_parity(W.make_dense("dense", B=2, T=333, Hq=H, Hkv=Hkv, d=d, causal=causal, seed=d + H))
 
 
-@pytest.mark.parametrize("T", [512, 2048, 16384])
+@pytest.mark.parametrize("T", W.FA2_SEQLENS)
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [True, False])
 def test_dense_fa2_shapes_sampled(T, d, causal):
