@@ -200,6 +200,31 @@ int attn_decode(const void *q, const void *kv_cache, int64_t n_pages, const int3
 size_t attn_decode_workspace_size(int B, int Hq, int Hkv, int head_dim, int max_ctx);
 
 /*
+ * attn_decode_noalloc -- attn_decode for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the same kernels and results, bit for bit, but the
+ * partial results of split contexts go to a static device array inside the
+ * library instead of a caller workspace.  Nothing is allocated or freed by
+ * the call.
+ *
+ *   Arguments as for attn_decode, without workspace / workspace_bytes.
+ *   Limit: the array holds 8 MiB on every GPU the library runs on, kept until
+ *   the process ends; a batch shape whose attn_decode_workspace_size exceeds
+ *   it returns PA_ERR_WORKSPACE (no shape does on a 256-CU MI355X, where the
+ *   largest is about 4.3 MB).  The array's device address is looked up on the
+ *   first call on each device (PA_ERR_LAUNCH if that lookup fails).
+ *   All calls on one GPU share the array: calls that overlap in time on the
+ *   same GPU (two streams, or two host threads) race and may return wrong
+ *   results; calls in sequence on one stream are safe.  Every byte a call
+ *   reads from the array it has written in the same call.
+ */
+int attn_decode_noalloc(const void *q, const void *kv_cache, int64_t n_pages,
+                        const int32_t *block_table, int n_slots, int n_layers,
+                        int max_blocks_per_seq, int layer, const int32_t *slot_ids,
+                        const int32_t *ctx_lens, int B, int Hq, int Hkv, int head_dim, float scale,
+                        int max_ctx, void *O, float *LSE, int32_t *err, void *stream);
+
+/*
  * attn_prefill_dense -- the prefill on contiguous K/V (FlashAttention-2
  * explainer, section "Results": the attention-only benchmark shapes).
  *

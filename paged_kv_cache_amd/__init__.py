@@ -61,6 +61,9 @@ def load():
         lib.attn_decode.restype = _I
         lib.attn_decode.argtypes = [_P, _P, _I64, _P, _I, _I, _I, _I, _P, _P, _I, _I, _I, _I, _F,
                                     _I, _P, _SZ, _P, _P, _P, _P]
+        lib.attn_decode_noalloc.restype = _I
+        lib.attn_decode_noalloc.argtypes = [_P, _P, _I64, _P, _I, _I, _I, _I, _P, _P, _I, _I, _I, _I,
+                                            _F, _I, _P, _P, _P, _P]
         lib.attn_decode_workspace_size.restype = _SZ
         lib.attn_decode_workspace_size.argtypes = [_I, _I, _I, _I, _I]
         lib.kv_append.restype = _I
@@ -204,6 +207,27 @@ def attn_decode(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tens
         _dev(out, torch.bfloat16, "out"), _dev(lse, torch.float32, "lse"),
         _dev(err, torch.int32, "err"), _stream(stream))
     _check(rc, "attn_decode")
+    return out, lse
+
+
+def attn_decode_noalloc(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tensor,
+                        layer: int, ctx_lens: torch.Tensor, n_kv_heads: int, scale: float,
+                        max_ctx: int, out: torch.Tensor, lse: torch.Tensor,
+                        slot_ids: torch.Tensor | None = None, err: torch.Tensor | None = None,
+                        stream=None):
+    """attn_decode without a workspace: the split partials go to the library's static
+    device array.  out [B, Hq, d] bf16 and lse [B, Hq] fp32 are caller-provided (this
+    wrapper allocates nothing either); returns (out, lse)."""
+    B, Hq, d = q.shape
+    n_slots, n_layers, mbps = block_table.shape
+    rc = load().attn_decode_noalloc(
+        _dev(q, torch.bfloat16, "q"), _dev(kv_cache, None, "kv_cache"),
+        _n_pages(kv_cache, n_kv_heads, d), _dev(block_table, torch.int32, "block_table"),
+        n_slots, n_layers, mbps, layer, _dev(slot_ids, torch.int32, "slot_ids"),
+        _dev(ctx_lens, torch.int32, "ctx_lens"), B, Hq, n_kv_heads, d, float(scale), int(max_ctx),
+        _dev(out, torch.bfloat16, "out"), _dev(lse, torch.float32, "lse"),
+        _dev(err, torch.int32, "err"), _stream(stream))
+    _check(rc, "attn_decode_noalloc")
     return out, lse
 
 

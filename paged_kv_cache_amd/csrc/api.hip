@@ -141,11 +141,15 @@ size_t attn_decode_workspace_size(int B, int Hq, int Hkv, int head_dim, int max_
   return pa::decode_workspace_bytes(B, Hq, Hkv, head_dim, max_ctx);
 }
 
-int attn_decode(const void *q, const void *kv_cache, int64_t n_pages, const int32_t *block_table,
-                int n_slots, int n_layers, int max_blocks_per_seq, int layer,
-                const int32_t *slot_ids, const int32_t *ctx_lens, int B, int Hq, int Hkv,
-                int head_dim, float scale, int max_ctx, void *workspace, size_t workspace_bytes,
-                void *O, float *LSE, int32_t *err, void *stream) {
+}  // extern "C"
+
+namespace {
+
+// Host checks shared by attn_decode and attn_decode_noalloc (PA_OK: launch).
+int decode_checks(const void *q, const void *kv_cache, int64_t n_pages, const int32_t *block_table,
+                  int n_slots, int n_layers, int max_blocks_per_seq, int layer,
+                  const int32_t *ctx_lens, int B, int Hq, int Hkv, int head_dim, float scale,
+                  int max_ctx, const void *O, const float *LSE) {
   if (B < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || max_ctx < 0) return PA_ERR_SHAPE;
   if (!supported_head_dim(head_dim)) return PA_ERR_UNSUPPORTED;
   const int G = Hq / Hkv;
@@ -157,6 +161,21 @@ int attn_decode(const void *q, const void *kv_cache, int64_t n_pages, const int3
   if (B == 0) return PA_OK;
   if (!q || !ctx_lens || !O || !LSE) return PA_ERR_NULL;
   if (!aligned16(q) || !aligned16(O)) return PA_ERR_ALIGN;
+  return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_decode(const void *q, const void *kv_cache, int64_t n_pages, const int32_t *block_table,
+                int n_slots, int n_layers, int max_blocks_per_seq, int layer,
+                const int32_t *slot_ids, const int32_t *ctx_lens, int B, int Hq, int Hkv,
+                int head_dim, float scale, int max_ctx, void *workspace, size_t workspace_bytes,
+                void *O, float *LSE, int32_t *err, void *stream) {
+  int rc = decode_checks(q, kv_cache, n_pages, block_table, n_slots, n_layers, max_blocks_per_seq,
+                         layer, ctx_lens, B, Hq, Hkv, head_dim, scale, max_ctx, O, LSE);
+  if (rc != PA_OK || B == 0) return rc;
   const size_t ws_need = pa::decode_workspace_bytes(B, Hq, Hkv, head_dim, max_ctx);
   if (ws_need > 0 && !workspace) return PA_ERR_NULL;
   if (ws_need > 0 && !aligned16(workspace)) return PA_ERR_ALIGN;
@@ -165,6 +184,23 @@ int attn_decode(const void *q, const void *kv_cache, int64_t n_pages, const int3
                            max_blocks_per_seq, layer, slot_ids, ctx_lens, B, Hq, Hkv, head_dim,
                            scale, max_ctx, workspace, O, LSE, err,
                            static_cast<hipStream_t>(stream));
+}
+
+int attn_decode_noalloc(const void *q, const void *kv_cache, int64_t n_pages,
+                        const int32_t *block_table, int n_slots, int n_layers,
+                        int max_blocks_per_seq, int layer, const int32_t *slot_ids,
+                        const int32_t *ctx_lens, int B, int Hq, int Hkv, int head_dim, float scale,
+                        int max_ctx, void *O, float *LSE, int32_t *err, void *stream) {
+  int rc = decode_checks(q, kv_cache, n_pages, block_table, n_slots, n_layers, max_blocks_per_seq,
+                         layer, ctx_lens, B, Hq, Hkv, head_dim, scale, max_ctx, O, LSE);
+  if (rc != PA_OK || B == 0) return rc;
+  if (pa::decode_workspace_bytes(B, Hq, Hkv, head_dim, max_ctx) > pa::decode_scratch_bytes())
+    return PA_ERR_WORKSPACE;
+  void *ws = pa::decode_scratch_ptr();
+  if (!ws) return PA_ERR_LAUNCH;
+  return pa::launch_decode(q, kv_cache, n_pages, block_table, n_slots, n_layers,
+                           max_blocks_per_seq, layer, slot_ids, ctx_lens, B, Hq, Hkv, head_dim,
+                           scale, max_ctx, ws, O, LSE, err, static_cast<hipStream_t>(stream));
 }
 
 int attn_prefill_dense(const void *q, const void *k, const void *v, int B, int T, int Hq, int Hkv,

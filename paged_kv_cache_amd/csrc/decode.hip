@@ -41,6 +41,7 @@
 // of workgroups takes the r-th longest context, so the longest work starts
 // first and the CUs finish together (contexts differ by up to 2048x).
 
+#include <mutex>
 #include <type_traits>
 
 #include "device.h"
@@ -569,6 +570,31 @@ Split split_policy(int B, int Hq, int Hkv, int D, int max_ctx) {
 size_t decode_workspace_bytes(int B, int Hq, int Hkv, int D, int max_ctx) {
   const Split s = split_policy(B, Hq, Hkv, D, max_ctx);
   return (size_t)(s.o_bytes + s.lse_bytes);
+}
+
+// ---- the workspace of attn_decode_noalloc: a static device array, one copy
+// per GPU, held until the process ends.  Splits are only made while B * Hkv
+// workgroups leave CUs idle, so on a 256-CU part the partials need at most
+// G * (256 + B * Hkv) * (D + 1) * 4 bytes, under 4.3 MB; 8 MiB leaves room.
+constexpr size_t kScratchBytes = 8u << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+size_t decode_scratch_bytes() { return kScratchBytes; }
+
+void *decode_scratch_ptr() {
+  // `scratch` names a host-side stand-in in host code: the device address of
+  // the current GPU's copy is looked up once per device and kept.
+  static std::mutex mu;
+  static void *ptr[64];
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!ptr[dev]) {
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+    ptr[dev] = p;
+  }
+  return ptr[dev];
 }
 
 template <int D, int G>

@@ -23,6 +23,12 @@ int launch_prefill_dense(const void *q, const void *k, const void *v, int B, int
 
 size_t decode_workspace_bytes(int B, int Hq, int Hkv, int D, int max_ctx);
 
+// attn_decode_noalloc's workspace: the capacity of the static device array and
+// the current device's address of it (looked up on the first call on each
+// device; nullptr if the lookup fails).
+size_t decode_scratch_bytes();
+void *decode_scratch_ptr();
+
 int launch_decode(const void *q, const void *kv_cache, int64_t n_pages, const int32_t *block_table,
                   int n_slots, int n_layers, int mbps, int layer, const int32_t *slot_ids,
                   const int32_t *ctx_lens, int B, int Hq, int Hkv, int D, float scale, int max_ctx,

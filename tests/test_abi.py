@@ -129,6 +129,19 @@ def test_scale_outside_its_domain_is_rejected(scale):
         assert lib.attn_prefill_dense(None, None, None, 0, 16, 4, 4, 64, ok, 1, None, None, None) == 0
 
 
+def test_noalloc_decode_host_checks():
+    """attn_decode_noalloc checks its arguments like attn_decode before it looks
+    anything up on the device; B == 0 is a no-op."""
+    lib = pa.load()
+    good = _fake()
+    args = [good, good, 64, good, 1, 1, 128, 0, None, good, 1, 32, 8, 64, 0.125, 64, good, good,
+            None, None]
+    assert lib.attn_decode_noalloc(*args[:14], 0.0, *args[15:]) == -8
+    assert lib.attn_decode_noalloc(None, *args[1:]) == -1
+    assert lib.attn_decode_noalloc(*args[:11], 96, 3, *args[13:]) == -3
+    assert lib.attn_decode_noalloc(*args[:10], 0, *args[11:]) == 0
+
+
 def _append(lib, **kw):
     good = _fake()
     a = dict(k=good, v=good, q_in=None, q_out=None, Hq=0, B=4, slot_ids=None, positions=good,
