@@ -23,7 +23,8 @@ def _parity(case, what=None):
 
 
 @pytest.mark.parametrize("Hq,Hkv,d", [(32, 8, 64), (8, 8, 64), (16, 8, 64), (64, 8, 64),
-                                      (16, 1, 64), (32, 8, 128), (8, 8, 128), (16, 1, 128)])
+                                      (16, 1, 64), (32, 8, 128), (8, 8, 128), (16, 1, 128),
+                                      (48, 12, 64), (32, 16, 64), (16, 4, 128)])
 def test_decode_ragged_contexts(Hq, Hkv, d):
     # lengths around page (16), chunk (32) and split boundaries, plus an empty context
     ctx = [1, 2, 15, 16, 17, 31, 32, 33, 63, 64, 65, 100, 255, 256, 257, 700, 1000, 0]
@@ -145,3 +146,28 @@ def test_decode_bad_length_is_flagged():
                    case.scale, 30, err=err)
     torch.cuda.synchronize()
     assert int(err.item()) & pa.PA_DEVERR_BAD_POS
+
+
+def test_decode_workspace_reused_across_shapes():
+    """One workspace, sized for the largest of three shapes and filled with NaN
+    bytes before every call (its contents on entry must not matter), serves:
+    long contexts split across workgroups (their partials in the workspace), a
+    ragged batch, and two short contexts."""
+    cases = [W.long_decode(),
+             W.make_decode("ragged", B=18, Hq=32, Hkv=8, d=64, n_pages=200,
+                           ctx_lens=[1, 2, 15, 16, 17, 31, 32, 33, 63, 64, 65, 100, 255, 256, 257, 700, 1000, 0],
+                           seed=3),
+             W.make_decode("short", B=2, Hq=32, Hkv=8, d=64, n_pages=16, ctx_lens=[40, 7], seed=4)]
+    n = max(pa.decode_workspace_size(c.B, c.Hq, c.cache.n_kv_heads, c.d, max(c.max_ctx, 1)) for c in cases)
+    ws = torch.empty(n, dtype=torch.uint8, device=DEV)
+    for case in cases:
+        c = case.cache
+        pool = device_pool(c)
+        bt = i32(c.block_table)
+        scatter(pool, c, case.context, bt)
+        scatter(pool, c, case.new_tokens, bt)
+        ws.view(torch.int16)[: n // 2].fill_(0x7FC0)   # bf16 / fp32 quiet-NaN bytes
+        O, L = pa.attn_decode(case.q.to(DEV), pool, bt, c.layer, i32(case.ctx_lens), c.n_kv_heads,
+                              case.scale, max(case.max_ctx, 1), slot_ids=i32(case.slot_ids), workspace=ws)
+        Oref, Lref, _ = oracle.decode_case(case)
+        assert_attn_close(O, L, Oref, Lref, what=case.name)
