@@ -29,8 +29,22 @@ _I = ctypes.c_int
 _D = ctypes.c_double
 
 
-def build(force: bool = True) -> str:
-    """Compile oracle.c into liboracle.so (portable flags: the .so may run on another host)."""
+SANITIZE_FLAGS = ["-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+                  "-fno-sanitize-recover=all"]
+
+
+def build(force: bool = True, sanitize: bool = False, out: str | None = None) -> str:
+    """Compile oracle.c into liboracle.so (portable flags: the .so may run on another host).
+
+    sanitize=True builds a host-only AddressSanitizer + UndefinedBehaviorSanitizer
+    copy instead (``out``, default liboracle_san.so next to the source), which
+    stops at the first error; a process that loads it needs libasan first in its
+    library list (LD_PRELOAD), since the Python interpreter is not instrumented."""
+    if sanitize:
+        out = out or os.path.join(_HERE, "liboracle_san.so")
+        subprocess.run(["gcc", "-std=c11", *SANITIZE_FLAGS, "-fopenmp", "-fPIC", "-shared", "-Wall",
+                        "-Werror", _SRC, "-o", out, "-lm"], check=True)
+        return out
     if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
         tmp = _LIB + ".tmp"
         subprocess.run(["gcc", "-std=c11", "-O2", "-fopenmp", "-fPIC", "-shared", "-Wall",
