@@ -210,8 +210,20 @@ def bench_prefill(steps: int, warmup: int):
     assert torch.equal(O, O_ref) and torch.equal(L, L_ref), "graph replay differs from eager"
     flops = prefill_flops(case.B, case.T, case.Hq, case.d, True)
     alg_bytes = (q.numel() + O.numel()) * 2 + L.numel() * 4 + 2 * k.numel() * 2
-    return dict(case=case, wall=wall, flops=flops, t_kernel=kernel_time(prefill),
+    t_kernel = kernel_time(prefill)
+    return dict(case=case, wall=wall, flops=flops, t_kernel=t_kernel, clock_ghz=sustained_clock(),
                 t_scatter=kernel_time(scatter), alg_bytes=alg_bytes, spread=launch_spread([prefill]))
+
+
+RATED_CLOCK_GHZ = 2.4          # the clock the 2.5 PFLOP/s bf16 figure is rated at
+
+
+def sustained_clock() -> float:
+    """Median shader clock (GHz) over 4096 waves that keep every SIMD issuing
+    bf16 matrix products for about a millisecond (pa_clock_probe)."""
+    pa.clock_probe(4096, 2000)          # untimed: raise the clock from idle
+    ghz = pa.clock_probe(4096, 20000).cpu()
+    return float(ghz.median())
 
 
 # ------------------------------------------------------------------ decode
@@ -279,38 +291,104 @@ def bench_decode(steps: int, warmup: int, replicas: int = 8):
 
 # -------------------------------------------------------------- CPU oracle
 
+def host_info() -> dict:
+    """Host CPU facts for the oracle timings: model, logical CPUs, CPUs this
+    process may run on."""
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"cpu_model": model, "nproc": os.cpu_count(), "affinity": len(os.sched_getaffinity(0))}
+
+
+def _repeat(fn, min_s: float):
+    """Seconds per call of fn, called until min_s have passed (at least once)."""
+    reps, t0 = 0, time.perf_counter()
+    while reps < 1 or time.perf_counter() - t0 < min_s:
+        fn()
+        reps += 1
+    return (time.perf_counter() - t0) / reps, reps
+
+
+def spread_rows(B: int, T: int, per_seq: int, seqs=None) -> np.ndarray:
+    """(b, t) rows spread evenly over the positions of sequences `seqs` (all by
+    default): a sample whose causal cost is that of the whole in proportion."""
+    ts = ((np.arange(per_seq) + 0.5) * T / per_seq).astype(np.int64)
+    seqs = range(B) if seqs is None else seqs
+    return np.array([(b, t) for b in seqs for t in ts], np.int32)
+
+
+def row_flops(rows: np.ndarray, T: int, Hq: int, d: int, causal: bool, offset=None) -> float:
+    """FLOPs of the given rows: 4 d Hq per visible (query, key) pair."""
+    t = rows[:, 1].astype(np.int64)
+    keys = (t + 1 + (0 if offset is None else offset[rows[:, 0]])) if causal else np.full_like(t, T)
+    return 4.0 * d * Hq * float(keys.sum())
+
+
+def _one_thread(fn):
+    import oracle
+    n = oracle.num_threads()
+    oracle.set_num_threads(1)
+    try:
+        return fn()
+    finally:
+        oracle.set_num_threads(n)
+
+
 def cpu_prefill_baseline(case):
+    """The fp64 oracle on the Llama prefill: the whole workload on every thread,
+    and an evenly spread row sample on one thread (its own FLOPs / its time)."""
     import oracle
     pool = oracle.pool_for(case)
     oracle.scatter_tokens(pool, case.cache, case.tokens)
-    reps = 0
-    t0 = time.perf_counter()
-    while reps < 1 or time.perf_counter() - t0 < 10.0:   # the whole workload, >= 10 s in all
-        oracle.prefill_case(case, pool=pool)
-        reps += 1
-    dt = (time.perf_counter() - t0) / reps
+    dt, reps = _repeat(lambda: oracle.prefill_case(case, pool=pool), 6.0)
     flops = prefill_flops(case.B, case.T, case.Hq, case.d, True)
+    rows = spread_rows(case.B, case.T, 32)
+    rf = row_flops(rows, case.T, case.Hq, case.d, True)
+    dt1, reps1 = _one_thread(lambda: _repeat(lambda: oracle.prefill_case(case, rows=rows, pool=pool), 4.0))
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.num_threads(),
             "kind": "oracle",
-            "sample": f"the whole workload (2 x 2048 rows x 32 heads, fp64), {reps} repeats of {dt:.2f} s"}
+            "sample": f"the whole workload (2 x 2048 rows x 32 heads, fp64), {reps} repeats of {dt:.2f} s",
+            "one_thread": {"value": round(rf / dt1 / 1e12, 6), "unit": "TFLOP/s", "cores": 1,
+                           "sample": f"{len(rows)} rows spread evenly over both sequences' positions "
+                                     f"({rf / flops * 100:.2f}% of the FLOPs), {reps1} repeats of {dt1:.3f} s",
+                           "whole_workload_s_extrapolated": round(flops * dt1 / rf, 2)},
+            "host": host_info()}
 
 
 def cpu_decode_baseline(case):
+    """The fp64 oracle on the decode step: the whole step on every thread, and
+    8 of the 64 sequences (every 8th by length) on one thread, as KV GB/s."""
     import oracle
     pool = oracle.pool_for(case)
     oracle.scatter_tokens(pool, case.cache, case.context)
     oracle.scatter_tokens(pool, case.cache, case.new_tokens)
-    reps = 0
-    t0 = time.perf_counter()
-    while True:
-        oracle.decode_case(case, pool=pool)
-        reps += 1
-        if time.perf_counter() - t0 > 5.0:
-            break
-    dt = (time.perf_counter() - t0) / reps
-    kv = int(case.ctx_lens.sum()) * case.cache.n_kv_heads * case.d * 4
+    dt, reps = _repeat(lambda: oracle.decode_case(case, pool=pool), 4.0)
+    per_tok = case.cache.n_kv_heads * case.d * 4
+    kv = int(case.ctx_lens.sum()) * per_tok
+    c = case.cache
+    pick = np.argsort(case.ctx_lens, kind="stable")[4::8]
+    sub = dict(q=case.q[torch.as_tensor(pick)], slot_ids=np.asarray(case.slot_ids)[pick], ctx=np.asarray(case.ctx_lens)[pick])
+    kv1 = int(sub["ctx"].sum()) * per_tok
+
+    def sample():
+        oracle.attn_decode(sub["q"], pool, c.n_pages, c.block_table, c.layer, sub["slot_ids"], sub["ctx"],
+                           c.n_kv_heads, case.scale)
+
+    dt1, reps1 = _one_thread(lambda: _repeat(sample, 3.0))
     return {"value": round(kv / dt / 1e9, 4), "unit": "GB/s", "cores": oracle.num_threads(),
-            "kind": "oracle", "sample": f"the whole decode step, {reps} repeats ({dt:.3f} s each)"}
+            "kind": "oracle", "sample": f"the whole decode step, {reps} repeats ({dt:.3f} s each)",
+            "one_thread": {"value": round(kv1 / dt1 / 1e9, 4), "unit": "GB/s", "cores": 1,
+                           "sample": f"8 of the 64 sequences (every 8th by context length, "
+                                     f"{int(sub['ctx'].sum())} of {int(case.ctx_lens.sum())} tokens), "
+                                     f"{reps1} repeats of {dt1:.3f} s",
+                           "whole_step_s_extrapolated": round(kv * dt1 / kv1, 3)},
+            "host": host_info()}
 
 
 COPY_BYTES = 256 << 20
@@ -353,7 +431,8 @@ def kernels_only(n: int) -> None:
     print(f"kernels-only: {n} launches each", flush=True)
 
 
-SWEEP_PARTS = ("tiny", "dense", "long_prefill", "long_decode", "decode_d128", "chunk", "append", "backward")
+SWEEP_PARTS = ("tiny", "dense", "long_prefill", "long_decode", "decode_d128", "chunk", "append", "backward",
+               "cpu")
 
 
 def sweep(parts=SWEEP_PARTS) -> None:
@@ -547,6 +626,58 @@ def sweep(parts=SWEEP_PARTS) -> None:
                          f"fwd+bwd {3.5 * fwd / (tf + tb) / 1e12:.1f} TFLOP/s")
                     del qd, kd, vd, dod, Od, Ld, dq, dk, dv, ws
 
+    if "cpu" in parts:
+        # the fp64 CPU oracle on the 17-token prompt (whole, every thread and one
+        # thread), the dense FA2 grid and the long prefill (64 rows spread
+        # evenly over the first sequence's positions, every thread; rate = the
+        # sample's FLOPs / its time, whole-case time extrapolated from it) and the
+        # long decode (whole, every thread)
+        import oracle
+        nt = oracle.num_threads()
+        host = host_info()
+        print(f"sweep: oracle host: {host}", flush=True)
+        case = W.tiny_prefill()
+        pool = oracle.pool_for(case)
+        oracle.scatter_tokens(pool, case.cache, case.tokens)
+        fl = prefill_flops(1, 17, 32, 64, True)
+        dt, reps = _repeat(lambda: oracle.prefill_case(case, pool=pool), 1.0)
+        dt1, reps1 = _one_thread(lambda: _repeat(lambda: oracle.prefill_case(case, pool=pool), 1.0))
+        emit(f"oracle, {nt} threads: 17-token prefill (whole)", dt * 1e6, fl / dt / 1e9, "GFLOP/s",
+             f"{reps} repeats")
+        emit("oracle, 1 thread: 17-token prefill (whole)", dt1 * 1e6, fl / dt1 / 1e9, "GFLOP/s",
+             f"{reps1} repeats")
+        for d, H in W.FA2_HEADS:
+            for T in W.FA2_SEQLENS:
+                for causal in (False, True):
+                    dc = W.fa2_dense(T, d, causal)
+                    B = 16384 // T
+                    rws = spread_rows(B, T, 64, seqs=[0])
+                    rf = row_flops(rws, T, H, d, causal)
+                    dt, reps = _repeat(lambda: oracle.dense_case(dc, rws), 0.3)
+                    full = prefill_flops(B, T, H, d, causal)
+                    emit(f"oracle, {nt} threads: dense d={d} H={H} T={T} B={B} {'causal' if causal else 'full'}",
+                         dt * full / rf * 1e6, rf / dt / 1e9, "GFLOP/s",
+                         f"64 rows of sequence 0, {rf / full * 100:.3f}% of the FLOPs; "
+                         f"whole case {dt * full / rf:.1f} s extrapolated")
+        lc = W.long_prefill()
+        rws = spread_rows(1, 16384, 64)
+        rf = row_flops(rws, 16384, 16, 128, True)
+        full = prefill_flops(1, 16384, 16, 128, True)
+        dt, reps = _repeat(lambda: oracle.dense_case(lc, rws), 1.0)
+        emit(f"oracle, {nt} threads: long prefill B=1 T=16384 16x128 causal", dt * full / rf * 1e6,
+             rf / dt / 1e9, "GFLOP/s",
+             f"64 rows spread over the positions, {rf / full * 100:.3f}% of the FLOPs; "
+             f"whole case {dt * full / rf:.1f} s extrapolated")
+        dcase = W.long_decode()
+        dpool = oracle.pool_for(dcase)
+        oracle.scatter_tokens(dpool, dcase.cache, dcase.context)
+        oracle.scatter_tokens(dpool, dcase.cache, dcase.new_tokens)
+        dt, reps = _repeat(lambda: oracle.decode_case(dcase, pool=dpool), 1.0)
+        kvb = int(dcase.ctx_lens.sum()) * dcase.cache.n_kv_heads * dcase.d * 2 * 2
+        emit(f"oracle, {nt} threads: long decode 4 x 16384 (whole)", dt * 1e6, kvb / dt / 1e9, "GB/s",
+             f"{reps} repeats")
+        del pool, dpool
+
     print("\n| workload | time (us) | throughput | note |\n|---|---:|---:|---|")
     for name, us, metric, unit, extra in rows:
         print(f"| {name} | {us:.2f} | {metric:.2f} {unit} | {extra} |")
@@ -617,6 +748,9 @@ def main() -> int:
                      "achieved": round(kern_tflops, 3), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(kern_tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic_of("prefill", prefill_digest),
+                     "clock_GHz": round(p["clock_ghz"], 3),
+                     "peak_at_clock": round(PEAK_BF16_TFLOPS * p["clock_ghz"] / RATED_CLOCK_GHZ, 1),
+                     "frac_at_clock": round(kern_tflops / (PEAK_BF16_TFLOPS * p["clock_ghz"] / RATED_CLOCK_GHZ), 4),
                      "avg_us": round(p["t_kernel"] * 1e6, 3), "alg_bytes": p["alg_bytes"],
                      "single_launch": p["spread"], "source_digest": prefill_digest},
         "scatter_us": round(p["t_scatter"] * 1e6, 3),

@@ -87,6 +87,20 @@ const char *pa_status_string(int status);
 int64_t pa_page_bytes(int n_kv_heads, int head_dim);
 
 /*
+ * pa_clock_probe -- a measurement aid, not a step of the attention path: the
+ * shader clock the chip sustains while every SIMD issues bf16 matrix products
+ * (32x32x16), so that MFMA throughput can be quoted against the peak at the
+ * measured clock as well as at the rated one.  Each of n_waves waves (launched
+ * as workgroups of four) runs `iters` steps of four independent products and
+ * writes cycles / (100 MHz real-time ticks / 1e8) / 1e9 -- its clock in GHz --
+ * to ghz[wave] (device memory, n_waves floats, caller-owned).  4096 waves fill
+ * a 256-CU part with four waves per SIMD; 20000 steps last about a millisecond.
+ * Errors: PA_ERR_NULL (ghz NULL with n_waves > 0), PA_ERR_SHAPE (n_waves or
+ * iters < 0), PA_ERR_LAUNCH.  n_waves == 0 is a no-op.
+ */
+int pa_clock_probe(float *ghz, int n_waves, int iters, void *stream);
+
+/*
  * kv_scatter -- write the K and V rows of n_tokens tokens into their pages
  * (page "3. The prefill path", section "Distributing K/V into paged blocks";
  * the decode append of page 6, section "Block contents").

@@ -78,6 +78,8 @@ def load():
         lib.attn_backward_workspace_size.argtypes = [_I, _I, _I]
         lib.attn_prefill_dense.restype = _I
         lib.attn_prefill_dense.argtypes = [_P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P, _P, _P]
+        lib.pa_clock_probe.restype = _I
+        lib.pa_clock_probe.argtypes = [_P, _I, _I, _P]
         _lib = lib
     return _lib
 
@@ -107,6 +109,14 @@ def _stream(stream) -> int | None:
 
 def page_bytes(n_kv_heads: int, head_dim: int) -> int:
     return int(load().pa_page_bytes(n_kv_heads, head_dim))
+
+
+def clock_probe(n_waves: int = 4096, iters: int = 20000, stream=None) -> torch.Tensor:
+    """Per-wave shader clock (GHz, float32 [n_waves]) while every SIMD issues bf16
+    matrix products (a measurement aid, not part of the attention path)."""
+    ghz = torch.zeros(n_waves, dtype=torch.float32, device=torch.device("cuda"))
+    _check(load().pa_clock_probe(ghz.data_ptr(), n_waves, iters, _stream(stream)), "pa_clock_probe")
+    return ghz
 
 
 def _n_pages(kv_cache: torch.Tensor, n_kv_heads: int, head_dim: int) -> int:

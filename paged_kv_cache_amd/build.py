@@ -20,7 +20,8 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libpagedattn.so")
-SOURCES = ["api.hip", "scatter.hip", "append.hip", "decode.hip", "prefill.hip", "backward.hip"]
+SOURCES = ["api.hip", "scatter.hip", "append.hip", "decode.hip", "prefill.hip", "backward.hip",
+           "clock.hip"]
 ARCH = "gfx950"
 
 

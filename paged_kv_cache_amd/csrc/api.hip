@@ -97,6 +97,13 @@ int64_t pa_page_bytes(int n_kv_heads, int head_dim) {
   return 2LL * 16 * n_kv_heads * head_dim * 2;
 }
 
+int pa_clock_probe(float *ghz, int n_waves, int iters, void *stream) {
+  if (n_waves < 0 || iters < 0) return PA_ERR_SHAPE;
+  if (n_waves == 0) return PA_OK;
+  if (!ghz) return PA_ERR_NULL;
+  return pa::launch_clock_probe(ghz, n_waves, iters, static_cast<hipStream_t>(stream));
+}
+
 int kv_scatter(const void *k, const void *v, int64_t n_tokens, const int32_t *slot_ids,
                const int32_t *positions, void *kv_cache, int64_t n_pages,
                const int32_t *block_table, int n_slots, int n_layers, int max_blocks_per_seq,

@@ -7,6 +7,7 @@
 
 namespace pa {
 
+int launch_clock_probe(float *ghz, int n_waves, int iters, hipStream_t stream);
 int launch_kv_scatter(const void *k, const void *v, int64_t n_tokens, const int32_t *slot_ids,
                       const int32_t *positions, void *kv_cache, int64_t n_pages,
                       const int32_t *block_table, int n_slots, int n_layers, int mbps, int layer,
