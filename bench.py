@@ -432,7 +432,7 @@ def kernels_only(n: int) -> None:
 
 
 SWEEP_PARTS = ("tiny", "dense", "long_prefill", "long_decode", "decode_d128", "chunk", "append", "backward",
-               "cpu")
+               "decode_batch", "cpu")
 
 
 def sweep(parts=SWEEP_PARTS) -> None:
@@ -535,6 +535,29 @@ def sweep(parts=SWEEP_PARTS) -> None:
         emit("decode B=64, ctx ~ U[1, 2048] (32/8/128, paged)", t * 1e6, kvb / t / 1e9, "GB/s",
              f"{int(dcase.ctx_lens.sum())} context tokens")
         del pool
+
+    if "decode_batch" in parts:
+        # larger decode batches of the same mix: 256 and 512 sequences, ctx ~ U[1, 2048],
+        # 32/8/64, an 8 GiB pool, 4 page-disjoint replicas cycled
+        for Bd in (256, 512):
+            dcase = W.make_decode(f"decode_b{Bd}", B=Bd, Hq=32, Hkv=8, d=64, n_pages=4 * W.POOL_PAGES,
+                                  seed=Bd, scale=1.0 / 8.0, mbps=128)
+            c = dcase.cache
+            pool = device_pool(c)
+            tables = [i32(tb) for tb in decode_replicas(dcase, 4)]
+            for tb in tables:
+                for tok in (dcase.context, dcase.new_tokens):
+                    pa.kv_scatter(tok.k.to(DEV), tok.v.to(DEV), i32(tok.slot_ids), i32(tok.positions), pool,
+                                  tb, c.layer)
+            qd, lens, sid = dcase.q.to(DEV), i32(dcase.ctx_lens), i32(dcase.slot_ids)
+            ws = pa.decode_workspace(dcase.B, dcase.Hq, c.n_kv_heads, dcase.d, dcase.max_ctx, DEV)
+            t = kernel_time(lambda: [pa.attn_decode(qd, pool, tb, c.layer, lens, c.n_kv_heads, dcase.scale,
+                                                    dcase.max_ctx, slot_ids=sid, workspace=ws)
+                                     for tb in tables], reps=4) / len(tables)
+            kvb = int(dcase.ctx_lens.sum()) * c.n_kv_heads * dcase.d * 2 * 2
+            emit(f"decode B={Bd}, ctx ~ U[1, 2048] (32/8/64, paged)", t * 1e6, kvb / t / 1e9, "GB/s",
+                 f"{int(dcase.ctx_lens.sum())} context tokens, {100 * kvb / t / 1e9 / PEAK_HBM_GBS:.1f}% of HBM")
+            del pool, tables
 
     if "chunk" in parts:
         # prefix continuation and a mixed prefill + decode batch (attn_prefill_chunk);

@@ -35,11 +35,11 @@ def test_decode_ragged_contexts(Hq, Hkv, d):
     assert torch.all(O[-1] == 0) and torch.all(torch.isneginf(L[-1]))
 
 
-@pytest.mark.parametrize("B", [6, 72, 300, 520])
+@pytest.mark.parametrize("B", [6, 72, 128, 129, 300, 520])
 def test_decode_batch_sizes_with_tied_lengths(B):
     # many equal context lengths (ties in the longest-first order), batches
-    # whose ranking is shared by 64, 4 and 1 lanes per sequence, and one above
-    # the ranked limit (512: identity order)
+    # whose ranking is shared by 64 and 4 lanes per sequence, the largest
+    # ranked batch (128) and batches above it (identity order)
     ctx = np.random.default_rng(B).choice([1, 17, 33, 64], size=B)
     case = W.make_decode("ties", B=B, Hq=32, Hkv=8, d=64, n_pages=4 * B + 8, ctx_lens=ctx,
                          seed=B)
