@@ -562,8 +562,11 @@ def sweep(parts=SWEEP_PARTS) -> None:
     if "chunk" in parts:
         # prefix continuation and a mixed prefill + decode batch (attn_prefill_chunk);
         # FLOPs count every visible (query, key) pair: 4 * d * Hq per pair
+        long_chunk = W.make_chunk("chunk_after_16k", B=1, Hq=32, Hkv=8, d=64, n_pages=4096,
+                                  kv_lens=[16384 + 128], q_lens=[128], seed=7, scale=1.0 / 8.0, mbps=1040)
         for cc, label in ((W.llama_chunk(), "chunk: 2 x (2048 cached + 2048 new), 32/8/64, causal"),
-                          (W.mixed_batch(), "mixed: 2 chunks of 512 + 62 decode rows, 32/8/64")):
+                          (W.mixed_batch(), "mixed: 2 chunks of 512 + 62 decode rows, 32/8/64"),
+                          (long_chunk, "chunk: 128 new after 16384 cached, 32/8/64, causal")):
             c = cc.cache
             pool = device_pool(c)
             bt = i32(c.block_table)
@@ -578,7 +581,21 @@ def sweep(parts=SWEEP_PARTS) -> None:
                         for q, k in zip(cc.q_lens, cc.seq_lens))
             emit(label, t * 1e6, 4.0 * cc.d * cc.Hq * pairs / t / 1e12, "TFLOP/s",
                  f"{pairs} visible (query, key) pairs per head")
-            del pool, qc, Oc, Lc
+            # the same batch with packed rows (attn_prefill_packed): the host plan is
+            # made once (outside the timed region, as one plan serves every layer)
+            plan = pa.prefill_packed_plan(cc.q_lens, cc.seq_lens, cc.Hq, c.n_kv_heads, cc.d, True)
+            prow = [(b, r) for b in range(cc.B) for r in range(int(cc.q_lens[b]))]
+            qp = cc.q[torch.tensor([r[0] for r in prow]), torch.tensor([r[1] for r in prow])].contiguous().to(DEV)
+            q_start = i32(np.concatenate([[0], np.cumsum(cc.q_lens)]))
+            wsp = plan.workspace()
+            Op = torch.empty_like(qp)
+            Lp = torch.empty(qp.shape[0], cc.Hq, dtype=torch.float32, device=DEV)
+            t = kernel_time(lambda: pa.attn_prefill_packed(qp, pool, bt, c.layer, kvl, q_start, plan, c.n_kv_heads,
+                                                           cc.scale, True, slot_ids=sid, workspace=wsp, out=Op,
+                                                           lse=Lp), reps=10, trials=3)
+            emit(label.replace(":", " (packed rows):", 1), t * 1e6, 4.0 * cc.d * cc.Hq * pairs / t / 1e12,
+                 "TFLOP/s", f"{plan.n_work} work items, {plan.n_merge} split row blocks merged")
+            del pool, qc, Oc, Lc, qp, Op, Lp, wsp
 
     if "append" in parts:
         # decode append for the 64-sequence batch: RoPE of K and q, page pops, K/V write

@@ -79,6 +79,8 @@ typedef enum pa_status {
 #define PA_DEVERR_DUP_SLOT 16    /* kv_append: a slot is named by two tokens           */
 #define PA_DEVERR_REASSIGNED 32  /* kv_append: an opened block's entry was not -1      */
 #define PA_DEVERR_STACK_FULL 64  /* kv_release: the free stack has no room left        */
+#define PA_DEVERR_BAD_PLAN 128   /* attn_prefill_packed: a work item names no row block   */
+                                 /* of the batch, or a partial slot past the workspace   */
 
 /* Human-readable name of a pa_status value (static string, never NULL). */
 const char *pa_status_string(int status);
@@ -180,6 +182,56 @@ int attn_prefill_chunk(const void *q, const void *kv_cache, int64_t n_pages,
                        const int32_t *q_lens, const int32_t *kv_lens, int B, int T, int Hq,
                        int Hkv, int head_dim, float scale, int causal, void *O, float *LSE,
                        int32_t *err, void *stream);
+
+/*
+ * attn_prefill_packed_plan / attn_prefill_packed -- attn_prefill_chunk for
+ * PACKED query rows: sequence b's q_lens[b] queries are rows q_start[b] ..
+ * q_start[b+1]-1 of q, O and LSE, so a batch mixing prompt chunks and decode
+ * rows (q_lens[b] == 1) stores and computes no padding.  The same reading of
+ * the pages as attn_prefill_chunk (queries aligned to the end of the sequence;
+ * tiny-vllm part 6, "pagedAttentionKernel": a step attends its new queries
+ * over all of the sequence's cached keys), with the key range of long row
+ * blocks split across workgroups (FlashAttention-2 explainer, "Parallelise
+ * along the sequence length") and the pieces merged by the log-sum-exp rule
+ * (tiny-vllm part 3, "causalMask and online softmax").
+ *
+ * attn_prefill_packed_plan runs on the host, once per batch (every layer of
+ * a step can reuse it): from HOST copies of q_lens[B] and kv_lens[B]
+ * (0 <= q_lens[b] <= kv_lens[b], else PA_ERR_SHAPE) it writes the work list
+ * to plan (host int32, plan_capacity entries; 6 * (n_work + n_merge) are
+ * needed) and returns the counts and the workspace the run needs.  plan ==
+ * NULL only computes the counts; a plan_capacity too small returns
+ * PA_ERR_WORKSPACE with the counts set.  The split follows the CU count of
+ * the current device.
+ *
+ * attn_prefill_packed runs the plan, copied to device memory by the caller:
+ *   q            [total_q][Hq][head_dim] bf16 (16-byte aligned).
+ *   kv_lens      [B] int32 (device), the same lengths the plan was made from.
+ *   q_start      [B + 1] int32 (device), q_start[b+1] - q_start[b] == q_lens[b]
+ *                of the plan, q_start[B] <= total_q.
+ *   plan         the plan's 6 * (n_work + n_merge) int32 (device).
+ *   workspace    device memory of at least the plan's workspace_bytes (may be
+ *                NULL when n_merge == 0); its contents on entry do not matter.
+ *   O            [total_q][Hq][head_dim] bf16; LSE [total_q][Hq] fp32: the
+ *                rows of every sequence are written; other rows are left as
+ *                they were.
+ *   other arguments as for attn_prefill_chunk.  Two launches on `stream`
+ *   (the prefill workgroups, then a small merge of the split row blocks).  A
+ *   plan that does not match the lengths gives wrong rows but no access out
+ *   of bounds: device-side, a length outside its range sets PA_DEVERR_BAD_POS
+ *   and a work item naming no row block or a slot past the workspace sets
+ *   PA_DEVERR_BAD_PLAN (the item is skipped).  Head groups 1, 2, 4, 8.
+ */
+int attn_prefill_packed_plan(const int32_t *q_lens, const int32_t *kv_lens, int B, int Hq, int Hkv,
+                             int head_dim, int causal, int32_t *plan, int64_t plan_capacity,
+                             int64_t *n_work, int64_t *n_merge, size_t *workspace_bytes);
+int attn_prefill_packed(const void *q, const void *kv_cache, int64_t n_pages,
+                        const int32_t *block_table, int n_slots, int n_layers,
+                        int max_blocks_per_seq, int layer, const int32_t *slot_ids,
+                        const int32_t *kv_lens, const int32_t *q_start, int B, int64_t total_q,
+                        int Hq, int Hkv, int head_dim, float scale, int causal,
+                        const int32_t *plan, int64_t n_work, int64_t n_merge, void *workspace,
+                        size_t workspace_bytes, void *O, float *LSE, int32_t *err, void *stream);
 
 /*
  * attn_decode -- attention of one new query per sequence over its whole cached

@@ -13,6 +13,7 @@ from __future__ import annotations
 import ctypes
 import os
 
+import numpy as np
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -27,6 +28,7 @@ PA_DEVERR_NO_FREE_PAGE = 8
 PA_DEVERR_DUP_SLOT = 16
 PA_DEVERR_REASSIGNED = 32
 PA_DEVERR_STACK_FULL = 64
+PA_DEVERR_BAD_PLAN = 128
 
 _P = ctypes.c_void_p
 _I = ctypes.c_int
@@ -78,6 +80,11 @@ def load():
         lib.attn_backward_workspace_size.argtypes = [_I, _I, _I]
         lib.attn_prefill_dense.restype = _I
         lib.attn_prefill_dense.argtypes = [_P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P, _P, _P]
+        lib.attn_prefill_packed_plan.restype = _I
+        lib.attn_prefill_packed_plan.argtypes = [_P, _P, _I, _I, _I, _I, _I, _P, _I64, _P, _P, _P]
+        lib.attn_prefill_packed.restype = _I
+        lib.attn_prefill_packed.argtypes = [_P, _P, _I64, _P, _I, _I, _I, _I, _P, _P, _P, _I, _I64, _I, _I,
+                                            _I, _F, _I, _P, _I64, _I64, _P, _SZ, _P, _P, _P, _P]
         lib.pa_clock_probe.restype = _I
         lib.pa_clock_probe.argtypes = [_P, _I, _I, _P]
         _lib = lib
@@ -172,6 +179,70 @@ def attn_prefill(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Ten
                                        _dev(q_lens, torch.int32, "q_lens"),
                                        _dev(seq_lens, torch.int32, "seq_lens"), *tail)
         _check(rc, "attn_prefill_chunk")
+    return out, lse
+
+
+class PackedPlan:
+    """The work list of one packed batch (attn_prefill_packed_plan): ``host`` the
+    int32 items, ``plan`` their device copy, the counts and the workspace bytes."""
+
+    def __init__(self, host: np.ndarray, n_work: int, n_merge: int, workspace_bytes: int, device):
+        self.host = host
+        self.n_work = n_work
+        self.n_merge = n_merge
+        self.workspace_bytes = workspace_bytes
+        self.plan = torch.from_numpy(host).to(device)
+
+    def workspace(self) -> torch.Tensor | None:
+        if self.workspace_bytes == 0:
+            return None
+        return torch.empty(self.workspace_bytes, dtype=torch.uint8, device=self.plan.device)
+
+
+def prefill_packed_plan(q_lens, kv_lens, n_q_heads: int, n_kv_heads: int, head_dim: int,
+                        causal: bool = True, device=None) -> PackedPlan:
+    """Plan a packed batch on the host from host lengths (sequences, arrays of int)."""
+    ql = np.ascontiguousarray(np.asarray(q_lens), dtype=np.int32)
+    kv = np.ascontiguousarray(np.asarray(kv_lens), dtype=np.int32)
+    if ql.shape != kv.shape or ql.ndim != 1:
+        raise ValueError("q_lens and kv_lens must be 1-D and of one length")
+    nw, nm, wb = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_size_t()
+    args = (ql.ctypes.data, kv.ctypes.data, ql.size, n_q_heads, n_kv_heads, head_dim, int(bool(causal)))
+    lib = load()
+    _check(lib.attn_prefill_packed_plan(*args, None, 0, ctypes.byref(nw), ctypes.byref(nm), ctypes.byref(wb)),
+           "attn_prefill_packed_plan")
+    host = np.zeros(max(6 * (nw.value + nm.value), 6), np.int32)
+    _check(lib.attn_prefill_packed_plan(*args, host.ctypes.data, host.size, ctypes.byref(nw), ctypes.byref(nm),
+                                        ctypes.byref(wb)), "attn_prefill_packed_plan")
+    return PackedPlan(host, nw.value, nm.value, wb.value, device or torch.device("cuda"))
+
+
+def attn_prefill_packed(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tensor, layer: int,
+                        kv_lens: torch.Tensor, q_start: torch.Tensor, plan: PackedPlan, n_kv_heads: int,
+                        scale: float, causal: bool = True, slot_ids: torch.Tensor | None = None,
+                        workspace: torch.Tensor | None = None, out: torch.Tensor | None = None,
+                        lse: torch.Tensor | None = None, err: torch.Tensor | None = None, stream=None):
+    """Packed prefill of q [total_q, Hq, d] (sequence b's rows q_start[b] .. q_start[b+1]-1)
+    by a plan from prefill_packed_plan; returns (O [total_q, Hq, d] bf16, LSE [total_q, Hq] fp32)."""
+    total_q, Hq, d = q.shape
+    B = kv_lens.numel()
+    n_slots, n_layers, mbps = block_table.shape
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty(total_q, Hq, dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = plan.workspace()
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = load().attn_prefill_packed(
+        _dev(q, torch.bfloat16, "q"), _dev(kv_cache, None, "kv_cache"), _n_pages(kv_cache, n_kv_heads, d),
+        _dev(block_table, torch.int32, "block_table"), n_slots, n_layers, mbps, layer,
+        _dev(slot_ids, torch.int32, "slot_ids"), _dev(kv_lens, torch.int32, "kv_lens"),
+        _dev(q_start, torch.int32, "q_start"), B, total_q, Hq, n_kv_heads, d, float(scale),
+        int(bool(causal)), _dev(plan.plan, torch.int32, "plan"), plan.n_work, plan.n_merge,
+        _dev(workspace, None, "workspace"), ws_bytes, _dev(out, torch.bfloat16, "out"),
+        _dev(lse, torch.float32, "lse"), _dev(err, torch.int32, "err"), _stream(stream))
+    _check(rc, "attn_prefill_packed")
     return out, lse
 
 

@@ -21,7 +21,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libpagedattn.so")
 SOURCES = ["api.hip", "scatter.hip", "append.hip", "decode.hip", "prefill.hip", "backward.hip",
-           "clock.hip"]
+           "clock.hip", "packed.hip"]
 ARCH = "gfx950"
 
 

@@ -143,6 +143,55 @@ int attn_prefill_chunk(const void *q, const void *kv_cache, int64_t n_pages,
                         O, LSE, err, stream);
 }
 
+int attn_prefill_packed_plan(const int32_t *q_lens, const int32_t *kv_lens, int B, int Hq, int Hkv,
+                             int head_dim, int causal, int32_t *plan, int64_t plan_capacity,
+                             int64_t *n_work, int64_t *n_merge, size_t *workspace_bytes) {
+  if (!n_work || !n_merge || !workspace_bytes) return PA_ERR_NULL;
+  *n_work = 0;
+  *n_merge = 0;
+  *workspace_bytes = 0;
+  if (B < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || plan_capacity < 0) return PA_ERR_SHAPE;
+  if (!supported_head_dim(head_dim)) return PA_ERR_UNSUPPORTED;
+  const int G = Hq / Hkv;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return PA_ERR_UNSUPPORTED;
+  if (B == 0) return PA_OK;
+  if (!q_lens || !kv_lens) return PA_ERR_NULL;
+  return pa::plan_prefill_packed(q_lens, kv_lens, B, Hq, Hkv, head_dim, causal ? 1 : 0,
+                                 pa::device_cu_count(), plan, plan_capacity, n_work, n_merge,
+                                 workspace_bytes);
+}
+
+int attn_prefill_packed(const void *q, const void *kv_cache, int64_t n_pages,
+                        const int32_t *block_table, int n_slots, int n_layers,
+                        int max_blocks_per_seq, int layer, const int32_t *slot_ids,
+                        const int32_t *kv_lens, const int32_t *q_start, int B, int64_t total_q,
+                        int Hq, int Hkv, int head_dim, float scale, int causal,
+                        const int32_t *plan, int64_t n_work, int64_t n_merge, void *workspace,
+                        size_t workspace_bytes, void *O, float *LSE, int32_t *err, void *stream) {
+  if (B < 0 || total_q < 0 || n_work < 0 || n_merge < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0)
+    return PA_ERR_SHAPE;
+  if (!supported_head_dim(head_dim)) return PA_ERR_UNSUPPORTED;
+  const int G = Hq / Hkv;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return PA_ERR_UNSUPPORTED;
+  if (!valid_scale(scale)) return PA_ERR_VALUE;
+  int rc = check_cache(kv_cache, n_pages, block_table, n_slots, n_layers, max_blocks_per_seq, layer,
+                       Hkv, head_dim);
+  if (rc != PA_OK) return rc;
+  if (B == 0 || total_q == 0 || n_work == 0) return PA_OK;
+  if (!q || !kv_lens || !q_start || !plan || !O || !LSE) return PA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(O)) return PA_ERR_ALIGN;
+  if (n_merge > 0 && !workspace) return PA_ERR_NULL;
+  if (workspace && !aligned16(workspace)) return PA_ERR_ALIGN;
+  if (total_q > INT64_MAX / ((int64_t)Hq * head_dim * 2)) return PA_ERR_RANGE;
+  const int64_t tile_bytes = (int64_t)pa::prefill_rows_per_block(G) * pa::prefill_heads_per_block(G) *
+                             (head_dim + 1) * 4;
+  const int64_t n_part_slots = workspace ? (int64_t)(workspace_bytes / tile_bytes) : 0;
+  return pa::launch_prefill_packed(q, kv_cache, n_pages, block_table, n_slots, n_layers,
+                                   max_blocks_per_seq, layer, slot_ids, kv_lens, q_start, B, total_q,
+                                   Hq, Hkv, head_dim, scale, causal, plan, n_work, n_merge, workspace,
+                                   n_part_slots, O, LSE, err, static_cast<hipStream_t>(stream));
+}
+
 size_t attn_decode_workspace_size(int B, int Hq, int Hkv, int head_dim, int max_ctx) {
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || head_dim <= 0 || max_ctx < 0) return 0;
   return pa::decode_workspace_bytes(B, Hq, Hkv, head_dim, max_ctx);

@@ -7,6 +7,21 @@
 
 namespace pa {
 
+// packed prefill: work list (host), prefill launch and merge of split row blocks
+int prefill_rows_per_block(int G);
+int prefill_heads_per_block(int G);
+int plan_prefill_packed(const int32_t *q_lens, const int32_t *kv_lens, int B, int Hq, int Hkv, int D,
+                        int causal, int n_cu, int32_t *plan, int64_t capacity, int64_t *n_work,
+                        int64_t *n_merge, size_t *part_bytes);
+int launch_prefill_packed(const void *q, const void *kv_cache, int64_t n_pages,
+                          const int32_t *block_table, int n_slots, int n_layers, int mbps, int layer,
+                          const int32_t *slot_ids, const int32_t *kv_lens, const int32_t *q_start, int B,
+                          int64_t total_q, int Hq, int Hkv, int D, float scale, int causal,
+                          const int32_t *plan, int64_t n_work, int64_t n_merge, void *part,
+                          int64_t n_part_slots, void *O, float *LSE, int32_t *err, hipStream_t stream);
+int launch_packed_merge(const int32_t *merge, int64_t n_merge, const int32_t *q_start, int B,
+                        const float *part, int64_t n_part_slots, void *O, float *LSE, int32_t *err,
+                        int64_t total_q, int Hq, int Hkv, int D, hipStream_t stream);
 int launch_clock_probe(float *ghz, int n_waves, int iters, hipStream_t stream);
 int launch_kv_scatter(const void *k, const void *v, int64_t n_tokens, const int32_t *slot_ids,
                       const int32_t *positions, void *kv_cache, int64_t n_pages,

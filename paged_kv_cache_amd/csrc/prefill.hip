@@ -75,9 +75,19 @@ struct PrefillArgs {
   int n_hgroups;               // head groups per sequence
   int n_rowblocks;             // query tiles per sequence
   int layer_ranks;             // query-tile ranks per layer of one workgroup per CU
-  uint16_t *O;                 // [B][T][Hq][D]
-  float *LSE;                  // [B][Hq][T]
+  uint16_t *O;                 // [B][T][Hq][D]  (packed: [total_q][Hq][D])
+  float *LSE;                  // [B][Hq][T]     (packed: [total_q][Hq])
   int32_t *err;
+  // packed rows (attn_prefill_packed): sequence b's queries are rows
+  // q_start[b] .. q_start[b+1]-1 of q, O and LSE; workgroup i runs work item
+  // work[6i..6i+5] = (b, row block, head group, first key tile, end key tile,
+  // partial slot or -1); a split row block leaves its partial tile (O
+  // normalised, then LSE, fp32) in part for the merge kernel.
+  const int32_t *q_start;
+  const int32_t *work;
+  float *part;
+  int64_t total_q;
+  int64_t n_part_slots;        // partial tiles the workspace holds
 };
 
 }  // namespace
@@ -94,8 +104,9 @@ struct Swz {
   __device__ static int v(int key) { return 4 * ((key / (128 / D)) % (D / 32)); }
 };
 
-template <int D, int G, bool PAGED, int NS, int OCC>
+template <int D, int G, bool PAGED, int NS, int OCC, bool PACKED>
 __global__ __launch_bounds__(64 * kBlocks, OCC) void prefill_kernel(PrefillArgs a) {
+  static_assert(PAGED || !PACKED, "packed rows are read through the block table");
   constexpr int NW = kBlocks;                      // waves per workgroup, one block each
   constexpr int HW = G < kBlocks ? G : kBlocks;    // heads per workgroup
   constexpr int RW = kBlocks / HW;                 // 32-row blocks per workgroup
@@ -152,8 +163,23 @@ __global__ __launch_bounds__(64 * kBlocks, OCC) void prefill_kernel(PrefillArgs 
   // ---- workgroup -> (sequence, head group, query tile)
   const int n_pairs = a.B * a.n_hgroups;
   const int wg = blockIdx.x;
-  int pair, rank;
-  if ((n_pairs & 7) == 0) {
+  int pair = 0, rank = 0;
+  int item_t0 = 0, item_t1 = 0x7fffffff, slot = -1;   // key tiles and partial slot (packed)
+  if constexpr (PACKED) {
+    const int32_t *it = a.work + 6 * (int64_t)wg;
+    pair = it[0] * a.n_hgroups + it[2];
+    rank = it[1];
+    item_t0 = it[3];
+    item_t1 = it[4];
+    slot = it[5];
+    // a work item naming no row block of this batch, or a slot past the
+    // workspace: flagged, nothing read or written
+    if (it[0] < 0 || it[0] >= a.B || it[2] < 0 || it[2] >= a.n_hgroups || rank < 0 || item_t0 < 0 ||
+        item_t1 < item_t0 || slot < -1 || slot >= a.n_part_slots) {
+      if (threadIdx.x == 0) raise_err(a.err, PA_DEVERR_BAD_PLAN);
+      return;
+    }
+  } else if ((n_pairs & 7) == 0) {
     const int ppx = n_pairs >> 3;
     const int k8 = wg >> 3;
     rank = k8 / ppx;
@@ -162,7 +188,7 @@ __global__ __launch_bounds__(64 * kBlocks, OCC) void prefill_kernel(PrefillArgs 
     rank = wg / n_pairs;
     pair = wg % n_pairs;
   }
-  if (a.causal && a.layer_ranks > 1) {
+  if (!PACKED && a.causal && a.layer_ranks > 1) {
     // Workgroups are dispatched in id order, one per CU at a time, so the
     // ids fill the CUs in layers.  Causal tiles are taken longest first,
     // snaking over the layers (odd layers in reverse), so that the tiles
@@ -171,7 +197,7 @@ __global__ __launch_bounds__(64 * kBlocks, OCC) void prefill_kernel(PrefillArgs 
     const int layer = rank / L, pos = rank % L;
     if (layer & 1) rank = layer * L + (min(L, a.n_rowblocks - layer * L) - 1 - pos);
   }
-  const int rb = a.causal ? a.n_rowblocks - 1 - rank : rank;
+  const int rb = (a.causal && !PACKED) ? a.n_rowblocks - 1 - rank : rank;
   const int b = pair / a.n_hgroups;
   const int hg = pair % a.n_hgroups;
   const int Hq = a.Hkv * G;
@@ -184,6 +210,7 @@ __global__ __launch_bounds__(64 * kBlocks, OCC) void prefill_kernel(PrefillArgs 
 
   int len = T;    // keys of this sequence (its cached tokens)
   int qlen = T;   // its query rows: the last qlen of its len tokens
+  int64_t qstart = 0;   // packed: row of q / O / LSE holding its query row 0
   // Errors are collected here and reported once at the end.
   int err_bits = 0;
   const int64_t page_bytes = 2LL * kPageTokens * a.Hkv * ROWB;
@@ -193,14 +220,24 @@ __global__ __launch_bounds__(64 * kBlocks, OCC) void prefill_kernel(PrefillArgs 
   if constexpr (PAGED) {
     const bool reporter = hg == 0 && rb == 0;   // one workgroup per sequence reports
     len = a.seq_lens[b];
-    if (len < 0 || (!a.q_lens && len > T)) {
+    if (len < 0 || (!PACKED && !a.q_lens && len > T)) {
       if (reporter) err_bits |= PA_DEVERR_BAD_POS;
       len = len < 0 ? 0 : T;
     }
-    qlen = a.q_lens ? a.q_lens[b] : len;
-    if (qlen < 0 || qlen > T || qlen > len) {
+    if constexpr (PACKED) {
+      const int64_t s0 = a.q_start[b], s1 = a.q_start[b + 1];
+      qstart = s0;
+      qlen = (s0 < 0 || s1 < s0 || s1 > a.total_q) ? -1 : (int)min(s1 - s0, (int64_t)0x7fffffff);
+      if (qlen < 0) {
+        if (reporter) err_bits |= PA_DEVERR_BAD_POS;
+        qlen = 0;
+      }
+    } else {
+      qlen = a.q_lens ? a.q_lens[b] : len;
+    }
+    if (qlen < 0 || (!PACKED && qlen > T) || qlen > len) {
       if (reporter) err_bits |= PA_DEVERR_BAD_POS;
-      qlen = qlen < 0 ? 0 : min(min(qlen, T), len);
+      qlen = qlen < 0 ? 0 : min(PACKED ? qlen : min(qlen, T), len);
     }
     const int slot = a.slot_ids ? a.slot_ids[b] : b;
     if (slot < 0 || slot >= a.n_slots) {
@@ -225,6 +262,26 @@ __global__ __launch_bounds__(64 * kBlocks, OCC) void prefill_kernel(PrefillArgs 
   const int wg_row_end = min(rb * BM + BM, qlen);
   const int kv_end = a.causal ? off + wg_row_end : len;   // keys past this are never visible here
   const int n_tiles = (kv_end > 0 && rb * BM < qlen) ? (kv_end + kBN - 1) / kBN : 0;
+  // key tiles of this workgroup: all of them, or (packed) the work item's share
+  const int t_begin = PACKED ? min(item_t0, n_tiles) : 0;
+  const int t_end = PACKED ? (slot < 0 ? n_tiles : min(item_t1, n_tiles)) : n_tiles;
+  // a partial tile: O (normalised), then LSE, of BM rows x HW heads
+  float *const part = PACKED && slot >= 0 ? a.part + (int64_t)slot * (BM * HW * (D + 1)) : nullptr;
+  if constexpr (PACKED) {
+    if (t_begin >= t_end) {
+      // nothing to attend (a row block past the query rows, or a split past
+      // the keys): an empty partial if one is expected, else nothing (packed
+      // rows past a sequence's length do not exist)
+      if (err_bits && tid == 0) raise_err(a.err, err_bits);
+      if (part) {
+        const int r = 32 * (wave / HW) + lr, h = wave % HW;
+        float *op = part + (r * HW + h) * D;
+        for (int d = lh; d < D; d += 2) op[d] = 0.f;
+        if (lh == 0) part[BM * HW * D + r * HW + h] = -INFINITY;
+      }
+      return;
+    }
+  }
   if (n_tiles == 0) {
     // every row of this workgroup is padding (rows past the query length of a
     // short sequence in a padded batch): O = 0, LSE = -inf, nothing else
@@ -252,8 +309,8 @@ __global__ __launch_bounds__(64 * kBlocks, OCC) void prefill_kernel(PrefillArgs 
   // scores finite.  (Unconditional loads: no wait between them.)
   bf16x8 qf[D / 16];
   {
-    const bf16x8 *qp = reinterpret_cast<const bf16x8 *>(
-        a.q + (((int64_t)b * T + (row < qlen ? row : 0)) * Hq + head) * D + lh * (D / 2));
+    const int64_t qrow = PACKED ? qstart + (row < qlen ? row : 0) : (int64_t)b * T + (row < qlen ? row : 0);
+    const bf16x8 *qp = reinterpret_cast<const bf16x8 *>(a.q + (qrow * Hq + head) * D + lh * (D / 2));
 #pragma unroll
     for (int k = 0; k < D / 16; ++k) qf[k] = qp[k];
   }
@@ -268,7 +325,7 @@ __global__ __launch_bounds__(64 * kBlocks, OCC) void prefill_kernel(PrefillArgs 
   if constexpr (PAGED) {
 #pragma unroll
     for (int pp = 0; pp < PPW; ++pp) {
-      const int blk = lane * (kBN / kPageTokens) + wave * PPW + pp;
+      const int blk = (64 * (t_begin >> 6) + lane) * (kBN / kPageTokens) + wave * PPW + pp;
       raw0[pp] = blk < nblk ? trow_v[blk] : -1;
     }
     bool found = false;
@@ -589,23 +646,25 @@ __global__ __launch_bounds__(64 * kBlocks, OCC) void prefill_kernel(PrefillArgs 
   // block-table reads above are in flight together until here.)
 #pragma unroll
   for (int k = 0; k < D / 16; ++k) asm("" : "+v"(qf[k]));
-  if (n_tiles > 0) {
-    if constexpr (PAGED) window_set(0, raw0);
-    fetch(0, std::integral_constant<int, 0>{});
-    if constexpr (NS > 2) fetch(1, std::integral_constant<int, 1>{});
-    if constexpr (NS > 3) fetch(2, std::integral_constant<int, 2>{});
-    for (int t = 0;;) {
+  // (stages are numbered from the first tile of the range: tile t_begin + j
+  // lives in stage j % NS)
+  if (t_end > t_begin) {
+    if constexpr (PAGED) window_set(t_begin >> 6, raw0);
+    fetch(t_begin, std::integral_constant<int, 0>{});
+    if constexpr (NS > 2) fetch(t_begin + 1, std::integral_constant<int, 1>{});
+    if constexpr (NS > 3) fetch(t_begin + 2, std::integral_constant<int, 2>{});
+    for (int t = t_begin;;) {
       step(t, std::integral_constant<int, 0>{});
-      if (++t >= n_tiles) break;
+      if (++t >= t_end) break;
       step(t, std::integral_constant<int, 1 % NS>{});
-      if (++t >= n_tiles) break;
+      if (++t >= t_end) break;
       if constexpr (NS > 2) {
         step(t, std::integral_constant<int, 2 % NS>{});
-        if (++t >= n_tiles) break;
+        if (++t >= t_end) break;
       }
       if constexpr (NS > 3) {
         step(t, std::integral_constant<int, 3 % NS>{});
-        if (++t >= n_tiles) break;
+        if (++t >= t_end) break;
       }
     }
     // no transfer may still be writing LDS when the workgroup ends
@@ -625,8 +684,31 @@ __global__ __launch_bounds__(64 * kBlocks, OCC) void prefill_kernel(PrefillArgs 
     const float l_row = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
     const bool has = row < qlen && l_row > 0.f;
     const float inv_l = has ? 1.f / l_row : 0.f;
-    if (row < T && lh == 0)
-      a.LSE[((int64_t)b * Hq + head) * T + row] = has ? (m_run + fast_log2(l_row)) * kLn2 : -INFINITY;
+    const float lse_row = has ? (m_run + fast_log2(l_row)) * kLn2 : -INFINITY;
+    if constexpr (PACKED) {
+      if (part) {
+        // a split row block: this wave's 32 rows x 1 head, straight from the
+        // registers (row r = 32*(wave/HW) + lr of the tile, head wave % HW)
+        const int r = 32 * (wave / HW) + lr, h = wave % HW;
+        float *op = part + (r * HW + h) * D;
+#pragma unroll
+        for (int mb = 0; mb < D / 32; ++mb)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            float4 v;
+            v.x = acc[mb][4 * g + 0] * inv_l;
+            v.y = acc[mb][4 * g + 1] * inv_l;
+            v.z = acc[mb][4 * g + 2] * inv_l;
+            v.w = acc[mb][4 * g + 3] * inv_l;
+            *reinterpret_cast<float4 *>(op + mb * 32 + 8 * g + 4 * lh) = v;
+          }
+        if (lh == 0) part[BM * HW * D + r * HW + h] = lse_row;
+        return;
+      }
+      if (row < qlen && lh == 0) a.LSE[(qstart + row) * Hq + head] = lse_row;
+    } else {
+      if (row < T && lh == 0) a.LSE[((int64_t)b * Hq + head) * T + row] = lse_row;
+    }
     constexpr int RB = HW * ROWB;   // bytes of one staged row
     constexpr int RC = RB / 16;     // its 16-byte chunks (chunk c sits at c ^ (row % 8))
     static_assert(RC % 8 == 0 && BM * RB == 2 * TILEB, "O tile = one ring stage");
@@ -647,9 +729,10 @@ __global__ __launch_bounds__(64 * kBlocks, OCC) void prefill_kernel(PrefillArgs 
         }
     }
     __syncthreads();
-    const int rows = min(BM, T - rb * BM);   // staged rows inside O
+    const int rows = min(BM, (PACKED ? qlen : T) - rb * BM);   // staged rows inside O
     const int64_t row_stride = (int64_t)Hq * ROWB;
-    uint8_t *obase = reinterpret_cast<uint8_t *>(a.O) + (((int64_t)b * T + rb * BM) * Hq + hg * HW) * ROWB;
+    const int64_t orow0 = PACKED ? qstart + rb * BM : (int64_t)b * T + rb * BM;
+    uint8_t *obase = reinterpret_cast<uint8_t *>(a.O) + (orow0 * Hq + hg * HW) * ROWB;
     const int64_t span = (int64_t)(rows - 1) * row_stride + RB;
     const __amdgpu_buffer_rsrc_t rs =
         __builtin_amdgcn_make_buffer_rsrc(obase, (short)0, (int)min(span, (int64_t)0x7fffffff), 0x00020000);
@@ -685,8 +768,20 @@ static int launch_prefill_t(PrefillArgs a, hipStream_t stream) {
   const int64_t grid = (int64_t)a.B * a.n_hgroups * a.n_rowblocks;
   if (grid == 0) return PA_OK;
   if (grid > 0x7fffffff) return PA_ERR_RANGE;
-  hipLaunchKernelGGL((prefill_kernel<D, G, PAGED, C::NS, C::OCC>), dim3((unsigned)grid), dim3(64 * kBlocks), 0,
-                     stream, a);
+  hipLaunchKernelGGL((prefill_kernel<D, G, PAGED, C::NS, C::OCC, false>), dim3((unsigned)grid),
+                     dim3(64 * kBlocks), 0, stream, a);
+  return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
+template <int D, int G>
+static int launch_prefill_packed_t(PrefillArgs a, int64_t n_work, hipStream_t stream) {
+  using C = PrefillCfg<D>;
+  constexpr int HW = G < kBlocks ? G : kBlocks;
+  a.n_hgroups = a.Hkv * G / HW;
+  if (n_work <= 0) return PA_OK;
+  if (n_work > 0x7fffffffLL) return PA_ERR_RANGE;
+  hipLaunchKernelGGL((prefill_kernel<D, G, true, C::NS, C::OCC, true>), dim3((unsigned)n_work),
+                     dim3(64 * kBlocks), 0, stream, a);
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
 
@@ -732,6 +827,54 @@ int launch_prefill_paged(const void *q, const void *kv_cache, int64_t n_pages,
   a.LSE = LSE;
   a.err = err;
   return dispatch_prefill<true>(a, D, Hq / Hkv, stream);
+}
+
+int launch_prefill_packed(const void *q, const void *kv_cache, int64_t n_pages,
+                          const int32_t *block_table, int n_slots, int n_layers, int mbps, int layer,
+                          const int32_t *slot_ids, const int32_t *kv_lens, const int32_t *q_start, int B,
+                          int64_t total_q, int Hq, int Hkv, int D, float scale, int causal,
+                          const int32_t *plan, int64_t n_work, int64_t n_merge, void *part,
+                          int64_t n_part_slots, void *O, float *LSE, int32_t *err, hipStream_t stream) {
+  PrefillArgs a{};
+  a.q = static_cast<const uint16_t *>(q);
+  a.pool = static_cast<const uint8_t *>(kv_cache);
+  a.n_pages = n_pages;
+  a.block_table = block_table;
+  a.slot_ids = slot_ids;
+  a.seq_lens = kv_lens;
+  a.n_slots = n_slots;
+  a.n_layers = n_layers;
+  a.mbps = mbps;
+  a.layer = layer;
+  a.B = B;
+  a.T = 0;
+  a.Hkv = Hkv;
+  a.scale_log2 = scale * kLog2e;
+  a.causal = causal ? 1 : 0;
+  a.O = static_cast<uint16_t *>(O);
+  a.LSE = LSE;
+  a.err = err;
+  a.q_start = q_start;
+  a.work = plan;
+  a.part = static_cast<float *>(part);
+  a.total_q = total_q;
+  a.n_part_slots = n_part_slots;
+  const int G = Hq / Hkv;
+  int rc = PA_ERR_UNSUPPORTED;
+#define PA_PACKED_CASE(DD, GG) \
+  if (D == DD && G == GG) rc = launch_prefill_packed_t<DD, GG>(a, n_work, stream);
+  PA_PACKED_CASE(64, 1)
+  PA_PACKED_CASE(64, 2)
+  PA_PACKED_CASE(64, 4)
+  PA_PACKED_CASE(64, 8)
+  PA_PACKED_CASE(128, 1)
+  PA_PACKED_CASE(128, 2)
+  PA_PACKED_CASE(128, 4)
+  PA_PACKED_CASE(128, 8)
+#undef PA_PACKED_CASE
+  if (rc != PA_OK) return rc;
+  return launch_packed_merge(plan + 6 * n_work, n_merge, q_start, B, static_cast<const float *>(part),
+                             n_part_slots, O, LSE, err, total_q, Hq, Hkv, D, stream);
 }
 
 int launch_prefill_dense(const void *q, const void *k, const void *v, int B, int T, int Hq, int Hkv,
