@@ -12,7 +12,8 @@
 // a chunk row block after a long prefix sees many more key tiles than one
 // near the start of a prompt.  The planner cuts every row block into pieces
 // of at most the even share of the batch's key tiles per CU (at least
-// kMinSplitTiles tiles), so that no row block outlasts the rest by more than
+// kMinSplitTiles tiles; a narrow row block, whose HW heads one wave computes,
+// counts 1/HW of its tiles), so that no row block outlasts the rest by more than
 // a share; each piece is a work item of its own, and the pieces of one row
 // block leave partial results (O normalised, LSE) that the merge kernel
 // combines by the log-sum-exp rule (tiny-vllm part 3, "causalMask and online
@@ -76,7 +77,10 @@ int plan_prefill_packed(const int32_t *q_lens, const int32_t *kv_lens, int B, in
       const int nt = (kv_end + kTileKeys - 1) / kTileKeys;
       if (nt == 0) continue;
       for (int hg = 0; hg < n_hgroups; ++hg) tiles.push_back({b, rb, hg, nt});
-      total += (int64_t)nt * n_hgroups;
+      // (a narrow row block -- rows that fit one wave as HW heads x 32/HW
+      // rows -- computes with one of its HW waves: it counts 1/HW)
+      const bool narrow = HW > 1 && row_end - rb * BM <= 32 / HW;
+      total += (int64_t)nt * n_hgroups / (narrow ? HW : 1);
     }
   }
   // pieces per row block: at most the even share of key tiles per CU

@@ -299,8 +299,17 @@ __global__ __launch_bounds__(64 * kBlocks, OCC) void prefill_kernel(PrefillArgs 
     return;
   }
   const int nblk = (kv_end + kPageTokens - 1) / kPageTokens;   // blocks read (paged)
-  // last key this lane's row may see (-1: padding row, sees nothing)
-  const int row = row0 + lr;
+  // A narrow row block (packed; a decode row, a short chunk tail): its rows
+  // fit the 32 columns of one wave as HW heads x NR rows (column lr is head
+  // lr / NR, row lr % NR).  Wave 0 then computes every head of the block and
+  // the other waves only fetch their share of each tile, so a decode row costs
+  // one wave's products per key tile instead of HW waves' with a single row.
+  constexpr int NR = 32 / HW;
+  const bool narrow = PACKED && HW > 1 && qlen - rb * BM <= NR;
+  // this lane's query row and head; the last key its row may see (-1: a
+  // padding row, sees nothing)
+  const int row = narrow ? rb * BM + lr % NR : row0 + lr;
+  const int head_l = narrow ? hg * HW + lr / NR : head;
   const int lim = row < qlen ? (a.causal ? off + row : len - 1) : -1;
 
   // ---- Q^T as B operands: lane holds row row0 + lr, d = lh*(D/2) + k*8 + e
@@ -310,7 +319,7 @@ __global__ __launch_bounds__(64 * kBlocks, OCC) void prefill_kernel(PrefillArgs 
   bf16x8 qf[D / 16];
   {
     const int64_t qrow = PACKED ? qstart + (row < qlen ? row : 0) : (int64_t)b * T + (row < qlen ? row : 0);
-    const bf16x8 *qp = reinterpret_cast<const bf16x8 *>(a.q + (qrow * Hq + head) * D + lh * (D / 2));
+    const bf16x8 *qp = reinterpret_cast<const bf16x8 *>(a.q + (qrow * Hq + head_l) * D + lh * (D / 2));
 #pragma unroll
     for (int k = 0; k < D / 16; ++k) qf[k] = qp[k];
   }
@@ -630,7 +639,8 @@ __global__ __launch_bounds__(64 * kBlocks, OCC) void prefill_kernel(PrefillArgs 
   // one constant wait is exact; the compiler's own bookkeeping then agrees
   // and adds no drain of its own.
   // last tile this wave's rows see (causal): later tiles are skipped
-  const int t_last = a.causal ? (off + wave_row_end) / kBN : 0x7fffffff;
+  const int t_last = narrow ? (wave != 0 ? -1 : a.causal ? (off + rb * BM + NR - 1) / kBN : 0x7fffffff)
+                            : (a.causal ? (off + wave_row_end) / kBN : 0x7fffffff);
   auto skip = [&](int t) { return t > t_last; };
   auto step = [&](int t, auto S_) {
     constexpr int S = decltype(S_)::value;
@@ -686,6 +696,38 @@ __global__ __launch_bounds__(64 * kBlocks, OCC) void prefill_kernel(PrefillArgs 
     const float inv_l = has ? 1.f / l_row : 0.f;
     const float lse_row = has ? (m_run + fast_log2(l_row)) * kLn2 : -INFINITY;
     if constexpr (PACKED) {
+      if (narrow) {
+        // wave 0 holds every row of the block: O (or the partial) straight
+        // from its registers, row lr % NR of the block, head lr / NR
+        if (wave != 0) return;
+        const int r = lr % NR, h = lr / NR;
+        if (part) {
+          float *op = part + (r * HW + h) * D;
+#pragma unroll
+          for (int mb = 0; mb < D / 32; ++mb)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+              float4 v;
+              v.x = acc[mb][4 * g + 0] * inv_l;
+              v.y = acc[mb][4 * g + 1] * inv_l;
+              v.z = acc[mb][4 * g + 2] * inv_l;
+              v.w = acc[mb][4 * g + 3] * inv_l;
+              *reinterpret_cast<float4 *>(op + mb * 32 + 8 * g + 4 * lh) = v;
+            }
+          if (lh == 0) part[BM * HW * D + r * HW + h] = lse_row;
+        } else if (row < qlen) {
+          uint16_t *op = a.O + ((qstart + row) * Hq + head_l) * D;
+#pragma unroll
+          for (int mb = 0; mb < D / 32; ++mb)
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+              *reinterpret_cast<uint2 *>(op + mb * 32 + 8 * g + 4 * lh) =
+                  make_uint2(pack_bf16x2(acc[mb][4 * g + 0] * inv_l, acc[mb][4 * g + 1] * inv_l),
+                             pack_bf16x2(acc[mb][4 * g + 2] * inv_l, acc[mb][4 * g + 3] * inv_l));
+          if (lh == 0) a.LSE[(qstart + row) * Hq + head_l] = lse_row;
+        }
+        return;
+      }
       if (part) {
         // a split row block: this wave's 32 rows x 1 head, straight from the
         // registers (row r = 32*(wave/HW) + lr of the tile, head wave % HW)

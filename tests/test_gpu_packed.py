@@ -81,6 +81,19 @@ def test_packed_split_pieces_past_one_window(Hq, Hkv, d, causal):
     assert plan.n_merge > 0 and (items[:, 3] >= 64).any() and (items[:, 3] % 64 != 0).any()
 
 
+@pytest.mark.parametrize("Hq,Hkv,d", [(32, 8, 64), (16, 8, 128), (8, 1, 64), (8, 8, 64)])
+@pytest.mark.parametrize("causal", [True, False])
+def test_packed_narrow_row_blocks_split(Hq, Hkv, d, causal):
+    """Decode rows and short row-block tails (at most 32/HW rows: one wave holds
+    every head of the block) after long contexts, cut into many pieces (little
+    other work, so the share per CU is small) and merged: every row."""
+    case = W.make_chunk("packed_narrow", B=4, Hq=Hq, Hkv=Hkv, d=d, n_pages=2048,
+                        kv_lens=[16000, 9005, 50, 4500], q_lens=[1, 5, 1, 37], seed=71 + d, causal=causal,
+                        mbps=1024)
+    _, _, _, _, plan = _parity(case)
+    assert plan.n_merge > 0
+
+
 def test_packed_missing_pages_in_later_windows():
     """A missing page in window 1 and one in window 2 under split pieces: their keys
     are left out and flagged, like the oracle does."""
