@@ -618,7 +618,9 @@ int oracle_kv_release(const int32_t *slots, int n, int32_t *block_table, int n_s
  * eQ, eK (nullable): how far dQ, dK move when D_i is taken from an output O
  * that was rounded to bf16 after a product with bf16-rounded weights, as an
  * implementation that reads the forward's O does: with
- *   E_i = 2^-9 * sum_c |dO_ic| (|O_ic| + sum_j P_ij |V_jc|)     (bound on |dD_i|)
+ *   E_i = 2^-8 * sum_c |dO_ic| (|O_ic| + sum_j P_ij |V_jc|)     (bound on |dD_i|)
+ * (2^-8: the largest relative error of rounding to bf16, whose significand
+ * holds 8 bits, applied to O itself and to every weight P_ij of its sum)
  * eQ_ic = scale E_i sum_j P_ij |K_jc| and eK_jc = scale sum_i P_ij E_i |q_ic|.
  */
 void oracle_attn_dense_backward(const uint16_t *q, const uint16_t *k, const uint16_t *v,
@@ -702,7 +704,7 @@ void oracle_attn_dense_backward(const uint16_t *q, const uint16_t *k, const uint
                     }
                     for (int c = 0; c < d; ++c)
                         E += fabs(od[c]) * (fabs(oex[c]) + pva[c]);
-                    E *= ldexp(1.0, -9);
+                    E *= ldexp(1.0, -8);
                 }
                 double *dq = dQ + (((int64_t)b * T + i) * Hq + h) * d;
                 double *aq = aQ ? aQ + (((int64_t)b * T + i) * Hq + h) * d : NULL;
