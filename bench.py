@@ -162,8 +162,8 @@ def source_digest(*names: str) -> str:
 # was taken on (digest of the .hip files), null otherwise.
 TRAFFIC = {
     # kernel: (source digest, fetched bytes, written bytes)
-    "prefill": ("10563d00c5b4b5ea", 25386061, 17301504),
-    "decode": ("6ad1bd1579d005d6", 152902681, 272928),
+    "prefill": ("69e67fbbb5d1b103", 25382733, 17301504),
+    "decode": ("c7fbbdb3a01a0cd3", 152916247, 273056),
 }
 
 
