@@ -148,7 +148,7 @@ int kv_scatter(const void *k, const void *v, int64_t n_tokens, const int32_t *sl
  *   O            [B][T][Hq][head_dim] bf16 output.
  *   LSE          [B][Hq][T] fp32 output (natural log, scaled scores).
  *   Rows t >= seq_lens[b] are written as O = 0, LSE = -INFINITY.
- *   Supported: head_dim 64 or 128, Hq/Hkv in {1, 2, 4, 8}.
+ *   Supported: head_dim 64 or 128, Hq/Hkv in {1, 2, 4, 8, 16}.
  */
 int attn_prefill(const void *q, const void *kv_cache, int64_t n_pages, const int32_t *block_table,
                  int n_slots, int n_layers, int max_blocks_per_seq, int layer,
@@ -220,7 +220,7 @@ int attn_prefill_chunk(const void *q, const void *kv_cache, int64_t n_pages,
  *   plan that does not match the lengths gives wrong rows but no access out
  *   of bounds: device-side, a length outside its range sets PA_DEVERR_BAD_POS
  *   and a work item naming no row block or a slot past the workspace sets
- *   PA_DEVERR_BAD_PLAN (the item is skipped).  Head groups 1, 2, 4, 8.
+ *   PA_DEVERR_BAD_PLAN (the item is skipped).  Head groups 1, 2, 4, 8, 16.
  */
 int attn_prefill_packed_plan(const int32_t *q_lens, const int32_t *kv_lens, int B, int Hq, int Hkv,
                              int head_dim, int causal, int32_t *plan, int64_t plan_capacity,
@@ -318,7 +318,7 @@ int attn_prefill_dense(const void *q, const void *k, const void *v, int B, int T
  *   workspace    attn_backward_workspace_size(B, T, Hq) bytes, 16-byte
  *                aligned (D of every row); contents on entry do not matter.
  *   causal, scale as for attn_prefill_dense.  Supported: head_dim 64 or 128,
- *   Hq/Hkv in {1, 2, 4, 8}.  Two launches on `stream` (dQ and the per-row D
+ *   Hq/Hkv in {1, 2, 4, 8, 16}.  Two launches on `stream` (dQ and the per-row D
  *   first, then dK and dV).
  */
 int attn_backward_dense(const void *q, const void *k, const void *v, const void *o,

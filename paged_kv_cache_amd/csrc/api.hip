@@ -153,7 +153,7 @@ int attn_prefill_packed_plan(const int32_t *q_lens, const int32_t *kv_lens, int 
   if (B < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || plan_capacity < 0) return PA_ERR_SHAPE;
   if (!supported_head_dim(head_dim)) return PA_ERR_UNSUPPORTED;
   const int G = Hq / Hkv;
-  if (G != 1 && G != 2 && G != 4 && G != 8) return PA_ERR_UNSUPPORTED;
+  if (G != 1 && G != 2 && G != 4 && G != 8 && G != 16) return PA_ERR_UNSUPPORTED;
   if (B == 0) return PA_OK;
   if (!q_lens || !kv_lens) return PA_ERR_NULL;
   return pa::plan_prefill_packed(q_lens, kv_lens, B, Hq, Hkv, head_dim, causal ? 1 : 0,
@@ -172,7 +172,7 @@ int attn_prefill_packed(const void *q, const void *kv_cache, int64_t n_pages,
     return PA_ERR_SHAPE;
   if (!supported_head_dim(head_dim)) return PA_ERR_UNSUPPORTED;
   const int G = Hq / Hkv;
-  if (G != 1 && G != 2 && G != 4 && G != 8) return PA_ERR_UNSUPPORTED;
+  if (G != 1 && G != 2 && G != 4 && G != 8 && G != 16) return PA_ERR_UNSUPPORTED;
   if (!valid_scale(scale)) return PA_ERR_VALUE;
   int rc = check_cache(kv_cache, n_pages, block_table, n_slots, n_layers, max_blocks_per_seq, layer,
                        Hkv, head_dim);
@@ -264,7 +264,7 @@ int attn_prefill_dense(const void *q, const void *k, const void *v, int B, int T
   if (B < 0 || T < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0) return PA_ERR_SHAPE;
   if (!supported_head_dim(head_dim)) return PA_ERR_UNSUPPORTED;
   const int G = Hq / Hkv;
-  if (G != 1 && G != 2 && G != 4 && G != 8) return PA_ERR_UNSUPPORTED;
+  if (G != 1 && G != 2 && G != 4 && G != 8 && G != 16) return PA_ERR_UNSUPPORTED;
   if (!valid_scale(scale)) return PA_ERR_VALUE;
   if (B == 0 || T == 0) return PA_OK;
   if (!q || !k || !v || !O || !LSE) return PA_ERR_NULL;
@@ -326,7 +326,7 @@ int attn_backward_dense(const void *q, const void *k, const void *v, const void 
   if (B < 0 || T < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0) return PA_ERR_SHAPE;
   if (!supported_head_dim(head_dim)) return PA_ERR_UNSUPPORTED;
   const int G = Hq / Hkv;
-  if (G != 1 && G != 2 && G != 4 && G != 8) return PA_ERR_UNSUPPORTED;
+  if (G != 1 && G != 2 && G != 4 && G != 8 && G != 16) return PA_ERR_UNSUPPORTED;
   if (!valid_scale(scale)) return PA_ERR_VALUE;
   if (B == 0 || T == 0) return PA_OK;
   if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !workspace) return PA_ERR_NULL;

@@ -514,10 +514,12 @@ int launch_backward_dense(const void *q, const void *k, const void *v, const voi
   PA_BWD_CASE(64, 2)
   PA_BWD_CASE(64, 4)
   PA_BWD_CASE(64, 8)
+  PA_BWD_CASE(64, 16)
   PA_BWD_CASE(128, 1)
   PA_BWD_CASE(128, 2)
   PA_BWD_CASE(128, 4)
   PA_BWD_CASE(128, 8)
+  PA_BWD_CASE(128, 16)
 #undef PA_BWD_CASE
   return PA_ERR_UNSUPPORTED;
 }

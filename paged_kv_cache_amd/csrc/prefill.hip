@@ -835,10 +835,12 @@ static int dispatch_prefill(const PrefillArgs &a, int D, int G, hipStream_t stre
   PA_PREFILL_CASE(64, 2)
   PA_PREFILL_CASE(64, 4)
   PA_PREFILL_CASE(64, 8)
+  PA_PREFILL_CASE(64, 16)
   PA_PREFILL_CASE(128, 1)
   PA_PREFILL_CASE(128, 2)
   PA_PREFILL_CASE(128, 4)
   PA_PREFILL_CASE(128, 8)
+  PA_PREFILL_CASE(128, 16)
 #undef PA_PREFILL_CASE
   return PA_ERR_UNSUPPORTED;
 }
@@ -909,10 +911,12 @@ int launch_prefill_packed(const void *q, const void *kv_cache, int64_t n_pages,
   PA_PACKED_CASE(64, 2)
   PA_PACKED_CASE(64, 4)
   PA_PACKED_CASE(64, 8)
+  PA_PACKED_CASE(64, 16)
   PA_PACKED_CASE(128, 1)
   PA_PACKED_CASE(128, 2)
   PA_PACKED_CASE(128, 4)
   PA_PACKED_CASE(128, 8)
+  PA_PACKED_CASE(128, 16)
 #undef PA_PACKED_CASE
   if (rc != PA_OK) return rc;
   return launch_packed_merge(plan + 6 * n_work, n_merge, q_start, B, static_cast<const float *>(part),

@@ -75,7 +75,7 @@ def test_backward_ragged_lengths(T, causal):
 
 
 @pytest.mark.parametrize("Hq,Hkv,d", [(4, 4, 64), (8, 1, 64), (32, 4, 64), (4, 4, 128), (8, 2, 128),
-                                      (16, 2, 128), (8, 8, 128)])
+                                      (16, 2, 128), (8, 8, 128), (32, 2, 64), (16, 1, 128)])
 @pytest.mark.parametrize("causal", [True, False])
 def test_backward_head_shapes(Hq, Hkv, d, causal):
     _parity(W.make_dense("bwd", B=2, T=200, Hq=Hq, Hkv=Hkv, d=d, causal=causal, seed=Hq + d, grad=True))

@@ -34,7 +34,7 @@ QL = [37, 64, 1, 65, 16, 1, 250, 0, 33, 129]
 
 
 @pytest.mark.parametrize("Hq,Hkv,d", [(32, 8, 64), (8, 8, 64), (16, 8, 64), (8, 1, 64),
-                                      (32, 8, 128), (16, 16, 128), (8, 1, 128)])
+                                      (32, 8, 128), (16, 16, 128), (8, 1, 128), (32, 2, 64)])
 @pytest.mark.parametrize("causal", [True, False])
 def test_chunk_ragged(Hq, Hkv, d, causal):
     n = len(KV)

@@ -52,7 +52,7 @@ QL = [37, 64, 1, 65, 16, 1, 250, 0, 33, 129]
 
 
 @pytest.mark.parametrize("Hq,Hkv,d", [(32, 8, 64), (8, 8, 64), (16, 8, 64), (8, 1, 64),
-                                      (32, 8, 128), (16, 16, 128), (8, 1, 128)])
+                                      (32, 8, 128), (16, 16, 128), (8, 1, 128), (32, 2, 64)])
 @pytest.mark.parametrize("causal", [True, False])
 def test_packed_ragged(Hq, Hkv, d, causal):
     n = len(KV)
@@ -81,7 +81,7 @@ def test_packed_split_pieces_past_one_window(Hq, Hkv, d, causal):
     assert plan.n_merge > 0 and (items[:, 3] >= 64).any() and (items[:, 3] % 64 != 0).any()
 
 
-@pytest.mark.parametrize("Hq,Hkv,d", [(32, 8, 64), (16, 8, 128), (8, 1, 64), (8, 8, 64)])
+@pytest.mark.parametrize("Hq,Hkv,d", [(32, 8, 64), (16, 8, 128), (8, 1, 64), (8, 8, 64), (32, 2, 128)])
 @pytest.mark.parametrize("causal", [True, False])
 def test_packed_narrow_row_blocks_split(Hq, Hkv, d, causal):
     """Decode rows and short row-block tails (at most 32/HW rows: one wave holds

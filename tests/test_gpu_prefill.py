@@ -30,7 +30,7 @@ def test_prefill_tiny_prompt():
     _full_parity(W.tiny_prefill())
 
 
-@pytest.mark.parametrize("Hq,Hkv", [(32, 8), (8, 8), (16, 8), (64, 8)])
+@pytest.mark.parametrize("Hq,Hkv", [(32, 8), (8, 8), (16, 8), (64, 8), (32, 2)])
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [True, False])
 def test_prefill_ragged(Hq, Hkv, d, causal):
@@ -251,7 +251,7 @@ def _dense_parity(case, rows=None):
     return O, L
 
 
-@pytest.mark.parametrize("d,H,Hkv", [(64, 8, 8), (128, 4, 4), (64, 16, 4), (128, 8, 2)])
+@pytest.mark.parametrize("d,H,Hkv", [(64, 8, 8), (128, 4, 4), (64, 16, 4), (128, 8, 2), (64, 32, 2), (128, 16, 1)])
 @pytest.mark.parametrize("causal", [True, False])
 def test_dense_small(d, H, Hkv, causal):
     _dense_parity(W.make_dense("dense", B=2, T=333, Hq=H, Hkv=Hkv, d=d, causal=causal, seed=d + H))

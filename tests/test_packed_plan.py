@@ -143,7 +143,7 @@ def test_plan_host_checks():
     assert lib.attn_prefill_packed_plan(*args(np.array([10, 60], np.int32), kv), None, 0, *refs) == -2
     assert lib.attn_prefill_packed_plan(*args(np.array([-1, 1], np.int32), kv), None, 0, *refs) == -2
     # unsupported head group, missing outputs, empty batch
-    assert lib.attn_prefill_packed_plan(ql.ctypes.data, kv.ctypes.data, 2, 32, 2, 64, 1, None, 0, *refs) == -3
+    assert lib.attn_prefill_packed_plan(ql.ctypes.data, kv.ctypes.data, 2, 64, 2, 64, 1, None, 0, *refs) == -3
     assert lib.attn_prefill_packed_plan(ql.ctypes.data, kv.ctypes.data, 2, 32, 8, 64, 1, None, 0, None, None,
                                         None) == -1
     assert lib.attn_prefill_packed_plan(None, None, 0, 32, 8, 64, 1, None, 0, *refs) == 0
