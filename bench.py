@@ -1,6 +1,6 @@
 """Benchmark of the paged attention path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--sustain S]
 
 Headline (``value``): causal prefill TFLOP/s on the Llama-3.2-1B attention
 shape -- 2 sequences x 2048 tokens, 32 q heads, 8 KV heads, head_dim 64, bf16,
@@ -40,6 +40,7 @@ import workloads as W  # noqa: E402
 
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+SUSTAIN_S = 5.0                # seconds of back-to-back steps after the timed ones (--sustain)
 DEV = torch.device("cuda")
 
 
@@ -119,6 +120,25 @@ def launch_spread(fns, n: int = 50, warmup: int = 10) -> dict:
     t = np.array([s.elapsed_time(e) * 1e3 for s, e in ev])
     return {"n": n, "median_us": round(float(np.median(t)), 2),
             "p10_us": round(float(np.percentile(t, 10)), 2), "p90_us": round(float(np.percentile(t, 90)), 2)}
+
+
+def sustained(step_fns, seconds: float, per_graph: int = 8) -> dict:
+    """The same steps replayed back to back for about `seconds` (graphs of
+    `per_graph` steps, one device sync every 16 graphs): the steady-state time
+    per step, beside the exactly-K-step timing, and a GPU busy long enough for
+    an outside sampler to see."""
+    n = len(step_fns)
+    per_graph = max(n, per_graph - per_graph % n)
+    g = capture(lambda: [step_fns[j % n]() for j in range(per_graph)])
+    warm(g, 0.1)
+    done, t0 = 0, time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(16):
+            g.replay()
+        torch.cuda.synchronize()
+        done += 16 * per_graph
+    dt = time.perf_counter() - t0
+    return {"seconds": round(dt, 2), "steps": done, "ms_per_step": round(dt / done * 1e3, 5)}
 
 
 def timed_steps(step_fns, steps: int, warmup: int, per_graph: int = 8) -> float:
@@ -208,10 +228,11 @@ def bench_prefill(steps: int, warmup: int):
     O_ref, L_ref = O.clone(), L.clone()
     wall = timed_steps([step], steps, warmup)
     assert torch.equal(O, O_ref) and torch.equal(L, L_ref), "graph replay differs from eager"
+    sus = sustained([step], SUSTAIN_S) if SUSTAIN_S > 0 else None
     flops = prefill_flops(case.B, case.T, case.Hq, case.d, True)
     alg_bytes = (q.numel() + O.numel()) * 2 + L.numel() * 4 + 2 * k.numel() * 2
     t_kernel = kernel_time(prefill)
-    return dict(case=case, wall=wall, flops=flops, t_kernel=t_kernel, clock_ghz=sustained_clock(),
+    return dict(case=case, wall=wall, flops=flops, t_kernel=t_kernel, clock_ghz=sustained_clock(), sustained=sus,
                 t_scatter=kernel_time(scatter), alg_bytes=alg_bytes, spread=launch_spread([prefill]))
 
 
@@ -277,6 +298,7 @@ def bench_decode(steps: int, warmup: int, replicas: int = 8):
     O_ref, L_ref = O.clone(), L.clone()
     wall = timed_steps([lambda r=r: step(r) for r in range(replicas)], steps, warmup)
     assert torch.equal(O, O_ref) and torch.equal(L, L_ref), "graph replay differs from eager"
+    sus = sustained([lambda r=r: step(r) for r in range(replicas)], SUSTAIN_S) if SUSTAIN_S > 0 else None
     n_ctx = int(case.ctx_lens.sum())
     kv_bytes = n_ctx * c.n_kv_heads * case.d * 2 * 2
     io_bytes = q.numel() * 2 + O.numel() * 2 + L.numel() * 4 + int(np.ceil(case.ctx_lens / 16).sum()) * 4
@@ -285,7 +307,7 @@ def bench_decode(steps: int, warmup: int, replicas: int = 8):
     # whole pages touched: ceil(ctx/16) pages of 16 tokens x all kv heads x (K, V)
     page_bytes = int(np.ceil(case.ctx_lens / 16).sum()) * 16 * c.n_kv_heads * case.d * 2 * 2
     spread = launch_spread([lambda r=r: decode(r) for r in range(replicas)])
-    return dict(case=case, wall=wall, kv_bytes=kv_bytes, io_bytes=io_bytes, t_kernel=t_kernel,
+    return dict(case=case, wall=wall, kv_bytes=kv_bytes, io_bytes=io_bytes, t_kernel=t_kernel, sustained=sus,
                 replicas=replicas, n_ctx=n_ctx, page_bytes=page_bytes, spread=spread)
 
 
@@ -724,11 +746,14 @@ def sweep(parts=SWEEP_PARTS) -> None:
 
 
 def main() -> int:
+    global SUSTAIN_S
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--sustain", type=float, default=SUSTAIN_S, metavar="S",
+                    help="seconds of back-to-back steps after the timed ones, reported as `sustained` (0: off)")
     ap.add_argument("--kernels-only", type=int, default=0, metavar="N",
                     help="launch each dominant kernel N times for a counter run; no JSON")
     ap.add_argument("--sweep", nargs="*", default=None, metavar="PART",
@@ -752,6 +777,7 @@ def main() -> int:
         sweep(tuple(args.sweep) or SWEEP_PARTS)
         return 0
 
+    SUSTAIN_S = max(0.0, args.sustain)
     p = bench_prefill(args.steps, args.warmup)
     d = bench_decode(args.steps, args.warmup)
 
@@ -794,10 +820,12 @@ def main() -> int:
                      "avg_us": round(p["t_kernel"] * 1e6, 3), "alg_bytes": p["alg_bytes"],
                      "single_launch": p["spread"], "source_digest": prefill_digest},
         "scatter_us": round(p["t_scatter"] * 1e6, 3),
+        "sustained": p["sustained"],
         "decode": {
             "metric": "decode KV-read GB/s", "unit": "GB/s",
             "value": round(d["kv_bytes"] / (d["wall"] / args.steps) / 1e9, 2),
             "ms_per_step": round(d_ms, 5),
+            "sustained": d["sustained"],
             "pct_of_hbm_peak": round(100 * d["kv_bytes"] / (d["wall"] / args.steps) / 1e9 / PEAK_HBM_GBS, 2),
             "config": {"workload": "paged decode step, 64 sequences, ctx ~ U[1, 2048]",
                        "batch": dcase.B, "ctx_tokens": d["n_ctx"], "kv_bytes": d["kv_bytes"],
