@@ -326,8 +326,9 @@ __global__ __launch_bounds__(64 * kBlocks, OCC) void prefill_kernel(PrefillArgs 
 
   // ---- pages: validated once for the whole workgroup.  A key that must not
   // count (past kv_end, or on a missing page) is fetched from a safe token
-  // instead (token 0 of the first valid block, or of pool page 0 if there is
-  // none) so that its V row stays finite; its score is masked.
+  // instead (token 0 of the first valid block the workgroup reads, or of pool
+  // page 0 if there is none) so that its V row stays finite; its score is
+  // masked.
   bool any_bad = false;
   int64_t safe_page = 0;
   int32_t raw0[PPW];   // first window of this wave's pages, read with the pass below
@@ -337,18 +338,33 @@ __global__ __launch_bounds__(64 * kBlocks, OCC) void prefill_kernel(PrefillArgs 
       const int blk = (64 * (t_begin >> 6) + lane) * (kBN / kPageTokens) + wave * PPW + pp;
       raw0[pp] = blk < nblk ? trow_v[blk] : -1;
     }
+    // the blocks of this workgroup's key tiles, 64 entries of the table per
+    // pass; a packed piece reads only its own range, four rows per pass with
+    // their loads in flight together (measured on the whole-prompt grid, the
+    // four-row pass is 1% slower there, so that one keeps a row per pass)
+    const int blk_lo = PACKED ? t_begin * (kBN / kPageTokens) : 0;
+    const int blk_hi = PACKED ? min(nblk, t_end * (kBN / kPageTokens)) : nblk;
+    constexpr int NROW = PACKED ? 4 : 1;
     bool found = false;
-    for (int b0 = 0; b0 < nblk; b0 += 64) {
-      const int blk = b0 + lane;
-      const bool in = blk < nblk;
-      const int p = in ? trow_v[blk] : 0;
-      const bool bad = in && (p < 0 || (int64_t)p >= a.n_pages);
-      const uint64_t badm = __ballot(bad);
-      const uint64_t goodm = __ballot(in && !bad);
-      if (badm) any_bad = true;
-      if (!found && goodm) {
-        safe_page = __builtin_amdgcn_readlane(p, (int)__builtin_ctzll(goodm));
-        found = true;
+    for (int b0 = blk_lo; b0 < blk_hi; b0 += 64 * NROW) {
+      int p[NROW];
+      bool in[NROW];
+#pragma unroll
+      for (int u = 0; u < NROW; ++u) {
+        const int blk = b0 + 64 * u + lane;
+        in[u] = blk < blk_hi;
+        p[u] = in[u] ? trow_v[blk] : 0;
+      }
+#pragma unroll
+      for (int u = 0; u < NROW; ++u) {
+        const bool bad = in[u] && (p[u] < 0 || (int64_t)p[u] >= a.n_pages);
+        const uint64_t badm = __ballot(bad);
+        const uint64_t goodm = __ballot(in[u] && !bad);
+        if (badm) any_bad = true;
+        if (!found && goodm) {
+          safe_page = __builtin_amdgcn_readlane(p[u], (int)__builtin_ctzll(goodm));
+          found = true;
+        }
       }
     }
     if (any_bad) err_bits |= PA_DEVERR_BAD_PAGE;
