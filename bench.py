@@ -761,7 +761,7 @@ def main() -> int:
                          + ", ".join(SWEEP_PARTS) + " (default: all)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
         return 2
     torch.cuda.set_device(0)
