@@ -182,8 +182,8 @@ def source_digest(*names: str) -> str:
 # was taken on (digest of the .hip files), null otherwise.
 TRAFFIC = {
     # kernel: (source digest, fetched bytes, written bytes)
-    "prefill": ("69e67fbbb5d1b103", 25382733, 17301504),
-    "decode": ("c7fbbdb3a01a0cd3", 152916247, 273056),
+    "prefill": ("ea1991cd164bd473", 25385805, 17301504),
+    "decode": ("c7fbbdb3a01a0cd3", 152910232, 272800),
 }
 
 
