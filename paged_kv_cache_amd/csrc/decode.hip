@@ -6,8 +6,9 @@
 // added).
 //
 // Work split.  A workgroup of kWaves wavefronts owns (sequence b, kv head,
-// cross-split of the context); its wavefronts take interleaved 32-token chunks
-// and merge their partial results through LDS at the end.  Only when the
+// cross-split of the context); its wavefronts take interleaved chunks (two
+// pages at d=64, one page at d=128: 8 KB of K and V either way) and merge
+// their partial results through LDS at the end.  Only when the
 // batch is too small to fill the GPU (few long sequences) is a context also
 // split across workgroups, whose partials a small second kernel merges.
 //
@@ -19,6 +20,9 @@
 //
 //   S^T[16 tok][16 col] = K[16 tok][32 d] x Q^T[32 d][16 col]
 //   O^T[16 d][16 col]  += V^T[16 d][32 tok] x P^T[32 tok][16 col]
+//
+// (d=128 takes one-page chunks, and its second product contracts over the 16
+// tokens of the page on v_mfma_f32_16x16x16_bf16.)
 //
 // Column c carries q head (c mod G) of the group (columns repeat when G < 16).
 // K rows go straight from the page into the A operand with 16-byte loads:
@@ -51,7 +55,7 @@ namespace pa {
 
 namespace {
 
-constexpr int kChunk = 32;             // tokens per wavefront step (two pages)
+constexpr int kChunk = 32;             // split granularity in tokens (a whole number of chunks)
 #ifndef PA_DECODE_WAVES
 #define PA_DECODE_WAVES 8
 #endif
@@ -106,11 +110,11 @@ __device__ __forceinline__ float rows_sum(float x) {
   return __uint_as_float(q[0]) + __uint_as_float(q[1]);
 }
 
-template <int D>
+template <int D, int NH>
 struct Chunk {
-  u32x4 k[2][D / 32];   // [16-token half][16-byte piece]
-  u32x4 v[2][D / 32];
-  bool ok[2];           // the half's page exists
+  u32x4 k[NH][D / 32];   // [16-token half][16-byte piece]
+  u32x4 v[NH][D / 32];
+  bool ok[NH];           // the half's page exists
 };
 
 // Context length actually used for sequence b: bad lengths and slots are
@@ -139,7 +143,11 @@ __global__ __launch_bounds__(64 * kWaves, PA_DECODE_MIN_WAVES_PER_SIMD) void dec
   static_assert(D % 32 == 0 && 16 % G == 0, "unsupported shape");
   constexpr int P = D / 32;          // 16-byte pieces per lane per token row
   constexpr int CH = D / 8;          // 16-byte chunks per V row
-  __shared__ __attribute__((aligned(16))) uint16_t vl[kWaves][kChunk * D];
+  // tokens per chunk: two pages at d=64, one at d=128 (the same bytes, so the
+  // same registers per chunk in flight)
+  constexpr int NH = D == 128 ? 1 : 2;
+  constexpr int CT = 16 * NH;
+  __shared__ __attribute__((aligned(16))) uint16_t vl[kWaves][CT * D];
   __shared__ float red_o[kWaves][G][D];
   __shared__ float red_m[kWaves][G];
   __shared__ float red_l[kWaves][G];
@@ -240,9 +248,9 @@ __global__ __launch_bounds__(64 * kWaves, PA_DECODE_MIN_WAVES_PER_SIMD) void dec
   uint16_t *vw = vl[w];
 
   // ---- this wavefront's steps: step i covers the kSub chunks from token
-  // t_begin + (w + kWaves*i)*kChunk*kSub
-  const int stride = kWaves * kChunk * kSub;
-  const int first_tok = t_begin + w * kChunk * kSub;
+  // t_begin + (w + kWaves*i)*CT*kSub
+  const int stride = kWaves * CT * kSub;
+  const int first_tok = t_begin + w * CT * kSub;
   const int n_my = first_tok < t_end ? (t_end - first_tok + stride - 1) / stride : 0;
   // block-table row read through the constant address space: a uniform
   // entry is then always a scalar load
@@ -257,9 +265,9 @@ __global__ __launch_bounds__(64 * kWaves, PA_DECODE_MIN_WAVES_PER_SIMD) void dec
   // Issue the loads of chunk i.  Every call issues the same loads, also past
   // the end, so that the number of loads in flight is the same on every path
   // and the compiler's wait before a chunk's use covers exactly that chunk.
-  auto issue = [&](Chunk<D> &r, int c0) {
+  auto issue = [&](Chunk<D, NH> &r, int c0) {
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
+    for (int h = 0; h < NH; ++h) {
       const int first = c0 + 16 * h;
       int64_t page = -1;
       if (first < t_end) {                  // uniform: the same entry for every lane
@@ -277,11 +285,13 @@ __global__ __launch_bounds__(64 * kWaves, PA_DECODE_MIN_WAVES_PER_SIMD) void dec
     }
   };
 
-  auto process = [&](const Chunk<D> &r, int c0) {
-    const bool tail = (c0 + kChunk > t_end) | !r.ok[0] | !r.ok[1];
+  auto process = [&](const Chunk<D, NH> &r, int c0) {
+    bool tail = c0 + CT > t_end;
+#pragma unroll
+    for (int h = 0; h < NH; ++h) tail |= !r.ok[h];
     // stage V (token 16h + lrow, chunk 4p + lgrp), zero rows that must not count
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
+    for (int h = 0; h < NH; ++h) {
       const int tok = 16 * h + lrow;
       const bool keep = !tail || (r.ok[h] && c0 + tok < t_end);
 #pragma unroll
@@ -292,10 +302,10 @@ __global__ __launch_bounds__(64 * kWaves, PA_DECODE_MIN_WAVES_PER_SIMD) void dec
       }
     }
 
-    // S^T = K Q^T for the two 16-token halves
-    f32x4 s[2];
+    // S^T = K Q^T for the 16-token halves
+    f32x4 s[NH];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
+    for (int h = 0; h < NH; ++h) {
       s[h] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int p = 0; p < P; ++p) s[h] = mfma16(__builtin_bit_cast(bf16x8, r.k[h][p]), qb[p], s[h]);
@@ -303,15 +313,16 @@ __global__ __launch_bounds__(64 * kWaves, PA_DECODE_MIN_WAVES_PER_SIMD) void dec
     // the lane holds tokens c0 + 16h + 4*lgrp + i of its column
     if (tail) {
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
+      for (int h = 0; h < NH; ++h)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const bool vis = r.ok[h] && (c0 + 16 * h + 4 * lgrp + i) < t_end;
           s[h][i] = vis ? s[h][i] : -INFINITY;
         }
     }
-    float cmax = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
-                       fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
+    float cmax = fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3]));
+#pragma unroll
+    for (int h = 1; h < NH; ++h) cmax = fmaxf(cmax, fmaxf(fmaxf(s[h][0], s[h][1]), fmaxf(s[h][2], s[h][3])));
     cmax = rows_max(cmax);
     const float mt = cmax * c;
     if (__any(mt > m_run + kRescaleSlack)) {
@@ -324,17 +335,35 @@ __global__ __launch_bounds__(64 * kWaves, PA_DECODE_MIN_WAVES_PER_SIMD) void dec
 #pragma unroll
         for (int i = 0; i < 4; ++i) acc[mb][i] *= corr;
     }
-    bf16x8 pb;
+    __bf16 pv[4 * NH];
     float psum = 0.f;
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
+    for (int h = 0; h < NH; ++h)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const float p = fast_exp2(__builtin_fmaf(s[h][i], c, -m_run));
         psum += p;
-        pb[4 * h + i] = (__bf16)p;
+        pv[4 * h + i] = (__bf16)p;
       }
     l_lane += psum;
+    if constexpr (NH == 1) {
+      // one page: O^T += V^T P^T on 16x16x16 products, contraction slot
+      // 4*lgrp + k = token 4*lgrp + k (the lane's own probabilities)
+      bf16x4 pb4;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pb4[i] = pv[i];
+#pragma unroll
+      for (int mb = 0; mb < D / 16; ++mb) {
+        const int tok = 4 * lgrp + (lrow >> 2);
+        const int d = 16 * mb + 4 * (lrow & 3);
+        const uint16_t *src = &vw[tok * D + ((d / 8) ^ swz(tok)) * 8 + (d % 8)];
+        const i16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4 *)(src));
+        acc[mb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, __builtin_bit_cast(i16x4, pb4), acc[mb], 0, 0, 0);
+      }
+    } else {
+    bf16x8 pb;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) pb[i] = pv[i];
 
     // O^T += V^T P^T.  Contraction slot lgrp*8 + 4*half + k is token
     // 16*half + 4*lgrp + k; one transposing read per half: lane lrow points at
@@ -354,91 +383,25 @@ __global__ __launch_bounds__(64 * kWaves, PA_DECODE_MIN_WAVES_PER_SIMD) void dec
       const bf16x8 va = __builtin_bit_cast(bf16x8, uint4{part[0].x, part[0].y, part[1].x, part[1].y});
       acc[mb] = mfma16(va, pb, acc[mb]);
     }
+    }
   };
 
-  if constexpr (D == 128) {
-    // d=128: a chunk loop driven by the next chunk's index, the partial saved
-    // inside it (fewer registers live at once than the loop below)
-    // a partial result (unnormalised output, reference max, exp-sum) into LDS,
-    // then start afresh
-    auto save = [&](float (*o)[D], float *m, float *l) {
-      const float l_tot = rows_sum(l_lane);
-      if (lrow < G) {
-  #pragma unroll
-        for (int mb = 0; mb < D / 16; ++mb)
-  #pragma unroll
-          for (int i = 0; i < 4; ++i) o[lrow][mb * 16 + 4 * lgrp + i] = acc[mb][i];
-        if (lgrp == 0) {
-          m[lrow] = m_run;
-          l[lrow] = l_tot;
-        }
-      }
-  #pragma unroll
-      for (int mb = 0; mb < D / 16; ++mb) acc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
-      m_run = kMaxFloor;
-      l_lane = 0.f;
-    };
-    // this wavefront's next chunk (-1: none left)
-    int taken = 0;
-    auto next = [&]() -> int {
-      if (taken < n_my) return w + kWaves * taken++;
-      return -1;
-    };
-    // the partial goes out after the wavefront's last chunk
-    const int last_static = w + kWaves * (n_my - 1);
-    auto after = [&](int k) {
-      if (k == last_static) save(red_o[w], red_m[w], red_l[w]);
-    };
-    if (n_my == 0) save(red_o[w], red_m[w], red_l[w]);   // no static chunk: an empty partial
-
-    // ---- ring of register chunks: chunk k is processed while the next one is
-    // in flight.  Exactly one chunk is in flight at the top of every iteration,
-    // on every path; the last chunk is processed in a branch of its own, with
-    // nothing issued after it, so no load is made past the end.
-    auto tok = [&](int k) { return t_begin + k * kChunk; };
-    int cur = next();
-    if (cur >= 0) {
-      Chunk<D> r0, r1;
-      issue(r0, tok(cur));
-      for (;;) {
-        int nx = next();
-        if (nx < 0) {
-          process(r0, tok(cur));
-          after(cur);
-          break;
-        }
-        issue(r1, tok(nx));
-        process(r0, tok(cur));
-        after(cur);
-        cur = nx;
-        nx = next();
-        if (nx < 0) {
-          process(r1, tok(cur));
-          after(cur);
-          break;
-        }
-        issue(r0, tok(nx));
-        process(r1, tok(cur));
-        after(cur);
-        cur = nx;
-      }
-    }
-  } else {
+  {
     // ---- ring of register steps: step i is processed while step i+1 is in
     // flight.  A step is kSub chunks (kSub*32 tokens): the more bytes a step
     // moves, the fewer latency-bound steps a workgroup takes.
     struct Step {
-      Chunk<D> c[kSub];
+      Chunk<D, NH> c[kSub];
     };
     Step r0, r1;
     auto issue_step = [&](Step &st, int i) {
   #pragma unroll
-      for (int j = 0; j < kSub; ++j) issue(st.c[j], t_begin + ((w + kWaves * i) * kSub + j) * kChunk);
+      for (int j = 0; j < kSub; ++j) issue(st.c[j], t_begin + ((w + kWaves * i) * kSub + j) * CT);
     };
     auto process_step = [&](Step &st, int i) {
   #pragma unroll
       for (int j = 0; j < kSub; ++j) {
-        const int c0 = t_begin + ((w + kWaves * i) * kSub + j) * kChunk;
+        const int c0 = t_begin + ((w + kWaves * i) * kSub + j) * CT;
         if (c0 < t_end) process(st.c[j], c0);
       }
     };
@@ -469,7 +432,7 @@ __global__ __launch_bounds__(64 * kWaves, PA_DECODE_MIN_WAVES_PER_SIMD) void dec
   if (err_bits && lane == 0) raise_err(a.err, err_bits);
 
   // ---- merge the wavefronts: unnormalised outputs, maxima and sums via LDS
-  if constexpr (D != 128) {
+  {
     const float l_tot = rows_sum(l_lane);
     if (lrow < G) {
 #pragma unroll

@@ -54,6 +54,21 @@ def test_decode_long_context():
     _parity(W.long_decode())
 
 
+def test_decode_d128_long_contexts_split():
+    """d=128 (one-page chunks): contexts split across workgroups and merged by the
+    combine kernel, next to a short one and a one-token one."""
+    case = W.make_decode("long128", B=4, Hq=32, Hkv=8, d=128, n_pages=2048, ctx_lens=[16384, 9000, 70, 1],
+                         max_ctx=16384, seed=21, mbps=1024)
+    assert pa.decode_splits(4, 32, 8, 128, 16384) > 1
+    _parity(case)
+
+
+def test_decode_d128_llama_shaped_batch():
+    """64 sequences, contexts U[1, 2048], 32/8/128: every (sequence, head)."""
+    _parity(W.make_decode("b64_d128", B=64, Hq=32, Hkv=8, d=128, n_pages=9000, max_ctx=2048, seed=22,
+                          mbps=128))
+
+
 def test_decode_single_split_and_many_splits_agree():
     """A long context split many ways equals the oracle; so does a short one (no combine)."""
     for ctx in ([3000], [40]):
@@ -121,8 +136,9 @@ def test_decode_equals_last_prefill_row():
     assert (Ld[0] - Lp[0, :, -1]).abs().max() <= 1e-3
 
 
-def test_decode_missing_page_is_flagged_and_skipped():
-    case = W.make_decode("bad", B=2, Hq=32, Hkv=8, d=64, n_pages=64, ctx_lens=[90, 40], seed=6)
+@pytest.mark.parametrize("d", [64, 128])
+def test_decode_missing_page_is_flagged_and_skipped(d):
+    case = W.make_decode("bad", B=2, Hq=32, Hkv=8, d=d, n_pages=64, ctx_lens=[90, 40], seed=6)
     Oref0, Lref0, pool_h = oracle.decode_case(case)
     O, L, pool = run_decode(case)
     bt = case.cache.block_table.copy()
