@@ -180,62 +180,84 @@ struct MergeArgs {
   int B, Hq, HW, BM;
 };
 
-// One workgroup per split row block: 128 (row, head) pairs (BM x HW) of D
-// values, D/8 lanes per pair, 8 values per lane.  O = sum_s w_s O_s / sum_s
-// w_s with w_s = exp(LSE_s - max LSE), LSE = max + ln(sum_s w_s).
+// One workgroup per split row block and group of PPP (row, head) pairs of its
+// 128 (BM x HW): D/8 lanes per pair, 8 values per lane.  O = sum_s w_s O_s /
+// sum_s w_s with w_s = exp(LSE_s - max LSE), LSE = max + ln(sum_s w_s).  The
+// lanes of a pair share the max over the pieces (each reads every LP-th
+// piece's LSE), and the weighted sum takes four pieces per step with their
+// loads in flight together.
 template <int D>
 __global__ __launch_bounds__(256) void packed_merge_kernel(MergeArgs a) {
   constexpr int LP = D / 8;          // lanes per pair
-  constexpr int PPP = 256 / LP;      // pairs per pass
+  constexpr int PPP = 256 / LP;      // pairs per workgroup
   constexpr int NP = 128;            // pairs per tile (BM * HW)
   constexpr int PT = NP * (D + 1);   // floats per partial tile
+  static_assert(64 % LP == 0 && NP % PPP == 0, "a pair's lanes sit in one wave");
   const int32_t *it = a.merge + 6 * (int64_t)blockIdx.x;
   const int b = it[0], rb = it[1], hg = it[2], slot0 = it[3], n = it[4];
   if (b < 0 || b >= a.B || rb < 0 || hg < 0 || hg >= a.Hq / a.HW || slot0 < 0 || n < 1 ||
       (int64_t)slot0 + n > a.n_part_slots) {
-    if (threadIdx.x == 0) raise_err(a.err, PA_DEVERR_BAD_PLAN);
+    if (threadIdx.x == 0 && blockIdx.y == 0) raise_err(a.err, PA_DEVERR_BAD_PLAN);
     return;
   }
   const int64_t s0 = a.q_start[b], s1 = a.q_start[b + 1];
   if (s0 < 0 || s1 < s0 || s1 > a.total_q) return;   // flagged by the prefill kernel
   const int qlen = (int)min(s1 - s0, (int64_t)0x7fffffff);
   const int j = threadIdx.x % LP;
-  for (int p0 = 0; p0 < NP; p0 += PPP) {
-    const int p = p0 + threadIdx.x / LP;
-    const int r = p / a.HW, h = p % a.HW;
-    const int row = rb * a.BM + r;
-    if (row >= qlen) continue;
-    float M = -INFINITY;
-    for (int s = 0; s < n; ++s) M = fmaxf(M, a.part[(int64_t)(slot0 + s) * PT + NP * D + p]);
-    float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    float L = 0.f;
-    if (M != -INFINITY) {
-      for (int s = 0; s < n; ++s) {
-        const float *tp = a.part + (int64_t)(slot0 + s) * PT;
-        const float w = fast_exp2((tp[NP * D + p] - M) * kLog2e);   // 0 for an empty piece
-        L += w;
-        const float4 x0 = *reinterpret_cast<const float4 *>(tp + p * D + 8 * j);
-        const float4 x1 = *reinterpret_cast<const float4 *>(tp + p * D + 8 * j + 4);
-        o[0] += w * x0.x;
-        o[1] += w * x0.y;
-        o[2] += w * x0.z;
-        o[3] += w * x0.w;
-        o[4] += w * x1.x;
-        o[5] += w * x1.y;
-        o[6] += w * x1.z;
-        o[7] += w * x1.w;
+  const int p = blockIdx.y * PPP + threadIdx.x / LP;
+  const int r = p / a.HW, h = p % a.HW;
+  const int row = rb * a.BM + r;
+  if (row >= qlen) return;   // (every lane of the pair)
+  const float *base = a.part + (int64_t)slot0 * PT;
+  auto lse = [&](int s) { return base[(int64_t)s * PT + NP * D + p]; };
+  float M = -INFINITY;
+  for (int s = j; s < n; s += LP) M = fmaxf(M, lse(s));
+#pragma unroll
+  for (int o = 1; o < LP; o <<= 1) M = fmaxf(M, __shfl_xor(M, o));
+  float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  float L = 0.f;
+  auto add = [&](float l, float4 x0, float4 x1) {
+    const float w = fast_exp2((l - M) * kLog2e);   // 0 for an empty piece
+    L += w;
+    o[0] += w * x0.x;
+    o[1] += w * x0.y;
+    o[2] += w * x0.z;
+    o[3] += w * x0.w;
+    o[4] += w * x1.x;
+    o[5] += w * x1.y;
+    o[6] += w * x1.z;
+    o[7] += w * x1.w;
+  };
+  if (M != -INFINITY) {
+    int s = 0;
+    for (; s + 4 <= n; s += 4) {
+      float l4[4];
+      float4 x0[4], x1[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float *tp = base + (int64_t)(s + u) * PT;
+        l4[u] = tp[NP * D + p];
+        x0[u] = *reinterpret_cast<const float4 *>(tp + p * D + 8 * j);
+        x1[u] = *reinterpret_cast<const float4 *>(tp + p * D + 8 * j + 4);
       }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) add(l4[u], x0[u], x1[u]);
     }
-    const float inv = L > 0.f ? 1.f / L : 0.f;
-    const int64_t oh = (s0 + row) * a.Hq + hg * a.HW + h;
-    uint4 v;
-    v.x = pack_bf16x2(o[0] * inv, o[1] * inv);
-    v.y = pack_bf16x2(o[2] * inv, o[3] * inv);
-    v.z = pack_bf16x2(o[4] * inv, o[5] * inv);
-    v.w = pack_bf16x2(o[6] * inv, o[7] * inv);
-    *reinterpret_cast<uint4 *>(a.O + oh * D + 8 * j) = v;
-    if (j == 0) a.LSE[oh] = L > 0.f ? M + fast_log2(L) * kLn2 : -INFINITY;
+    for (; s < n; ++s) {
+      const float *tp = base + (int64_t)s * PT;
+      add(tp[NP * D + p], *reinterpret_cast<const float4 *>(tp + p * D + 8 * j),
+          *reinterpret_cast<const float4 *>(tp + p * D + 8 * j + 4));
+    }
   }
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  const int64_t oh = (s0 + row) * a.Hq + hg * a.HW + h;
+  uint4 v;
+  v.x = pack_bf16x2(o[0] * inv, o[1] * inv);
+  v.y = pack_bf16x2(o[2] * inv, o[3] * inv);
+  v.z = pack_bf16x2(o[4] * inv, o[5] * inv);
+  v.w = pack_bf16x2(o[6] * inv, o[7] * inv);
+  *reinterpret_cast<uint4 *>(a.O + oh * D + 8 * j) = v;
+  if (j == 0) a.LSE[oh] = L > 0.f ? M + fast_log2(L) * kLn2 : -INFINITY;
 }
 
 }  // namespace
@@ -248,10 +270,11 @@ int launch_packed_merge(const int32_t *merge, int64_t n_merge, const int32_t *q_
   const int G = Hq / Hkv;
   MergeArgs a{merge, q_start, part, static_cast<uint16_t *>(O), LSE, err, total_q, n_part_slots, B, Hq,
               prefill_heads_per_block(G), prefill_rows_per_block(G)};
+  // grid.y: the groups of 256 / (D/8) pairs of a tile's 128
   if (D == 64)
-    hipLaunchKernelGGL(packed_merge_kernel<64>, dim3((unsigned)n_merge), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(packed_merge_kernel<64>, dim3((unsigned)n_merge, 4), dim3(256), 0, stream, a);
   else if (D == 128)
-    hipLaunchKernelGGL(packed_merge_kernel<128>, dim3((unsigned)n_merge), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(packed_merge_kernel<128>, dim3((unsigned)n_merge, 8), dim3(256), 0, stream, a);
   else
     return PA_ERR_UNSUPPORTED;
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
