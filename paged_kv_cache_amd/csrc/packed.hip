@@ -18,11 +18,13 @@
 // block leave partial results (O normalised, LSE) that the merge kernel
 // combines by the log-sum-exp rule (tiny-vllm part 3, "causalMask and online
 // softmax": rescale to the larger maximum and add).  A piece costs a start
-// (Q, page offsets) and a partial tile written and read again: measured on a
-// chunk of 128 rows after 16384 cached tokens, a mixed batch and two prompt
-// chunks, half the share and twice the share were both slower, and pieces
-// sized to fill every resident workgroup slot much slower (the merge and the
-// starts outweigh the occupancy).
+// (Q, page offsets) and a partial tile written and read again.  Where the
+// share leaves under two items per CU (a few long row blocks, as a chunk of
+// 128 rows after 16384 cached tokens: one item per CU), it is halved until
+// there are two (that chunk 37.9 -> 33.7 us); a mixed batch and two prompt
+// chunks, with 3-4 items per CU already, are slower with half the share, and
+// pieces sized to fill all four workgroup slots of a CU are slower on all
+// three (the starts and the partial traffic outweigh the occupancy).
 //
 // Order.  Workgroup i runs on XCD i % 8, and the row blocks of one (sequence,
 // head group) read the same K/V: the planner gives every (sequence, head
@@ -83,10 +85,21 @@ int plan_prefill_packed(const int32_t *q_lens, const int32_t *kv_lens, int B, in
       total += (int64_t)nt * n_hgroups / (narrow ? HW : 1);
     }
   }
-  // pieces per row block: at most the even share of key tiles per CU
-  const int64_t share = std::max<int64_t>(kMinSplitTiles, (total + n_cu - 1) / std::max(1, n_cu));
+  // pieces per row block: at most the even share of key tiles per CU; while
+  // that leaves fewer than two items per CU (a few long row blocks), the share
+  // is halved (down to kMinSplitTiles), so that a CU runs two workgroups
+  const int64_t cus = std::max(1, n_cu);
+  int64_t share = std::max<int64_t>(kMinSplitTiles, (total + cus - 1) / cus);
   std::vector<int> pieces(tiles.size(), 1);
-  for (size_t i = 0; i < tiles.size(); ++i) pieces[i] = (int)((tiles[i].n_tiles + share - 1) / share);
+  for (;;) {
+    int64_t n_items = 0;
+    for (size_t i = 0; i < tiles.size(); ++i) {
+      pieces[i] = (int)((tiles[i].n_tiles + share - 1) / share);
+      n_items += pieces[i];
+    }
+    if (n_items >= 2 * cus || share <= kMinSplitTiles) break;
+    share = std::max<int64_t>(kMinSplitTiles, (share + 1) / 2);
+  }
   struct Item {
     int b, rb, hg, t0, t1, slot;
   };

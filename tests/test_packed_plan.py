@@ -107,7 +107,8 @@ def test_plan_splits_only_long_row_blocks():
     p, items, merges = plan([37, 1, 64], [300, 17, 64])
     assert p.n_merge == 0 and p.workspace_bytes == 0 and np.all(items[:, 5] == -1)
     # a chunk after a long prefix next to short work: its row blocks are cut into
-    # pieces of at most the even share of key tiles per CU (256 CUs), >= 8 tiles
+    # pieces of at most the even share of key tiles per CU (256 CUs), >= 8 tiles,
+    # halved while the plan has fewer than two items per CU
     ql, kv = [300, 1, 1], [13300, 5, 9]
     p, items, merges = plan(ql, kv)
     blocks, _ = row_blocks(ql, kv, 32, 8, True)
@@ -116,6 +117,9 @@ def test_plan_splits_only_long_row_blocks():
     total = sum(n for (b, rb, hg), n in blocks.items() if b == 0) + sum(
         n for (b, rb, hg), n in blocks.items() if b > 0) // 4
     share = max(8, -(-total // 256))
+    # fewer than two items per CU: the share is halved (not below 8) until there are
+    while sum(-(-n // share) for n in blocks.values()) < 2 * 256 and share > 8:
+        share = max(8, -(-share // 2))
     lengths = items[:, 4] - items[:, 3]
     assert p.n_merge > 0 and lengths.max() <= share
     for (b, rb, hg), n in blocks.items():
