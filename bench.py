@@ -183,7 +183,7 @@ def source_digest(*names: str) -> str:
 TRAFFIC = {
     # kernel: (source digest, fetched bytes, written bytes)
     "prefill": ("ea1991cd164bd473", 25385805, 17301504),
-    "decode": ("c7fbbdb3a01a0cd3", 152910232, 272800),
+    "decode": ("86de613c0b43599b", 152909592, 273184),
 }
 
 
