@@ -307,8 +307,20 @@ def bench_decode(steps: int, warmup: int, replicas: int = 8):
     # whole pages touched: ceil(ctx/16) pages of 16 tokens x all kv heads x (K, V)
     page_bytes = int(np.ceil(case.ctx_lens / 16).sum()) * 16 * c.n_kv_heads * case.d * 2 * 2
     spread = launch_spread([lambda r=r: decode(r) for r in range(replicas)])
+    # the same step in one launch: attn_decode_append writes the 64 new tokens
+    # and attends to them with the cached context
+    O2, L2 = torch.empty_like(O), torch.empty_like(L)
+
+    def append_step(r):
+        pa.attn_decode_append(q, new_k, new_v, pool, tables[r], c.layer, lens, c.n_kv_heads, case.scale,
+                              max_ctx, slot_ids=sid, workspace=ws, out=O2, lse=L2)
+
+    append_step(0)
+    torch.cuda.synchronize()
+    assert (O2.float() - O_ref.float()).abs().max().item() <= 2e-2 and (L2 - L_ref).abs().max().item() <= 1e-3
+    wall_append = timed_steps([lambda r=r: append_step(r) for r in range(replicas)], steps, warmup)
     return dict(case=case, wall=wall, kv_bytes=kv_bytes, io_bytes=io_bytes, t_kernel=t_kernel, sustained=sus,
-                replicas=replicas, n_ctx=n_ctx, page_bytes=page_bytes, spread=spread)
+                replicas=replicas, n_ctx=n_ctx, page_bytes=page_bytes, spread=spread, wall_append=wall_append)
 
 
 # -------------------------------------------------------------- CPU oracle
@@ -830,6 +842,9 @@ def main() -> int:
             "config": {"workload": "paged decode step, 64 sequences, ctx ~ U[1, 2048]",
                        "batch": dcase.B, "ctx_tokens": d["n_ctx"], "kv_bytes": d["kv_bytes"],
                        "replicas": d["replicas"], "step": "kv_scatter(64 tokens) + attn_decode"},
+            "append_step": {"step": "attn_decode_append (the 64 new tokens written and attended in one launch)",
+                            "ms_per_step": round(d["wall_append"] / args.steps * 1e3, 5),
+                            "value": round(d["kv_bytes"] / (d["wall_append"] / args.steps) / 1e9, 2)},
             "roofline": {"kernel": "decode_kernel<64,4>", "bound": "hbm",
                          "achieved": round(d_kern, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": round(d_kern / PEAK_HBM_GBS, 4),

@@ -262,6 +262,32 @@ int attn_decode(const void *q, const void *kv_cache, int64_t n_pages, const int3
                 int head_dim, float scale, int max_ctx, void *workspace, size_t workspace_bytes,
                 void *O, float *LSE, int32_t *err, void *stream);
 
+/*
+ * attn_decode_append -- one decode step in one launch: the new token of every
+ * sequence is written to its page and attended to with the rest of the
+ * context (page 6, "pagedAttentionKernel"; page 3, "Distributing K/V into
+ * paged blocks" for the write).  The same result as kv_scatter of the new
+ * tokens at positions ctx_lens[b] - 1 followed by attn_decode, to the
+ * rounding of one token's contribution (the new token is added after the
+ * cached ones instead of among them); the pool bytes are identical.
+ *
+ *   k_new, v_new [B][Hkv][head_dim] bf16 (16-byte aligned): the new token's
+ *                K and V rows; written into kv_cache (which must be writable)
+ *                at slot slot_ids[b], position ctx_lens[b] - 1.
+ *   ctx_lens     [B] tokens of each sequence including the new one; a
+ *                sequence with ctx_lens[b] == 0, a bad slot or a length that
+ *                sets PA_DEVERR_BAD_POS writes nothing.  A missing page for
+ *                the new token sets PA_DEVERR_BAD_PAGE; the token is then
+ *                neither written nor attended to.
+ *   Other arguments, workspace and results as for attn_decode.
+ */
+int attn_decode_append(const void *q, const void *k_new, const void *v_new, void *kv_cache,
+                       int64_t n_pages, const int32_t *block_table, int n_slots, int n_layers,
+                       int max_blocks_per_seq, int layer, const int32_t *slot_ids,
+                       const int32_t *ctx_lens, int B, int Hq, int Hkv, int head_dim, float scale,
+                       int max_ctx, void *workspace, size_t workspace_bytes, void *O, float *LSE,
+                       int32_t *err, void *stream);
+
 /* Workspace bytes attn_decode needs for this batch shape (0 on bad sizes). */
 size_t attn_decode_workspace_size(int B, int Hq, int Hkv, int head_dim, int max_ctx);
 

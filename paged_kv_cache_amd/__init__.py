@@ -63,6 +63,9 @@ def load():
         lib.attn_decode.restype = _I
         lib.attn_decode.argtypes = [_P, _P, _I64, _P, _I, _I, _I, _I, _P, _P, _I, _I, _I, _I, _F,
                                     _I, _P, _SZ, _P, _P, _P, _P]
+        lib.attn_decode_append.restype = _I
+        lib.attn_decode_append.argtypes = [_P, _P, _P, _P, _I64, _P, _I, _I, _I, _I, _P, _P, _I, _I, _I,
+                                           _I, _F, _I, _P, _SZ, _P, _P, _P, _P]
         lib.attn_decode_noalloc.restype = _I
         lib.attn_decode_noalloc.argtypes = [_P, _P, _I64, _P, _I, _I, _I, _I, _P, _P, _I, _I, _I, _I,
                                             _F, _I, _P, _P, _P, _P]
@@ -288,6 +291,34 @@ def attn_decode(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tens
         _dev(out, torch.bfloat16, "out"), _dev(lse, torch.float32, "lse"),
         _dev(err, torch.int32, "err"), _stream(stream))
     _check(rc, "attn_decode")
+    return out, lse
+
+
+def attn_decode_append(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor, kv_cache: torch.Tensor,
+                       block_table: torch.Tensor, layer: int, ctx_lens: torch.Tensor, n_kv_heads: int,
+                       scale: float, max_ctx: int, slot_ids: torch.Tensor | None = None,
+                       workspace: torch.Tensor | None = None, out: torch.Tensor | None = None,
+                       lse: torch.Tensor | None = None, err: torch.Tensor | None = None, stream=None):
+    """One decode step in one launch: k_new, v_new [B, Hkv, d] are written to the pages
+    at position ctx_lens - 1 and attended to with the cached context; returns
+    (O [B, Hq, d] bf16, LSE [B, Hq] fp32)."""
+    B, Hq, d = q.shape
+    n_slots, n_layers, mbps = block_table.shape
+    if workspace is None:
+        workspace = decode_workspace(B, Hq, n_kv_heads, d, max_ctx, q.device)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty(B, Hq, dtype=torch.float32, device=q.device)
+    rc = load().attn_decode_append(
+        _dev(q, torch.bfloat16, "q"), _dev(k_new, torch.bfloat16, "k_new"), _dev(v_new, torch.bfloat16, "v_new"),
+        _dev(kv_cache, None, "kv_cache"), _n_pages(kv_cache, n_kv_heads, d),
+        _dev(block_table, torch.int32, "block_table"), n_slots, n_layers, mbps, layer,
+        _dev(slot_ids, torch.int32, "slot_ids"), _dev(ctx_lens, torch.int32, "ctx_lens"), B, Hq, n_kv_heads,
+        d, float(scale), int(max_ctx), _dev(workspace, None, "workspace"),
+        workspace.numel() * workspace.element_size(), _dev(out, torch.bfloat16, "out"),
+        _dev(lse, torch.float32, "lse"), _dev(err, torch.int32, "err"), _stream(stream))
+    _check(rc, "attn_decode_append")
     return out, lse
 
 

@@ -242,6 +242,27 @@ int attn_decode(const void *q, const void *kv_cache, int64_t n_pages, const int3
                            static_cast<hipStream_t>(stream));
 }
 
+int attn_decode_append(const void *q, const void *k_new, const void *v_new, void *kv_cache,
+                       int64_t n_pages, const int32_t *block_table, int n_slots, int n_layers,
+                       int max_blocks_per_seq, int layer, const int32_t *slot_ids,
+                       const int32_t *ctx_lens, int B, int Hq, int Hkv, int head_dim, float scale,
+                       int max_ctx, void *workspace, size_t workspace_bytes, void *O, float *LSE,
+                       int32_t *err, void *stream) {
+  int rc = decode_checks(q, kv_cache, n_pages, block_table, n_slots, n_layers, max_blocks_per_seq,
+                         layer, ctx_lens, B, Hq, Hkv, head_dim, scale, max_ctx, O, LSE);
+  if (rc != PA_OK || B == 0) return rc;
+  if (!k_new || !v_new) return PA_ERR_NULL;
+  if (!aligned16(k_new) || !aligned16(v_new)) return PA_ERR_ALIGN;
+  const size_t ws_need = pa::decode_workspace_bytes(B, Hq, Hkv, head_dim, max_ctx);
+  if (ws_need > 0 && !workspace) return PA_ERR_NULL;
+  if (ws_need > 0 && !aligned16(workspace)) return PA_ERR_ALIGN;
+  if (workspace_bytes < ws_need) return PA_ERR_WORKSPACE;
+  return pa::launch_decode(q, kv_cache, n_pages, block_table, n_slots, n_layers,
+                           max_blocks_per_seq, layer, slot_ids, ctx_lens, B, Hq, Hkv, head_dim,
+                           scale, max_ctx, workspace, O, LSE, err, static_cast<hipStream_t>(stream),
+                           k_new, v_new);
+}
+
 int attn_decode_noalloc(const void *q, const void *kv_cache, int64_t n_pages,
                         const int32_t *block_table, int n_slots, int n_layers,
                         int max_blocks_per_seq, int layer, const int32_t *slot_ids,

@@ -94,6 +94,10 @@ struct DecodeArgs {
   uint16_t *out;                // [B][Hq][D]
   float *lse;                   // [B][Hq]
   int32_t *err;
+  // attn_decode_append: the new token of every sequence, [B][Hkv][D] each,
+  // written to its page (position ctx_lens[b] - 1) by the same launch
+  const uint16_t *k_new, *v_new;
+  uint8_t *pool_w;              // the pool, for those writes
 };
 
 // max / sum over the four 16-lane rows of a wave (lanes l, l^16, l^32, l^48)
@@ -137,7 +141,7 @@ __device__ __forceinline__ int clamped_ctx(const DecodeArgs &a, int b, int *slot
 
 }  // namespace
 
-template <int D, int G>
+template <int D, int G, bool APPEND>
 __global__ __launch_bounds__(64 * kWaves, PA_DECODE_MIN_WAVES_PER_SIMD) void decode_kernel(DecodeArgs a) {
   constexpr int kSub = D == 64 ? PA_DECODE_SUB : 1;   // chunks per step (registers: d=128 one)
   static_assert(D % 32 == 0 && 16 % G == 0, "unsupported shape");
@@ -216,9 +220,16 @@ __global__ __launch_bounds__(64 * kWaves, PA_DECODE_MIN_WAVES_PER_SIMD) void dec
   int err_bits = 0;
   int slot;
   const int ctx = clamped_ctx(a, b, &slot, &err_bits);
+  const bool ctx_ok = err_bits == 0;         // neither the slot nor the length was cut
   if (xs != 0 || kvh != 0) err_bits = 0;     // one workgroup per sequence reports these
   const int t_begin = xs * a.xsplit_tokens;
-  const int t_end = min(ctx, t_begin + a.xsplit_tokens);
+  const int t_split = min(ctx, t_begin + a.xsplit_tokens);
+  // attn_decode_append: the split holding the new token (position ctx-1)
+  // streams its other tokens from the pages and takes the new one from
+  // k_new / v_new after its chunk loop
+  const int new_tok = ctx - 1;
+  const bool has_new = APPEND && ctx_ok && new_tok >= t_begin && new_tok < t_split;
+  const int t_end = has_new ? new_tok : t_split;   // the chunk loop's end
 
   const int32_t *trow = a.block_table + ((int64_t)slot * a.n_layers + a.layer) * a.mbps;
   const int64_t row_bytes = (int64_t)a.Hkv * D * 2;
@@ -262,6 +273,26 @@ __global__ __launch_bounds__(64 * kWaves, PA_DECODE_MIN_WAVES_PER_SIMD) void dec
     const int32_t e = trow_c[t_begin / kPageTokens];
     if (e >= 0 && (int64_t)e < a.n_pages) safe_page = e;
   }
+  // The new token's K and V row of this kv head go to its page (wave 0 of
+  // the split holding it, one 16-byte piece per lane); nothing in the launch
+  // reads that write back.
+  const int64_t new_row = ((int64_t)b * a.Hkv + kvh) * D;   // the new row in k_new / v_new
+  if constexpr (APPEND) {
+    if (has_new) {
+      if (w == 0 && lane < 2 * (D / 8)) {
+        const bool isv = lane >= D / 8;
+        const int cc = isv ? lane - D / 8 : lane;
+        const u32x4 x = *reinterpret_cast<const u32x4 *>((isv ? a.v_new : a.k_new) + new_row + 8 * cc);
+        const int32_t e = trow_c[new_tok / kPageTokens];
+        if (e >= 0 && (int64_t)e < a.n_pages) {   // a missing page is flagged by the chunk loads
+          uint8_t *dst = a.pool_w + (int64_t)e * page_bytes + (isv ? v_offset : 0) +
+                         (int64_t)(new_tok % kPageTokens) * row_bytes + (int64_t)kvh * D * 2 + 16 * cc;
+          __builtin_nontemporal_store(x, reinterpret_cast<u32x4 *>(dst));
+        }
+      }
+    }
+  }
+
   // Issue the loads of chunk i.  Every call issues the same loads, also past
   // the end, so that the number of loads in flight is the same on every path
   // and the compiler's wait before a chunk's use covers exactly that chunk.
@@ -429,6 +460,47 @@ __global__ __launch_bounds__(64 * kWaves, PA_DECODE_MIN_WAVES_PER_SIMD) void dec
     }
   }
 
+  if constexpr (APPEND) {
+    if (has_new && w == 0) {
+      // the new token: its score for this lane's column (the Q operand's d
+      // order: d = p*32 + lgrp*8 + i, the four lanes of a column summed), the
+      // exponential against the reference max, p * v_new into the output
+      const int32_t e = trow_c[new_tok / kPageTokens];
+      if (e < 0 || (int64_t)e >= a.n_pages) {
+        err_bits |= PA_DEVERR_BAD_PAGE;   // masked, as a token on a missing page
+      } else {
+        const uint16_t *kn = a.k_new + new_row;
+        const uint16_t *vn = a.v_new + new_row;
+        float dot = 0.f;
+#pragma unroll
+        for (int p = 0; p < P; ++p) {
+          const bf16x8 kk = *reinterpret_cast<const bf16x8 *>(kn + p * 32 + lgrp * 8);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) dot = __builtin_fmaf((float)qb[p][i], (float)kk[i], dot);
+        }
+        const float mt = rows_sum(dot) * c;
+        if (__any(mt > m_run + kRescaleSlack)) {
+          const float m_new = fmaxf(m_run, mt);
+          const float corr = fast_exp2(m_run - m_new);
+          m_run = m_new;
+          l_lane *= corr;
+#pragma unroll
+          for (int mb = 0; mb < D / 16; ++mb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[mb][i] *= corr;
+        }
+        const float pn = fast_exp2(mt - m_run);
+        if (lgrp == 0) l_lane += pn;   // one lane of the column counts it
+#pragma unroll
+        for (int mb = 0; mb < D / 16; ++mb) {
+          const bf16x4 vv = *reinterpret_cast<const bf16x4 *>(vn + 16 * mb + 4 * lgrp);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[mb][i] = __builtin_fmaf(pn, (float)vv[i], acc[mb][i]);
+        }
+      }
+    }
+  }
+
   if (err_bits && lane == 0) raise_err(a.err, err_bits);
 
   // ---- merge the wavefronts: unnormalised outputs, maxima and sums via LDS
@@ -568,7 +640,10 @@ template <int D, int G>
 static int launch_decode_t(DecodeArgs a, int B, hipStream_t stream) {
   const int64_t grid = (int64_t)B * a.Hkv * a.n_xsplits;
   if (grid > 0x7fffffff) return PA_ERR_RANGE;
-  hipLaunchKernelGGL((decode_kernel<D, G>), dim3((unsigned)grid), dim3(64 * kWaves), 0, stream, a);
+  if (a.k_new)
+    hipLaunchKernelGGL((decode_kernel<D, G, true>), dim3((unsigned)grid), dim3(64 * kWaves), 0, stream, a);
+  else
+    hipLaunchKernelGGL((decode_kernel<D, G, false>), dim3((unsigned)grid), dim3(64 * kWaves), 0, stream, a);
   if (hipGetLastError() != hipSuccess) return PA_ERR_LAUNCH;
   if (a.n_xsplits > 1) {
     hipLaunchKernelGGL((decode_combine_kernel<D>), dim3((unsigned)(B * a.Hkv * G)), dim3(64), 0,
@@ -581,7 +656,8 @@ static int launch_decode_t(DecodeArgs a, int B, hipStream_t stream) {
 int launch_decode(const void *q, const void *kv_cache, int64_t n_pages, const int32_t *block_table,
                   int n_slots, int n_layers, int mbps, int layer, const int32_t *slot_ids,
                   const int32_t *ctx_lens, int B, int Hq, int Hkv, int D, float scale, int max_ctx,
-                  void *workspace, void *O, float *LSE, int32_t *err, hipStream_t stream) {
+                  void *workspace, void *O, float *LSE, int32_t *err, hipStream_t stream,
+                  const void *k_new, const void *v_new) {
   const Split s = split_policy(B, Hq, Hkv, D, max_ctx);
   uint8_t *ws = static_cast<uint8_t *>(workspace);
   DecodeArgs a{};
@@ -606,6 +682,9 @@ int launch_decode(const void *q, const void *kv_cache, int64_t n_pages, const in
   a.out = static_cast<uint16_t *>(O);
   a.lse = LSE;
   a.err = err;
+  a.k_new = static_cast<const uint16_t *>(k_new);
+  a.v_new = static_cast<const uint16_t *>(v_new);
+  a.pool_w = k_new ? static_cast<uint8_t *>(const_cast<void *>(kv_cache)) : nullptr;
   const int G = Hq / Hkv;
 #define PA_DECODE_CASE(DD, GG) \
   if (D == DD && G == GG) return launch_decode_t<DD, GG>(a, B, stream);

@@ -45,10 +45,13 @@ size_t decode_workspace_bytes(int B, int Hq, int Hkv, int D, int max_ctx);
 size_t decode_scratch_bytes();
 void *decode_scratch_ptr();
 
+// k_new, v_new (attn_decode_append): the new token of every sequence, written
+// to kv_cache at position ctx_lens[b] - 1 by the same launch; null: none.
 int launch_decode(const void *q, const void *kv_cache, int64_t n_pages, const int32_t *block_table,
                   int n_slots, int n_layers, int mbps, int layer, const int32_t *slot_ids,
                   const int32_t *ctx_lens, int B, int Hq, int Hkv, int D, float scale, int max_ctx,
-                  void *workspace, void *O, float *LSE, int32_t *err, hipStream_t stream);
+                  void *workspace, void *O, float *LSE, int32_t *err, hipStream_t stream,
+                  const void *k_new = nullptr, const void *v_new = nullptr);
 
 int launch_kv_append(const void *k, const void *v, const void *q_in, void *q_out, int Hq, int B,
                      const int32_t *slot_ids, const int32_t *positions, const float *cos_t,

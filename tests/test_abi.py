@@ -142,6 +142,22 @@ def test_noalloc_decode_host_checks():
     assert lib.attn_decode_noalloc(*args[:10], 0, *args[11:]) == 0
 
 
+def test_decode_append_host_checks():
+    """attn_decode_append checks its arguments like attn_decode, then the new
+    token's rows (present, 16-byte aligned); B == 0 is a no-op.  (Every call
+    here is rejected on the host or does nothing: none launches.)"""
+    lib = pa.load()
+    good = _fake()
+    args = [good, good, good, good, 64, good, 1, 1, 128, 0, None, good, 1, 32, 8, 64, 0.125, 64, None, 0,
+            good, good, None, None]
+    assert lib.attn_decode_append(*args[:16], 0.0, *args[17:]) == -8          # scale
+    assert lib.attn_decode_append(args[0], None, *args[2:]) == -1              # k_new
+    assert lib.attn_decode_append(*args[:2], None, *args[3:]) == -1            # v_new
+    assert lib.attn_decode_append(args[0], ctypes.c_void_p(0x10002), *args[2:]) == -4
+    assert lib.attn_decode_append(*args[:13], 96, 3, *args[15:]) == -3         # group 32
+    assert lib.attn_decode_append(*args[:12], 0, *args[13:]) == 0              # B == 0
+
+
 def _append(lib, **kw):
     good = _fake()
     a = dict(k=good, v=good, q_in=None, q_out=None, Hq=0, B=4, slot_ids=None, positions=good,
