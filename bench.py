@@ -183,7 +183,7 @@ def source_digest(*names: str) -> str:
 TRAFFIC = {
     # kernel: (source digest, fetched bytes, written bytes)
     "prefill": ("ea1991cd164bd473", 25385805, 17301504),
-    "decode": ("86de613c0b43599b", 152909592, 273184),
+    "decode": ("e52f15b10dab480f", 152930454, 273056),
 }
 
 
@@ -845,7 +845,7 @@ def main() -> int:
             "append_step": {"step": "attn_decode_append (the 64 new tokens written and attended in one launch)",
                             "ms_per_step": round(d["wall_append"] / args.steps * 1e3, 5),
                             "value": round(d["kv_bytes"] / (d["wall_append"] / args.steps) / 1e9, 2)},
-            "roofline": {"kernel": "decode_kernel<64,4>", "bound": "hbm",
+            "roofline": {"kernel": "decode_kernel<64,4,false>", "bound": "hbm",
                          "achieved": round(d_kern, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": round(d_kern / PEAK_HBM_GBS, 4),
                          "traffic": traffic_of("decode", decode_digest),
