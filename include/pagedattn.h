@@ -279,6 +279,9 @@ int attn_decode(const void *q, const void *kv_cache, int64_t n_pages, const int3
  *                sets PA_DEVERR_BAD_POS writes nothing.  A missing page for
  *                the new token sets PA_DEVERR_BAD_PAGE; the token is then
  *                neither written nor attended to.
+ *   slot_ids     must name distinct slots (one sequence per slot): two
+ *                entries on one slot would write one position while the other
+ *                reads it, and the results of both are then undefined.
  *   Other arguments, workspace and results as for attn_decode.
  */
 int attn_decode_append(const void *q, const void *k_new, const void *v_new, void *kv_cache,
