@@ -284,7 +284,7 @@ __global__ __launch_bounds__(64 * kWaves, PA_DECODE_MIN_WAVES_PER_SIMD) void dec
         const int cc = isv ? lane - D / 8 : lane;
         const u32x4 x = *reinterpret_cast<const u32x4 *>((isv ? a.v_new : a.k_new) + new_row + 8 * cc);
         const int32_t e = trow_c[new_tok / kPageTokens];
-        if (e >= 0 && (int64_t)e < a.n_pages) {   // a missing page is flagged by the chunk loads
+        if (e >= 0 && (int64_t)e < a.n_pages) {   // a missing page is flagged after the chunk loop
           uint8_t *dst = a.pool_w + (int64_t)e * page_bytes + (isv ? v_offset : 0) +
                          (int64_t)(new_tok % kPageTokens) * row_bytes + (int64_t)kvh * D * 2 + 16 * cc;
           __builtin_nontemporal_store(x, reinterpret_cast<u32x4 *>(dst));

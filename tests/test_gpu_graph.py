@@ -136,3 +136,55 @@ def test_packed_with_merges_graph_replays():
     case.q = qpad
     Oref, Lref, _ = oracle.prefill_case(case, rows=rows)
     assert_attn_close(out, lse, Oref, Lref, what="packed, last graph replay")
+
+
+def test_decode_append_graph_replays():
+    """The one-launch decode step in a graph: before each replay new queries and
+    new K/V rows are written into the captured buffers; every replay writes the
+    same pool bytes and gives the same O, LSE as an eager call, and the last one
+    matches kv_scatter's pool and the oracle (split contexts and the combine
+    kernel included)."""
+    import dataclasses
+    case = W.make_decode("graph_append", B=3, Hq=32, Hkv=8, d=64, n_pages=4096, ctx_lens=[16384, 9000, 70],
+                         max_ctx=16384, seed=6, scale=0.125, mbps=1024)
+    c = case.cache
+    bt = i32(c.block_table)
+    pool = device_pool(c)
+    scatter(pool, c, case.context, bt)
+    ws = pa.decode_workspace(3, 32, 8, 64, 16384, DEV)
+    lens, slots = i32(case.ctx_lens), i32(case.slot_ids)
+    q_buf = case.q.to(DEV).clone()
+    k_buf = case.new_tokens.k.to(DEV).clone()
+    v_buf = case.new_tokens.v.to(DEV).clone()
+    out = torch.empty_like(q_buf)
+    lse = torch.empty(3, 32, dtype=torch.float32, device=DEV)
+
+    def call(q, k, v, o=None, l=None):
+        return pa.attn_decode_append(q, k, v, pool, bt, c.layer, lens, c.n_kv_heads, case.scale, 16384,
+                                     slot_ids=slots, workspace=ws, out=o, lse=l)
+
+    graph, outs = _capture(lambda: call(q_buf, k_buf, v_buf, out, lse))
+    for r in range(REPLAYS):
+        q_buf.copy_(_new_q(tuple(q_buf.shape), 2000 + r))
+        k_buf.copy_(_new_q(tuple(k_buf.shape), 3000 + r))
+        v_buf.copy_(_new_q(tuple(v_buf.shape), 4000 + r))
+        graph.replay()
+        torch.cuda.synchronize()
+        pool_after = pool.clone()
+        _ = (out.float() * 2).sum().item()              # eager work between replays
+        ref = call(q_buf.clone(), k_buf.clone(), v_buf.clone())
+        torch.cuda.synchronize()
+        assert torch.equal(pool, pool_after), f"replay {r}: the eager call wrote other pool bytes"
+        for a, b in zip(outs, ref):
+            assert torch.equal(a, b), f"replay {r}: graph result differs from the eager call"
+    # the last replay: the pool as kv_scatter of the last new rows leaves it, O and LSE as the oracle's
+    new = dataclasses.replace(case.new_tokens, k=k_buf.cpu(), v=v_buf.cpu())
+    ref_pool = device_pool(c)
+    scatter(ref_pool, c, case.context, bt)
+    scatter(ref_pool, c, new, bt)
+    torch.cuda.synchronize()
+    assert torch.equal(pool, ref_pool)
+    case.q = q_buf.cpu()
+    case.new_tokens = new
+    Oref, Lref, _ = oracle.decode_case(case)
+    assert_attn_close(out, lse, Oref, Lref, what="decode append, last graph replay")
