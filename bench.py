@@ -183,7 +183,7 @@ def source_digest(*names: str) -> str:
 TRAFFIC = {
     # kernel: (source digest, fetched bytes, written bytes)
     "prefill": ("ea1991cd164bd473", 25385805, 17301504),
-    "decode": ("e52f15b10dab480f", 152930454, 273056),
+    "decode": ("11bdd7943ed8e803", 152919319, 273088),
 }
 
 
