@@ -232,8 +232,23 @@ def bench_prefill(steps: int, warmup: int):
     flops = prefill_flops(case.B, case.T, case.Hq, case.d, True)
     alg_bytes = (q.numel() + O.numel()) * 2 + L.numel() * 4 + 2 * k.numel() * 2
     t_kernel = kernel_time(prefill)
+    # the same step in one launch: attn_prefill_append writes the prompt's K/V
+    # to the pages and attends to the rows of its inputs
+    kd = k.view(case.B, case.T, c.n_kv_heads, case.d)
+    vd = v.view(case.B, case.T, c.n_kv_heads, case.d)
+    O2, L2 = torch.empty_like(O), torch.empty_like(L)
+
+    def append_step():
+        pa.attn_prefill_append(q, kd, vd, pool, bt, c.layer, lens, case.scale, True, slot_ids=sid,
+                               out=O2, lse=L2)
+
+    append_step()
+    torch.cuda.synchronize()
+    assert (O2.float() - O_ref.float()).abs().max().item() <= 2e-2 and (L2 - L_ref).abs().max().item() <= 1e-3
+    wall_append = timed_steps([append_step], steps, warmup)
     return dict(case=case, wall=wall, flops=flops, t_kernel=t_kernel, clock_ghz=sustained_clock(), sustained=sus,
-                t_scatter=kernel_time(scatter), alg_bytes=alg_bytes, spread=launch_spread([prefill]))
+                t_scatter=kernel_time(scatter), alg_bytes=alg_bytes, spread=launch_spread([prefill]),
+                wall_append=wall_append)
 
 
 RATED_CLOCK_GHZ = 2.4          # the clock the 2.5 PFLOP/s bf16 figure is rated at
@@ -832,6 +847,9 @@ def main() -> int:
                      "avg_us": round(p["t_kernel"] * 1e6, 3), "alg_bytes": p["alg_bytes"],
                      "single_launch": p["spread"], "source_digest": prefill_digest},
         "scatter_us": round(p["t_scatter"] * 1e6, 3),
+        "append_step": {"step": "attn_prefill_append (the 4096 prompt tokens written and attended in one launch)",
+                        "ms_per_step": round(p["wall_append"] / args.steps * 1e3, 5),
+                        "value": round(p["flops"] / (p["wall_append"] / args.steps) / 1e12, 3)},
         "sustained": p["sustained"],
         "decode": {
             "metric": "decode KV-read GB/s", "unit": "GB/s",

@@ -157,6 +157,30 @@ int attn_prefill(const void *q, const void *kv_cache, int64_t n_pages, const int
                  void *stream);
 
 /*
+ * attn_prefill_append -- a prefill step in one launch: the prompts' K/V rows
+ * are written to their pages and the prompts attend to them.  The pages'
+ * prefill attends to the K/V it has just computed while it copies them into
+ * the cache (page "3. The prefill path", sections "Distributing K/V into paged
+ * blocks" and "Per-head attention scores and GQA"); this call does both.  The
+ * result is that of kv_scatter of every prompt token (slot slot_ids[b],
+ * position t for t < seq_lens[b]) followed by attn_prefill: the pool bytes and
+ * O, LSE are identical, errors included (a token on a missing page is flagged
+ * PA_DEVERR_BAD_PAGE, not written, and left out of the attention).
+ *
+ *   q            [B][T][Hq][head_dim] bf16, as for attn_prefill.
+ *   k, v         [B][T][Hkv][head_dim] bf16 (16-byte aligned): the prompts'
+ *                K and V rows; rows t >= seq_lens[b] are not read.
+ *   kv_cache     written (the prompt rows' bytes only); other cache arguments,
+ *                slot_ids, seq_lens, causal, scale, O, LSE as for attn_prefill.
+ *   slot_ids     must name distinct slots, as for attn_decode_append.
+ */
+int attn_prefill_append(const void *q, const void *k, const void *v, void *kv_cache, int64_t n_pages,
+                        const int32_t *block_table, int n_slots, int n_layers, int max_blocks_per_seq,
+                        int layer, const int32_t *slot_ids, const int32_t *seq_lens, int B, int T,
+                        int Hq, int Hkv, int head_dim, float scale, int causal, void *O, float *LSE,
+                        int32_t *err, void *stream);
+
+/*
  * attn_prefill_chunk -- the prefill of a prompt chunk that continues a cached
  * prefix, and of mixed batches: sequence b has kv_lens[b] tokens in the
  * cache (prefix and chunk, the chunk's K/V already scattered) and its queries

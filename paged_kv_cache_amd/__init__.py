@@ -57,6 +57,9 @@ def load():
         lib.attn_prefill.restype = _I
         lib.attn_prefill.argtypes = [_P, _P, _I64, _P, _I, _I, _I, _I, _P, _P, _I, _I, _I, _I, _I,
                                      _F, _I, _P, _P, _P, _P]
+        lib.attn_prefill_append.restype = _I
+        lib.attn_prefill_append.argtypes = [_P, _P, _P, _P, _I64, _P, _I, _I, _I, _I, _P, _P, _I, _I, _I,
+                                            _I, _I, _F, _I, _P, _P, _P, _P]
         lib.attn_prefill_chunk.restype = _I
         lib.attn_prefill_chunk.argtypes = [_P, _P, _I64, _P, _I, _I, _I, _I, _P, _P, _P, _I, _I, _I,
                                            _I, _I, _F, _I, _P, _P, _P, _P]
@@ -200,6 +203,34 @@ class PackedPlan:
         if self.workspace_bytes == 0:
             return None
         return torch.empty(self.workspace_bytes, dtype=torch.uint8, device=self.plan.device)
+
+
+def attn_prefill_append(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, kv_cache: torch.Tensor,
+                        block_table: torch.Tensor, layer: int, seq_lens: torch.Tensor, scale: float,
+                        causal: bool = True, slot_ids: torch.Tensor | None = None,
+                        out: torch.Tensor | None = None, lse: torch.Tensor | None = None,
+                        err: torch.Tensor | None = None, stream=None):
+    """Prefill step in one launch: k, v [B, T, Hkv, d] (the prompts' K/V rows) are written to
+    their pages and q [B, T, Hq, d] attends to them; returns (O [B, T, Hq, d] bf16,
+    LSE [B, Hq, T] fp32), as kv_scatter of the prompt tokens followed by attn_prefill."""
+    B, T, Hq, d = q.shape
+    n_kv_heads = k.shape[2]
+    if tuple(k.shape) != (B, T, n_kv_heads, d) or tuple(v.shape) != tuple(k.shape):
+        raise ValueError("k and v must be [B, T, Hkv, d] with q's B, T and d")
+    n_slots, n_layers, mbps = block_table.shape
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty(B, Hq, T, dtype=torch.float32, device=q.device)
+    rc = load().attn_prefill_append(
+        _dev(q, torch.bfloat16, "q"), _dev(k, torch.bfloat16, "k"), _dev(v, torch.bfloat16, "v"),
+        _dev(kv_cache, None, "kv_cache"), _n_pages(kv_cache, n_kv_heads, d),
+        _dev(block_table, torch.int32, "block_table"), n_slots, n_layers, mbps, layer,
+        _dev(slot_ids, torch.int32, "slot_ids"), _dev(seq_lens, torch.int32, "seq_lens"),
+        B, T, Hq, n_kv_heads, d, float(scale), int(bool(causal)), _dev(out, torch.bfloat16, "out"),
+        _dev(lse, torch.float32, "lse"), _dev(err, torch.int32, "err"), _stream(stream))
+    _check(rc, "attn_prefill_append")
+    return out, lse
 
 
 def prefill_packed_plan(q_lens, kv_lens, n_q_heads: int, n_kv_heads: int, head_dim: int,

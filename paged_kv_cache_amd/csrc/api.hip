@@ -131,6 +131,27 @@ int attn_prefill(const void *q, const void *kv_cache, int64_t n_pages, const int
                         O, LSE, err, stream);
 }
 
+int attn_prefill_append(const void *q, const void *k, const void *v, void *kv_cache, int64_t n_pages,
+                        const int32_t *block_table, int n_slots, int n_layers, int max_blocks_per_seq,
+                        int layer, const int32_t *slot_ids, const int32_t *seq_lens, int B, int T,
+                        int Hq, int Hkv, int head_dim, float scale, int causal, void *O, float *LSE,
+                        int32_t *err, void *stream) {
+  if (B < 0 || T < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0) return PA_ERR_SHAPE;
+  if (!supported_head_dim(head_dim)) return PA_ERR_UNSUPPORTED;
+  if (!valid_scale(scale)) return PA_ERR_VALUE;
+  int rc = check_cache(kv_cache, n_pages, block_table, n_slots, n_layers, max_blocks_per_seq, layer,
+                       Hkv, head_dim);
+  if (rc != PA_OK) return rc;
+  if (B == 0 || T == 0) return PA_OK;
+  if (!q || !k || !v || !seq_lens || !O || !LSE) return PA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(O)) return PA_ERR_ALIGN;
+  if ((int64_t)B * T * Hq > 0x7fffffffLL) return PA_ERR_RANGE;
+  return pa::launch_prefill_store(q, k, v, kv_cache, n_pages, block_table, n_slots, n_layers,
+                                  max_blocks_per_seq, layer, slot_ids, seq_lens, B, T, Hq, Hkv,
+                                  head_dim, scale, causal, O, LSE, err,
+                                  static_cast<hipStream_t>(stream));
+}
+
 int attn_prefill_chunk(const void *q, const void *kv_cache, int64_t n_pages,
                        const int32_t *block_table, int n_slots, int n_layers,
                        int max_blocks_per_seq, int layer, const int32_t *slot_ids,

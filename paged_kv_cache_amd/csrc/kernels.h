@@ -37,6 +37,14 @@ int launch_prefill_paged(const void *q, const void *kv_cache, int64_t n_pages,
 int launch_prefill_dense(const void *q, const void *k, const void *v, int B, int T, int Hq, int Hkv,
                          int D, float scale, int causal, void *O, float *LSE, hipStream_t stream);
 
+// attn_prefill_append: the prefill of whole prompts on the inputs k, v
+// [B][T][Hkv][D], which also writes every prompt token's K/V row to its page.
+int launch_prefill_store(const void *q, const void *k, const void *v, void *kv_cache, int64_t n_pages,
+                         const int32_t *block_table, int n_slots, int n_layers, int mbps, int layer,
+                         const int32_t *slot_ids, const int32_t *seq_lens, int B, int T, int Hq, int Hkv,
+                         int D, float scale, int causal, void *O, float *LSE, int32_t *err,
+                         hipStream_t stream);
+
 size_t decode_workspace_bytes(int B, int Hq, int Hkv, int D, int max_ctx);
 
 // attn_decode_noalloc's workspace: the capacity of the static device array and

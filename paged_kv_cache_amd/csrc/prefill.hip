@@ -88,6 +88,9 @@ struct PrefillArgs {
   float *part;
   int64_t total_q;
   int64_t n_part_slots;        // partial tiles the workspace holds
+  // attn_prefill_append: the same pool, writable; the prompt's K/V rows (k, v)
+  // are also written to their pages
+  uint8_t *pool_w;
 };
 
 }  // namespace
@@ -104,9 +107,10 @@ struct Swz {
   __device__ static int v(int key) { return 4 * ((key / (128 / D)) % (D / 32)); }
 };
 
-template <int D, int G, bool PAGED, int NS, int OCC, bool PACKED>
+template <int D, int G, bool PAGED, int NS, int OCC, bool PACKED, bool STORE>
 __global__ __launch_bounds__(64 * kBlocks, OCC) void prefill_kernel(PrefillArgs a) {
   static_assert(PAGED || !PACKED, "packed rows are read through the block table");
+  static_assert(!(PAGED && STORE), "a storing prefill reads its K/V from the inputs");
   constexpr int NW = kBlocks;                      // waves per workgroup, one block each
   constexpr int HW = G < kBlocks ? G : kBlocks;    // heads per workgroup
   constexpr int RW = kBlocks / HW;                 // 32-row blocks per workgroup
@@ -255,6 +259,29 @@ __global__ __launch_bounds__(64 * kBlocks, OCC) void prefill_kernel(PrefillArgs 
     trow_v = a.block_table + ((int64_t)uniform(len > 0 ? slot : 0) * a.n_layers + a.layer) * a.mbps;
     trow = as_const(trow_v);
   }
+  if constexpr (STORE) {
+    // a whole prompt (query row t is token t) attended from the inputs k, v,
+    // whose rows also go to the pages: length and slot checked as above
+    const bool reporter = hg == 0 && rb == 0;
+    len = a.seq_lens[b];
+    if (len < 0 || len > T) {
+      if (reporter) err_bits |= PA_DEVERR_BAD_POS;
+      len = len < 0 ? 0 : T;
+    }
+    const int slot = a.slot_ids ? a.slot_ids[b] : b;
+    if (slot < 0 || slot >= a.n_slots) {
+      if (reporter) err_bits |= PA_DEVERR_BAD_SLOT;
+      len = 0;
+    }
+    if (len > a.mbps * kPageTokens) {
+      if (reporter) err_bits |= PA_DEVERR_BAD_POS;
+      len = a.mbps * kPageTokens;
+    }
+    len = uniform(len);
+    qlen = len;
+    trow_v = a.block_table + ((int64_t)uniform(len > 0 ? slot : 0) * a.n_layers + a.layer) * a.mbps;
+    trow = as_const(trow_v);
+  }
 
   // query row t is the token at position off + t (a chunk continuing a cached
   // prefix is aligned to the end of the sequence; off = 0 for a whole prompt)
@@ -332,7 +359,7 @@ __global__ __launch_bounds__(64 * kBlocks, OCC) void prefill_kernel(PrefillArgs 
   bool any_bad = false;
   int64_t safe_page = 0;
   int32_t raw0[PPW];   // first window of this wave's pages, read with the pass below
-  if constexpr (PAGED) {
+  if constexpr (PAGED || STORE) {
 #pragma unroll
     for (int pp = 0; pp < PPW; ++pp) {
       const int blk = (64 * (t_begin >> 6) + lane) * (kBN / kPageTokens) + wave * PPW + pp;
@@ -541,7 +568,7 @@ __global__ __launch_bounds__(64 * kBlocks, OCC) void prefill_kernel(PrefillArgs 
     const uint8_t *vt = vbuf(S_);
     // mask: only tiles that cross a diagonal, kv_end or a missing page
     uint32_t bad_pages = 0;
-    if constexpr (PAGED) {
+    if constexpr (PAGED || STORE) {
       if (any_bad) {
 #pragma unroll
         for (int p = 0; p < kBN / kPageTokens; ++p) {
@@ -697,6 +724,30 @@ __global__ __launch_bounds__(64 * kBlocks, OCC) void prefill_kernel(PrefillArgs 
     wait_vm_lgkm0<0>();
   }
 
+  // attn_prefill_append: the prompt's K and V rows of this workgroup's tokens
+  // go to their pages, 16 bytes per lane, once per kv head (by the kv head's
+  // first head group).  They are loaded here and stored after O, so that the
+  // loads' latency passes while O is staged.  A missing page is flagged and
+  // its rows are not written (its keys were masked above, as attn_prefill
+  // masks them).
+  constexpr int HPK = G > HW ? G / HW : 1;                   // head groups per kv head
+  constexpr int NCP = STORE ? BM * 2 * CH / (64 * NW) : 1;   // 16-byte pieces per lane
+  static_assert(!STORE || NCP * 64 * NW == BM * 2 * CH, "whole pieces per lane");
+  u32x4 cp[NCP];
+  const bool cp_on = STORE && hg % HPK == 0;
+  if constexpr (STORE) {
+    if (cp_on) {
+#pragma unroll
+      for (int j = 0; j < NCP; ++j) {
+        const int ci = tid + j * 64 * NW;
+        const int r = ci / (2 * CH), part = ci % (2 * CH);
+        const int t = rb * BM + r;
+        const uint16_t *src = (part >= CH ? a.v : a.k) + (((int64_t)b * T + t) * a.Hkv + kvh) * D + (part % CH) * 8;
+        cp[j] = t < len ? *reinterpret_cast<const u32x4 *>(src) : u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+  }
+
   if (err_bits && tid == 0) raise_err(a.err, err_bits);
 
   // ---- epilogue: one divide per row, LSE in natural-log units.  O leaves
@@ -800,6 +851,37 @@ __global__ __launch_bounds__(64 * kBlocks, OCC) void prefill_kernel(PrefillArgs 
       __builtin_amdgcn_raw_buffer_store_b128(v, rs, (int)(r * row_stride) + cc * 16, 0, kStoreDevice);
     }
   }
+  if constexpr (STORE) {
+    // The rows a wave stores with one instruction (64 lanes / (2 CH) pieces
+    // per row: 2 or 4 consecutive rows, starting at a multiple of that) lie on
+    // one page, so the page is wave-uniform and the store goes through a
+    // buffer resource over that page, at device scope like O's stores.
+    constexpr int RPW = 64 / (2 * CH);   // rows per wave and piece
+    static_assert(RPW >= 1 && kPageTokens % RPW == 0 && BM % RPW == 0, "a wave's rows on one page");
+    if (cp_on) {
+      bool bad = false;
+#pragma unroll
+      for (int j = 0; j < NCP; ++j) {
+        const int ci = tid + j * 64 * NW;
+        const int r = ci / (2 * CH), part = ci % (2 * CH);
+        const int t = rb * BM + r;
+        const int tw = rb * BM + uniform((64 * wave + j * 64 * NW) / (2 * CH));   // the wave's first row
+        if (tw < len) {
+          const int32_t e = trow[tw / kPageTokens];
+          if (e >= 0 && (int64_t)e < a.n_pages) {
+            const __amdgpu_buffer_rsrc_t prs = __builtin_amdgcn_make_buffer_rsrc(
+                a.pool_w + (int64_t)e * page_bytes, (short)0, (int)page_bytes, 0x00020000);
+            const int off = (part >= CH ? (int)v_offset : 0) + (t % kPageTokens) * a.Hkv * ROWB + kvh * ROWB +
+                            (part % CH) * 16;
+            if (t < len) __builtin_amdgcn_raw_buffer_store_b128(cp[j], prs, off, 0, kStoreDevice);
+          } else {
+            bad = true;
+          }
+        }
+      }
+      if (bad && lane == 0) raise_err(a.err, PA_DEVERR_BAD_PAGE);
+    }
+  }
 }
 
 
@@ -812,7 +894,7 @@ struct PrefillCfg {
   static constexpr int OCC = D == 64 ? 4 : 2;
 };
 
-template <int D, int G, bool PAGED>
+template <int D, int G, bool PAGED, bool STORE>
 static int launch_prefill_t(PrefillArgs a, hipStream_t stream) {
   using C = PrefillCfg<D>;
   constexpr int HW = G < kBlocks ? G : kBlocks;
@@ -826,7 +908,7 @@ static int launch_prefill_t(PrefillArgs a, hipStream_t stream) {
   const int64_t grid = (int64_t)a.B * a.n_hgroups * a.n_rowblocks;
   if (grid == 0) return PA_OK;
   if (grid > 0x7fffffff) return PA_ERR_RANGE;
-  hipLaunchKernelGGL((prefill_kernel<D, G, PAGED, C::NS, C::OCC, false>), dim3((unsigned)grid),
+  hipLaunchKernelGGL((prefill_kernel<D, G, PAGED, C::NS, C::OCC, false, STORE>), dim3((unsigned)grid),
                      dim3(64 * kBlocks), 0, stream, a);
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
@@ -838,15 +920,15 @@ static int launch_prefill_packed_t(PrefillArgs a, int64_t n_work, hipStream_t st
   a.n_hgroups = a.Hkv * G / HW;
   if (n_work <= 0) return PA_OK;
   if (n_work > 0x7fffffffLL) return PA_ERR_RANGE;
-  hipLaunchKernelGGL((prefill_kernel<D, G, true, C::NS, C::OCC, true>), dim3((unsigned)n_work),
+  hipLaunchKernelGGL((prefill_kernel<D, G, true, C::NS, C::OCC, true, false>), dim3((unsigned)n_work),
                      dim3(64 * kBlocks), 0, stream, a);
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
 
-template <bool PAGED>
+template <bool PAGED, bool STORE = false>
 static int dispatch_prefill(const PrefillArgs &a, int D, int G, hipStream_t stream) {
 #define PA_PREFILL_CASE(DD, GG) \
-  if (D == DD && G == GG) return launch_prefill_t<DD, GG, PAGED>(a, stream);
+  if (D == DD && G == GG) return launch_prefill_t<DD, GG, PAGED, STORE>(a, stream);
   PA_PREFILL_CASE(64, 1)
   PA_PREFILL_CASE(64, 2)
   PA_PREFILL_CASE(64, 4)
@@ -937,6 +1019,36 @@ int launch_prefill_packed(const void *q, const void *kv_cache, int64_t n_pages,
   if (rc != PA_OK) return rc;
   return launch_packed_merge(plan + 6 * n_work, n_merge, q_start, B, static_cast<const float *>(part),
                              n_part_slots, O, LSE, err, total_q, Hq, Hkv, D, stream);
+}
+
+int launch_prefill_store(const void *q, const void *k, const void *v, void *kv_cache, int64_t n_pages,
+                         const int32_t *block_table, int n_slots, int n_layers, int mbps, int layer,
+                         const int32_t *slot_ids, const int32_t *seq_lens, int B, int T, int Hq, int Hkv,
+                         int D, float scale, int causal, void *O, float *LSE, int32_t *err,
+                         hipStream_t stream) {
+  PrefillArgs a{};
+  a.q = static_cast<const uint16_t *>(q);
+  a.k = static_cast<const uint16_t *>(k);
+  a.v = static_cast<const uint16_t *>(v);
+  a.pool = static_cast<const uint8_t *>(kv_cache);
+  a.pool_w = static_cast<uint8_t *>(kv_cache);
+  a.n_pages = n_pages;
+  a.block_table = block_table;
+  a.slot_ids = slot_ids;
+  a.seq_lens = seq_lens;
+  a.n_slots = n_slots;
+  a.n_layers = n_layers;
+  a.mbps = mbps;
+  a.layer = layer;
+  a.B = B;
+  a.T = T;
+  a.Hkv = Hkv;
+  a.scale_log2 = scale * kLog2e;
+  a.causal = causal ? 1 : 0;
+  a.O = static_cast<uint16_t *>(O);
+  a.LSE = LSE;
+  a.err = err;
+  return dispatch_prefill<false, true>(a, D, Hq / Hkv, stream);
 }
 
 int launch_prefill_dense(const void *q, const void *k, const void *v, int B, int T, int Hq, int Hkv,

@@ -158,6 +158,26 @@ def test_decode_append_host_checks():
     assert lib.attn_decode_append(*args[:12], 0, *args[13:]) == 0              # B == 0
 
 
+def test_prefill_append_host_checks():
+    """attn_prefill_append checks its arguments like attn_prefill, then the
+    prompt's K/V rows (present, 16-byte aligned); B == 0 or T == 0 is a no-op.
+    (Every call here is rejected on the host or does nothing: none launches.)"""
+    lib = pa.load()
+    good = _fake()
+    args = [good, good, good, good, 64, good, 1, 1, 128, 0, None, good, 1, 32, 32, 8, 64, 0.125, 1,
+            good, good, None, None]
+    assert lib.attn_prefill_append(*args[:17], 0.0, *args[18:]) == -8          # scale
+    assert lib.attn_prefill_append(args[0], None, *args[2:]) == -1             # k
+    assert lib.attn_prefill_append(*args[:2], None, *args[3:]) == -1           # v
+    assert lib.attn_prefill_append(args[0], ctypes.c_void_p(0x10002), *args[2:]) == -4
+    assert lib.attn_prefill_append(*args[:3], ctypes.c_void_p(0x10008), *args[4:]) == -4   # kv_cache
+    assert lib.attn_prefill_append(*args[:14], 96, 3, *args[16:]) == -3        # group 32
+    assert lib.attn_prefill_append(*args[:16], 72, *args[17:]) == -3           # head_dim 72
+    assert lib.attn_prefill_append(*args[:9], 1, *args[10:]) == -2             # layer past n_layers
+    assert lib.attn_prefill_append(*args[:12], 0, *args[13:]) == 0             # B == 0
+    assert lib.attn_prefill_append(*args[:13], 0, *args[14:]) == 0             # T == 0
+
+
 def _append(lib, **kw):
     good = _fake()
     a = dict(k=good, v=good, q_in=None, q_out=None, Hq=0, B=4, slot_ids=None, positions=good,
