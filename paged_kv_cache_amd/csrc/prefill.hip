@@ -633,7 +633,7 @@ __global__ __launch_bounds__(64 * kBlocks, OCC) void prefill_kernel(PrefillArgs 
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const float p = fast_exp2(__builtin_fmaf(s[r], c, -m_run));
-          sum += p;
+          sum = r == 0 ? p : sum + p;   // (p >= 0: the same value as 0 + p, one add fewer)
           pb[r / 8][r % 8] = (__bf16)p;
         }
         return sum;
