@@ -563,6 +563,11 @@ __global__ __launch_bounds__(64 * kBlocks, OCC) void prefill_kernel(PrefillArgs 
   // 32-key halves one after the other (each an online-softmax step), so that
   // only one half's scores and operands are live at a time.  The lane holds
   // keys kv0 + 32h + 8*(r/4) + 4*lh + r%4 of its row in s[r].
+  // the last key any row of this wave may see: a 32-key half past it (the
+  // half beyond the diagonal in the last tile of an even causal row block,
+  // or past the end of the keys) is skipped, since all its scores are masked
+  const int wave_last_key =
+      uniform(min(kv_end - 1, a.causal ? off + (narrow ? rb * BM + NR - 1 : wave_row_end) : 0x7fffffff));
   auto compute = [&](int t, auto S_) {
     const uint8_t *kt = kbuf(S_);
     const uint8_t *vt = vbuf(S_);
@@ -668,10 +673,12 @@ __global__ __launch_bounds__(64 * kBlocks, OCC) void prefill_kernel(PrefillArgs 
     // the matrix unit while the first half's exponentials run; each half's V
     // operands are read after its exponentials (read before them, they would
     // push the wave past the 128 registers of four workgroups per CU)
+    const bool half1 = t * kBN + 32 <= wave_last_key;
     f32x16 s0 = qk(0);
-    f32x16 s1 = qk(1);
+    f32x16 s1;
+    if (half1) s1 = qk(1);
     soft_pv(s0, 0);
-    soft_pv(s1, 1);
+    if (half1) soft_pv(s1, 1);
   };
 
   // ---- the ring.  Step t: wait for this wave's transfers of tile t, barrier
