@@ -1,6 +1,9 @@
-// prefill.hip -- attn_prefill / attn_prefill_dense: FlashAttention-2-style
-// exact attention of whole prompts, K/V read through the block table (paged)
-// or from contiguous tensors (dense).
+// prefill.hip -- attn_prefill / attn_prefill_dense / attn_prefill_append:
+// FlashAttention-2-style exact attention of whole prompts, K/V read through
+// the block table (paged) or from contiguous tensors (dense; the storing
+// instance behind attn_prefill_append also writes those rows to their pages,
+// as the pages' prefill copies the K/V it has computed into the cache while
+// attending to them: page "3. The prefill path").
 //
 // Algorithm (FlashAttention-2 explainer, "Step by step (the two forward
 // tweaks)"): walk the key tiles of a query tile, keep a running max m and an
