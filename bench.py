@@ -24,6 +24,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+import re
 import json
 import os
 import sys
@@ -169,21 +170,28 @@ def timed_steps(step_fns, steps: int, warmup: int, per_graph: int = 8) -> float:
 
 
 def source_digest(*names: str) -> str:
+    """Digest of the code of the named sources: comments and runs of white
+    space are dropped first, so that an edit of a comment leaves it (and the
+    traffic measured on that code) unchanged."""
     h = hashlib.sha256()
     for n in names:
-        with open(os.path.join(ROOT, "paged_kv_cache_amd", "csrc", n), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "paged_kv_cache_amd", "csrc", n), encoding="utf-8") as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 
 # HBM traffic per launch measured with rocprofv3 --pmc FETCH_SIZE and
 # WRITE_SIZE (separate runs), scaled by the factor a plain copy kernel of
 # known size reads on the same counters; valid only for the kernel source it
-# was taken on (digest of the .hip files), null otherwise.
+# was taken on (digest of the code of the .hip files, comments excluded),
+# null otherwise.
 TRAFFIC = {
     # kernel: (source digest, fetched bytes, written bytes)
-    "prefill": ("64dbb2b52497b610", 25386829, 17301504),
-    "decode": ("11bdd7943ed8e803", 152919319, 273088),
+    "prefill": ("f6b15280df2341e4", 25386829, 17301504),
+    "decode": ("776cf067f4ba0de7", 152914328, 273056),
 }
 
 
