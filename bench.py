@@ -488,8 +488,8 @@ def kernels_only(n: int) -> None:
     print(f"kernels-only: {n} launches each", flush=True)
 
 
-SWEEP_PARTS = ("tiny", "dense", "long_prefill", "long_decode", "decode_d128", "chunk", "append", "backward",
-               "decode_batch", "cpu")
+SWEEP_PARTS = ("tiny", "dense", "long_prefill", "long_decode", "decode_d128", "prefill_d128", "chunk", "append",
+               "backward", "decode_batch", "cpu")
 
 
 def sweep(parts=SWEEP_PARTS) -> None:
@@ -591,6 +591,28 @@ def sweep(parts=SWEEP_PARTS) -> None:
         kvb = int(dcase.ctx_lens.sum()) * c.n_kv_heads * dcase.d * 2 * 2
         emit("decode B=64, ctx ~ U[1, 2048] (32/8/128, paged)", t * 1e6, kvb / t / 1e9, "GB/s",
              f"{int(dcase.ctx_lens.sum())} context tokens")
+        del pool
+
+    if "prefill_d128" in parts:
+        # the Llama prefill shape with head_dim 128 (2 x 2048 tokens, 32/8/128, paged,
+        # causal), as two launches and as one (attn_prefill_append)
+        pc = W.make_prefill("prefill_d128", B=2, T=2048, Hq=32, Hkv=8, d=128, n_pages=4096, seed=0,
+                            scale=1.0 / np.sqrt(128.0))
+        c = pc.cache
+        pool = device_pool(c)
+        bt = i32(c.block_table)
+        kk, vv = pc.tokens.k.to(DEV), pc.tokens.v.to(DEV)
+        pa.kv_scatter(kk, vv, i32(pc.tokens.slot_ids), i32(pc.tokens.positions), pool, bt, c.layer)
+        qq, lens, sid = pc.q.to(DEV), i32(pc.seq_lens), i32(pc.slot_ids)
+        fl = prefill_flops(pc.B, pc.T, pc.Hq, pc.d, True)
+        t = kernel_time(lambda: pa.attn_prefill(qq, pool, bt, c.layer, lens, c.n_kv_heads, pc.scale, True,
+                                                slot_ids=sid))
+        emit("prefill 2 x 2048, 32/8/128, paged, causal", t * 1e6, fl / t / 1e12, "TFLOP/s", "attn_prefill")
+        kd, vd = kk.view(pc.B, pc.T, c.n_kv_heads, pc.d), vv.view(pc.B, pc.T, c.n_kv_heads, pc.d)
+        t = kernel_time(lambda: pa.attn_prefill_append(qq, kd, vd, pool, bt, c.layer, lens, pc.scale, True,
+                                                       slot_ids=sid))
+        emit("prefill step in one launch, 2 x 2048, 32/8/128 (attn_prefill_append)", t * 1e6, fl / t / 1e12,
+             "TFLOP/s", "K/V rows written to the pages in the same launch")
         del pool
 
     if "decode_batch" in parts:
