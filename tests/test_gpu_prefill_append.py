@@ -130,3 +130,31 @@ def test_prefill_append_bad_slot_and_lengths():
     assert a[3] & pa.PA_DEVERR_BAD_POS and a[3] & pa.PA_DEVERR_BAD_SLOT
     assert_same(a, b, "bad slot and lengths")
     assert torch.all(a[0][1] == 0) and torch.all(torch.isneginf(a[1][1]))
+
+
+def test_prefill_append_long_prompt_past_one_window():
+    """A 9000-token prompt (key tiles past the first 64, whose pages the paged
+    instance reads in a second window) with a missing page in that second
+    window: the same pool, flags and O, LSE as the two launches, and sampled
+    rows whose keys span the windows against the oracle."""
+    from gpu_util import sample_rows
+    T = 9000
+    case = W.make_prefill("append_long", B=1, T=T, Hq=32, Hkv=8, d=64, n_pages=700, seed=41, mbps=600)
+    bt = case.cache.block_table.copy()
+    bt[case.slot_ids[0], 0, 300] = -1        # keys 4800..4815
+    k, v = dense_kv(case)
+    a, b = both_paths(case, k, v, case.seq_lens, case.slot_ids, bt, case.tokens)
+    assert a[3] & pa.PA_DEVERR_BAD_PAGE
+    assert_same(a, b, "long prompt")
+    rows = sample_rows(1, T, 24, seed=3)
+    rows = np.unique(np.concatenate([rows, np.array([[0, 4799], [0, 4800], [0, 4815], [0, 4816], [0, 8191],
+                                                      [0, 8192]], np.int32)]), axis=0)
+    holed = dataclasses.replace(case.cache, block_table=bt)
+    pool_h = oracle.pool_for(case)
+    assert oracle.scatter_tokens(pool_h, holed, case.tokens) == 16
+    Oref, Lref, bad = oracle.attn_prefill(case.q, pool_h, holed.n_pages, bt, holed.layer, case.slot_ids,
+                                          case.seq_lens, holed.n_kv_heads, case.scale, True, rows)
+    assert bad > 0
+    Og = a[0][0, torch.as_tensor(rows[:, 1], dtype=torch.long)]
+    Lg = a[1][0][:, torch.as_tensor(rows[:, 1], dtype=torch.long)].T
+    assert_attn_close(Og, Lg, Oref, Lref, what="long prompt, sampled rows")
