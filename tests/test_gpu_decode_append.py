@@ -52,8 +52,8 @@ def run_both(case, bt_host=None):
 CTX = [1, 2, 15, 16, 17, 31, 32, 33, 63, 64, 65, 100, 255, 256, 257, 700, 1000, 0]
 
 
-@pytest.mark.parametrize("Hq,Hkv,d", [(32, 8, 64), (8, 8, 64), (16, 1, 64), (32, 16, 64),
-                                      (32, 8, 128), (16, 1, 128), (16, 4, 128)])
+@pytest.mark.parametrize("Hq,Hkv,d", [(32, 8, 64), (8, 8, 64), (16, 1, 64), (32, 16, 64), (64, 8, 64),
+                                      (32, 8, 128), (16, 1, 128), (16, 4, 128), (64, 8, 128)])
 def test_append_ragged_contexts(Hq, Hkv, d):
     case = W.make_decode("append_ragged", B=len(CTX), Hq=Hq, Hkv=Hkv, d=d, n_pages=200, ctx_lens=CTX,
                          seed=Hq + d + 1, n_layers=2, layer=1, n_slots=len(CTX) + 3,
