@@ -876,6 +876,10 @@ def main() -> int:
                      "frac_at_clock": round(kern_tflops / (PEAK_BF16_TFLOPS * p["clock_ghz"] / RATED_CLOCK_GHZ), 4),
                      "avg_us": round(p["t_kernel"] * 1e6, 3), "alg_bytes": p["alg_bytes"],
                      "single_launch": p["spread"], "source_digest": prefill_digest},
+        "context": {"note": "figures the FlashAttention-2 explainer reports on A100 (section Results); "
+                            "other hardware, quoted for context, not targets",
+                    "fa2_forward_frac_of_peak_a100": [0.50, 0.73],
+                    "fa2_training_tflops_per_a100": 225},
         "scatter_us": round(p["t_scatter"] * 1e6, 3),
         "append_step": {"step": "attn_prefill_append (the 4096 prompt tokens written and attended in one launch)",
                         "ms_per_step": round(p["wall_append"] / args.steps * 1e3, 5),
