@@ -272,6 +272,14 @@ def sustained_clock() -> float:
 
 # ------------------------------------------------------------------ decode
 
+def decode_path_note(B: int, Hq: int, Hkv: int, d: int, max_ctx: int) -> str:
+    """Which attn_decode kernel serves this shape, for the sweep's notes."""
+    if pa.decode_whole_pages(B, Hq, Hkv, d):
+        return "whole-page kernel (one workgroup per CU, equal page shares) + merge kernel"
+    n = pa.decode_splits(B, Hq, Hkv, d, max_ctx)
+    return "per-head kernel" + (f", {n} workgroup splits per context + combine kernel" if n > 1 else "")
+
+
 def decode_replicas(case, n: int):
     """Block tables placing the same contexts on n disjoint page sets."""
     bt0 = case.cache.block_table
@@ -484,6 +492,21 @@ def kernels_only(n: int) -> None:
     for i in range(n):
         pa.attn_decode(q, pool, tables[i % 8], c.layer, lens, c.n_kv_heads, d.scale, d.max_ctx,
                        slot_ids=sid, workspace=ws)
+    del pool
+    # the long decode (4 x 16384): the whole-page kernel and its merge kernel
+    d = W.long_decode()
+    c = d.cache
+    pool = device_pool(c)
+    tables = [i32(t) for t in decode_replicas(d, 4)]
+    for bt in tables:
+        for tok in (d.context, d.new_tokens):
+            pa.kv_scatter(tok.k.to(DEV), tok.v.to(DEV), i32(tok.slot_ids), i32(tok.positions), pool,
+                          bt, c.layer)
+    q, lens, sid = d.q.to(DEV), i32(d.ctx_lens), i32(d.slot_ids)
+    ws = pa.decode_workspace(d.B, d.Hq, c.n_kv_heads, d.d, d.max_ctx, DEV)
+    for i in range(n):
+        pa.attn_decode(q, pool, tables[i % 4], c.layer, lens, c.n_kv_heads, d.scale, d.max_ctx,
+                       slot_ids=sid, workspace=ws)
     torch.cuda.synchronize()
     print(f"kernels-only: {n} launches each", flush=True)
 
@@ -553,11 +576,11 @@ def sweep(parts=SWEEP_PARTS) -> None:
         del ql, kl, vl
 
     if "long_decode" in parts:
-        # long decode, 2 page-disjoint replicas cycled
+        # long decode, 4 page-disjoint replicas cycled (537 MB, past the 256 MB MALL)
         dcase = W.long_decode()
         c = dcase.cache
         pool = device_pool(c)
-        tables = [i32(tb) for tb in decode_replicas(dcase, 2)]
+        tables = [i32(tb) for tb in decode_replicas(dcase, 4)]
         for tb in tables:
             for tok in (dcase.context, dcase.new_tokens):
                 pa.kv_scatter(tok.k.to(DEV), tok.v.to(DEV), i32(tok.slot_ids), i32(tok.positions), pool, tb,
@@ -568,9 +591,8 @@ def sweep(parts=SWEEP_PARTS) -> None:
                                                 dcase.max_ctx, slot_ids=sid, workspace=ws) for tb in tables],
                         reps=4) / len(tables)
         kvb = int(dcase.ctx_lens.sum()) * c.n_kv_heads * dcase.d * 2 * 2
-        n_splits = pa.decode_splits(dcase.B, dcase.Hq, c.n_kv_heads, dcase.d, dcase.max_ctx)
         emit("long decode 4 x 16384 (32/8/64, paged)", t * 1e6, kvb / t / 1e9, "GB/s",
-             f"{n_splits} workgroup splits per context (+ combine kernel)")
+             decode_path_note(dcase.B, dcase.Hq, c.n_kv_heads, dcase.d, dcase.max_ctx))
 
     if "decode_d128" in parts:
         # the decode batch with head_dim 128: 64 sequences, ctx ~ U[1, 2048], 32/8 heads,
@@ -616,14 +638,18 @@ def sweep(parts=SWEEP_PARTS) -> None:
         del pool
 
     if "decode_batch" in parts:
-        # larger decode batches of the same mix: 256 and 512 sequences, ctx ~ U[1, 2048],
+        # other decode batches of the same mix: 16 to 512 sequences, ctx ~ U[1, 2048],
         # 32/8/64, an 8 GiB pool, 4 page-disjoint replicas cycled
-        for Bd in (256, 512):
+        for Bd in (16, 32, 48, 80, 96, 128, 256, 512):
             dcase = W.make_decode(f"decode_b{Bd}", B=Bd, Hq=32, Hkv=8, d=64, n_pages=4 * W.POOL_PAGES,
                                   seed=Bd, scale=1.0 / 8.0, mbps=128)
             c = dcase.cache
             pool = device_pool(c)
-            tables = [i32(tb) for tb in decode_replicas(dcase, 4)]
+            # enough page-disjoint replicas that the cycled K/V (>= 600 MB) is not
+            # served from the 256 MB MALL
+            kvb1 = int(dcase.ctx_lens.sum()) * c.n_kv_heads * dcase.d * 2 * 2
+            n_rep = max(4, -(-600_000_000 // kvb1))
+            tables = [i32(tb) for tb in decode_replicas(dcase, n_rep)]
             for tb in tables:
                 for tok in (dcase.context, dcase.new_tokens):
                     pa.kv_scatter(tok.k.to(DEV), tok.v.to(DEV), i32(tok.slot_ids), i32(tok.positions), pool,
@@ -635,7 +661,8 @@ def sweep(parts=SWEEP_PARTS) -> None:
                                      for tb in tables], reps=4) / len(tables)
             kvb = int(dcase.ctx_lens.sum()) * c.n_kv_heads * dcase.d * 2 * 2
             emit(f"decode B={Bd}, ctx ~ U[1, 2048] (32/8/64, paged)", t * 1e6, kvb / t / 1e9, "GB/s",
-                 f"{int(dcase.ctx_lens.sum())} context tokens, {100 * kvb / t / 1e9 / PEAK_HBM_GBS:.1f}% of HBM")
+                 f"{int(dcase.ctx_lens.sum())} context tokens, {100 * kvb / t / 1e9 / PEAK_HBM_GBS:.1f}% of HBM; "
+                 + decode_path_note(Bd, 32, 8, 64, dcase.max_ctx))
             del pool, tables
 
     if "chunk" in parts:

@@ -260,10 +260,15 @@ int attn_prefill_packed(const void *q, const void *kv_cache, int64_t n_pages,
 /*
  * attn_decode -- attention of one new query per sequence over its whole cached
  * context, the newest token included (page 6, sections "pagedAttentionKernel"
- * and "logical block -> physical block -> byte address").  Long contexts are
- * split across workgroups and merged with the log-sum-exp rule of the online
- * softmax (page 3, "causalMask and online softmax": two partial results are
- * rescaled to the larger maximum and added).
+ * and "logical block -> physical block -> byte address").  Contexts are cut
+ * into pieces across workgroups where needed and the pieces merged with the
+ * log-sum-exp rule of the online softmax (page 3, "causalMask and online
+ * softmax": two partial results are rescaled to the larger maximum and
+ * added).  Two kernels serve it: for 8 kv heads of head_dim 64 (groups up to
+ * 8, up to 512 sequences; see attn_decode_whole_pages) each workgroup streams
+ * whole pages, all kv heads, of an equal share of the batch's pages and a
+ * second small kernel merges the pieces; otherwise a workgroup per (sequence,
+ * kv head) reads that head's slice of each page.
  *
  *   q            [B][Hq][head_dim] bf16, the query of the token at ctx_len-1.
  *   ctx_lens     [B] int32, tokens cached for each sequence including the
@@ -272,10 +277,9 @@ int attn_prefill_packed(const void *q, const void *kv_cache, int64_t n_pages,
  *                a larger ctx_lens[b] sets PA_DEVERR_BAD_POS and is cut to max_ctx.
  *   workspace    device scratch of attn_decode_workspace_size(B, Hq, Hkv,
  *                head_dim, max_ctx) bytes, 16-byte aligned, for the partial
- *                results when contexts are split across workgroups (few long
- *                sequences); the size is 0 (workspace may be NULL) when they
- *                are not.  Contents on entry do not matter; two calls in
- *                flight must not share it.
+ *                results of context pieces; the size is 0 (workspace may be
+ *                NULL) when no context is cut.  Contents on entry do not
+ *                matter; two calls in flight must not share it.
  *   O            [B][Hq][head_dim] bf16 output;  LSE [B][Hq] fp32 output.
  *   Other arguments as for attn_prefill.  Supported: head_dim 64 or 128,
  *   Hq/Hkv in {1, 2, 4, 8, 16}.
@@ -317,6 +321,16 @@ int attn_decode_append(const void *q, const void *k_new, const void *v_new, void
 
 /* Workspace bytes attn_decode needs for this batch shape (0 on bad sizes). */
 size_t attn_decode_workspace_size(int B, int Hq, int Hkv, int head_dim, int max_ctx);
+
+/*
+ * 1 when attn_decode (and attn_decode_noalloc) take the whole-page kernel for
+ * this shape on the current device, 0 when they take the per-head kernel
+ * (attn_decode_append always does).  Whole pages: head_dim 64, Hkv 8, Hq/Hkv
+ * up to 8, 1 <= B <= 512, except B * Hkv between one and two times the CU
+ * count (there the per-head kernel's schedule measured faster).  No device
+ * work; 0 on bad sizes.
+ */
+int attn_decode_whole_pages(int B, int Hq, int Hkv, int head_dim);
 
 /*
  * attn_decode_noalloc -- attn_decode for callers that cannot allocate device

@@ -74,6 +74,8 @@ def load():
                                             _F, _I, _P, _P, _P, _P]
         lib.attn_decode_workspace_size.restype = _SZ
         lib.attn_decode_workspace_size.argtypes = [_I, _I, _I, _I, _I]
+        lib.attn_decode_whole_pages.restype = _I
+        lib.attn_decode_whole_pages.argtypes = [_I, _I, _I, _I]
         lib.kv_append.restype = _I
         lib.kv_append.argtypes = [_P, _P, _P, _P, _I, _I, _P, _P, _P, _P, _I, _P, _I64, _P, _I, _I,
                                   _I, _I, _P, _I, _P, _I, _I, _P, _P]
@@ -284,10 +286,17 @@ def decode_workspace_size(B: int, Hq: int, Hkv: int, head_dim: int, max_ctx: int
     return int(load().attn_decode_workspace_size(B, Hq, Hkv, head_dim, max_ctx))
 
 
+def decode_whole_pages(B: int, Hq: int, Hkv: int, head_dim: int) -> bool:
+    """Whether attn_decode (and attn_decode_noalloc) take the whole-page kernel
+    for this shape on the current device (the library's own rule)."""
+    return bool(load().attn_decode_whole_pages(B, Hq, Hkv, head_dim))
+
+
 def decode_splits(B: int, Hq: int, Hkv: int, head_dim: int, max_ctx: int) -> int:
-    """Workgroup splits per context that attn_decode uses for this shape (1: no
-    workspace).  Read off the workspace size, whose fp32 partial outputs
-    [B, Hq, splits, head_dim] dominate it."""
+    """Workgroup splits per context of the per-head decode kernel for this
+    shape (1: no workspace).  Read off the workspace size, whose fp32 partial
+    outputs [B, Hq, splits, head_dim] dominate it.  Meaningless where
+    decode_whole_pages() holds."""
     ws = decode_workspace_size(B, Hq, Hkv, head_dim, max_ctx)
     return 1 if ws == 0 else ws // (B * Hq * head_dim * 4)
 

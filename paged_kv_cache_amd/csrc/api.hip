@@ -213,6 +213,10 @@ int attn_prefill_packed(const void *q, const void *kv_cache, int64_t n_pages,
                                    n_part_slots, O, LSE, err, static_cast<hipStream_t>(stream));
 }
 
+int attn_decode_whole_pages(int B, int Hq, int Hkv, int head_dim) {
+  return pa::rows_path(B, Hq, Hkv, head_dim, false) ? 1 : 0;
+}
+
 size_t attn_decode_workspace_size(int B, int Hq, int Hkv, int head_dim, int max_ctx) {
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || head_dim <= 0 || max_ctx < 0) return 0;
   return pa::decode_workspace_bytes(B, Hq, Hkv, head_dim, max_ctx);

@@ -45,6 +45,7 @@
 // of workgroups takes the r-th longest context, so the longest work starts
 // first and the CUs finish together (contexts differ by up to 2048x).
 
+#include <algorithm>
 #include <mutex>
 #include <type_traits>
 
@@ -91,6 +92,7 @@ struct DecodeArgs {
   int n_xsplits;                // workgroup splits per (sequence, kv head)
   float *ws_o;                  // [B][Hq][n_xsplits][D] normalised partials (n_xsplits > 1)
   float *ws_lse;                // [B][Hq][n_xsplits] partial LSE, natural log
+  int32_t *ws_seg;              // whole-page path: [B][2] first partial slot, partial count
   uint16_t *out;                // [B][Hq][D]
   float *lse;                   // [B][Hq]
   int32_t *err;
@@ -575,6 +577,429 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(DecodeArgs a, int Hq
   if (lane == 0) a.lse[bh] = L > 0.f ? M + fast_log2(L) * kLn2 : -INFINITY;
 }
 
+
+// ---- whole-page decode: 8 kv heads, head_dim 64, head groups up to 8 ------
+//
+// A token row of a page holds every kv head ([token][kv head][d], tiny-vllm
+// part 6, "block contents"), 1 KB here.  Reading one head's 128-byte slice
+// of each row, as decode_kernel does, HBM delivers far less than for whole
+// rows (loads alone, the 64-sequence batch on MI355X: about 4.7 TB/s for the
+// slices against 6.6 TB/s for whole rows).  So here a workgroup streams whole
+// pages (K and V of every head, 32 KB) into LDS and each of its 8 wavefronts
+// computes one kv head from them: S^T = K Q^T and O^T += V^T P^T on 16x16
+// MFMAs with the G query heads of the group in the columns, as in
+// decode_kernel, and the same online softmax.
+//
+// Work split: the pages of all sequences, in batch order, form one list;
+// workgroup g takes pages [g*total/n_wg, (g+1)*total/n_wg), one workgroup per
+// CU, so every CU streams the same bytes (to a page) in one round and no
+// ordering by length is needed.  Every (sequence, workgroup) piece leaves
+// its partial (normalised O, LSE) in workspace slot b + g, and a second
+// kernel merges each sequence's slots by the log-sum-exp rule (tiny-vllm part
+// 3, "causalMask and online softmax": partials rescaled to the larger
+// maximum and added).
+//
+// Ring: NS stages of [K rows 16 x 1 KB][V rows 16 x 1 KB][Q, G KB], filled by
+// direct global->LDS transfers NS-1 pages ahead; wave w transfers rows
+// 4w..4w+3 of the 32 K/V rows on every step (also past the end, from a safe
+// page), and Q row w % G of the page's sequence with the first page of each
+// sequence piece only (every workgroup of a long context re-reading the same
+// 4 KB of Q with each page concentrates its L2 lines).  The wait for a page
+// then counts the transfers of the newer page in flight: 4, or 5 when that
+// page carries Q.  Chunks of 16 bytes are XOR-swizzled per
+// row so that the operand reads are free of bank conflicts: K chunk c of row
+// t sits at c ^ (t & 15) (a K read, 16 rows of one chunk, hits the 16 chunks
+// of one 256-byte group), V chunk c at c ^ 2(t & 7) (a transposing read, 8
+// rows of one chunk pair per half wave, hits 8 distinct pairs).  A wave's
+// logical chunks map to physical chunks no other wave reads, so a wave may
+// zero its own V rows of tokens that must not count.
+constexpr int kRowsMaxB = 512;
+constexpr int kRowsList = 1024;   // pages of a workgroup's range resolved up front
+#ifndef PA_ROWS_WGPC
+#define PA_ROWS_WGPC 1
+#endif
+// workgroups per CU of the whole-page path (2 needs a 2-stage ring, groups up to 4)
+template <int G>
+constexpr int rows_wgpc() { return G <= 4 ? PA_ROWS_WGPC : 1; }
+
+template <int G>
+__global__ __launch_bounds__(512, rows_wgpc<G>()) void decode_rows_kernel(DecodeArgs a, int n_wg) {
+  constexpr int D = 64, HKV = 8, ROW = HKV * D * 2;   // bytes of one token row
+  constexpr int QB = G * ROW;                          // Q of one sequence (Hq x D bf16)
+  constexpr int STAGE = 32 * ROW + QB;
+  constexpr int NS = rows_wgpc<G>() == 2 ? 2 : G <= 4 ? 4 : 3;   // LDS: NS x (32 + G) KB
+  constexpr int PAGE = 2 * kPageTokens * ROW;          // 32 KB
+  constexpr int VOFF = PAGE / 2;
+  static_assert(G >= 1 && G <= 8, "head group");
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[NS * STAGE];
+  __shared__ int s_ctx[kRowsMaxB], s_start[kRowsMaxB], s_slot[kRowsMaxB];
+  __shared__ int s_wsum[8];
+  __shared__ int s_first;
+  // physical page of each of the first kRowsList pages of the range (-1:
+  // missing), resolved in one parallel pass before the ring starts: a
+  // block-table read per page on the ring's path would stall the transfers
+  // behind it on every scalar-cache miss
+  __shared__ int s_page[kRowsList];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = uniform(tid >> 6);     // wavefront = kv head
+  const int lrow = lane & 15;
+  const int lgrp = lane >> 4;
+  const int g = blockIdx.x;
+  const int B = a.B;
+  const int Hq = HKV * G;
+  int err_bits = 0;
+
+  // ---- lengths (cut as decode_kernel cuts them), slots, page counts and
+  // their prefix sum over the batch
+  int np = 0, seq_err = 0;
+  if (tid < B) {
+    int ctx = a.ctx_lens[tid];
+    const int slot = a.slot_ids ? a.slot_ids[tid] : tid;
+    const bool slot_ok = slot >= 0 && slot < a.n_slots;
+    if (!slot_ok) {
+      seq_err |= PA_DEVERR_BAD_SLOT;
+      ctx = 0;
+    }
+    if (ctx < 0 || ctx > a.max_ctx || ctx > a.mbps * kPageTokens) {
+      seq_err |= PA_DEVERR_BAD_POS;
+      ctx = ctx < 0 ? 0 : min(min(ctx, a.max_ctx), a.mbps * kPageTokens);
+    }
+    s_ctx[tid] = ctx;
+    s_slot[tid] = slot_ok ? slot : 0;
+    np = (ctx + kPageTokens - 1) / kPageTokens;
+  }
+  int incl = np;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(incl, o);
+    if (lane >= o) incl += y;
+  }
+  if (lane == 63) s_wsum[w] = incl;
+  __syncthreads();
+  int before = 0, total = 0;
+#pragma unroll
+  for (int v = 0; v < 8; ++v) {
+    const int x = s_wsum[v];
+    before += v < w ? x : 0;
+    total += x;
+  }
+  total = uniform(total);
+  // workgroup g < n_eff = min(n_wg, total) takes pages [g*total/n_eff,
+  // (g+1)*total/n_eff): floor or ceil of total/n_eff pages, at least one, so
+  // the workgroups holding a sequence's pages are consecutive and each holds
+  // some; page j is workgroup owner(j)'s; workgroups past n_eff have none
+  const int n_eff = max(1, min(n_wg, total));
+  auto first_of = [&](int gg) { return (int)(((int64_t)min(gg, n_eff) * total) / n_eff); };
+  auto owner = [&](int j) { return (int)((((int64_t)j + 1) * n_eff - 1) / total); };
+  const int lo = uniform(first_of(g));
+  const int n_my = uniform(first_of(g + 1) - lo);
+  if (tid < B) {
+    const int start = before + incl - np;
+    s_start[tid] = start;
+    // the workgroup holding a sequence's first page reports its length and
+    // slot errors and writes where its partials are (the first workgroup
+    // does so for sequences without pages)
+    const int gf = np > 0 ? owner(start) : 0;
+    if (gf == g) {
+      const int gl = np > 0 ? owner(start + np - 1) : -1;
+      a.ws_seg[2 * tid] = tid + gf;
+      a.ws_seg[2 * tid + 1] = gl - gf + 1;
+      if (seq_err) raise_err(a.err, seq_err);
+    }
+    if (np > 0 && start <= lo && lo < start + np) s_first = tid;
+  }
+  __syncthreads();
+  // the range's pages: sequence by binary search over the starts, then the
+  // table entry, all threads' loads in flight together
+  for (int i = tid; i < min(n_my, kRowsList); i += 512) {
+    const int j = lo + i;
+    int lo_b = 0, hi_b = B - 1;   // last sequence with start <= j and pages
+    while (lo_b < hi_b) {
+      const int mid = (lo_b + hi_b + 1) >> 1;
+      if (s_start[mid] <= j) lo_b = mid; else hi_b = mid - 1;
+    }
+    // sequences without pages share the start of the next: step back to the
+    // one that holds page j
+    while (lo_b > 0 && s_ctx[lo_b] == 0) --lo_b;
+    const int k = j - s_start[lo_b];
+    const int32_t e = a.block_table[((int64_t)s_slot[lo_b] * a.n_layers + a.layer) * a.mbps + k];
+    s_page[i] = (e >= 0 && (int64_t)e < a.n_pages) ? e : -1;
+  }
+  __syncthreads();
+
+  const_i32_ptr table = as_const(a.block_table);
+  auto page_entry = [&](int b, int k) -> int32_t {
+    const int slot = uniform(s_slot[b]);
+    return table[((int64_t)slot * a.n_layers + a.layer) * a.mbps + k];
+  };
+  auto pages_of = [&](int b) { return (uniform(s_ctx[b]) + kPageTokens - 1) / kPageTokens; };
+  // next page of the list after (b, k); b == B past the last sequence
+  auto advance = [&](int &b, int &k) {
+    if (++k < pages_of(b)) return;
+    k = 0;
+    do {
+      ++b;
+    } while (b < B && pages_of(b) == 0);
+  };
+
+  // physical page u of the range, -1 when missing
+  auto page_at = [&](int u, int b, int k) -> int32_t {
+    if (u < kRowsList) return uniform(s_page[u]);
+    const int32_t e = page_entry(b, k);
+    return (e >= 0 && (int64_t)e < a.n_pages) ? e : -1;
+  };
+
+  // ---- transfers of page u of the range (sequence b, block k; and, with_q,
+  // the sequence's Q) into a stage
+  auto fetch = [&](int u, int b, int k, bool real, bool with_q, int stage) {
+    uint8_t *st = ring + stage * STAGE;
+    int64_t page = 0;   // a missing page, or a step past the end: pool page 0 (masked)
+    int qs = 0;
+    if (real) {
+      const int32_t e = page_at(u, b, k);
+      if (e >= 0) page = e;
+      qs = b;
+    }
+    const uint8_t *pbase = a.pool + page * PAGE;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t32 = 4 * w + r;       // K rows 0..15, then V rows 0..15
+      const int t = t32 & 15;
+      const bool isv = t32 >= 16;      // wave-uniform
+      const int chunk = isv ? (lane ^ ((t & 7) << 1)) : (lane ^ (t & 15));
+      dma16(pbase, (uint32_t)((isv ? VOFF : 0) + t * ROW + chunk * 16), st + t32 * ROW);
+    }
+    if (with_q) {
+      const uint8_t *qbase = reinterpret_cast<const uint8_t *>(a.q) + (int64_t)qs * QB;
+      dma16(qbase, (uint32_t)((w % G) * ROW + lane * 16), st + 32 * ROW + (w % G) * ROW);
+    }
+  };
+
+  f32x4 acc[D / 16];
+  bf16x8 qf[2];
+  float m_run = kMaxFloor;
+  float l_lane = 0.f;
+  const float c = a.scale_log2;
+  int cur_b = -1;
+
+  // partial of the current sequence piece into slot cur_b + g
+  auto flush = [&]() {
+    const float l_tot = rows_sum(l_lane);
+    if (lrow < G) {
+      const int hq = w * G + lrow;
+      const int64_t sidx = (int64_t)(cur_b + g) * Hq + hq;
+      const bool empty = !(l_tot > 0.f);
+      const float inv = empty ? 0.f : 1.f / l_tot;
+      float *op = a.ws_o + sidx * D;
+#pragma unroll
+      for (int mb = 0; mb < D / 16; ++mb) {
+        f32x4 v;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = acc[mb][i] * inv;
+        *reinterpret_cast<f32x4 *>(op + 16 * mb + 4 * lgrp) = v;
+      }
+      if (lgrp == 0) a.ws_lse[sidx] = empty ? -INFINITY : (m_run + fast_log2(l_tot)) * kLn2;
+    }
+  };
+
+  auto compute = [&](int u, int b, int k, int stage) {
+    const uint8_t *st = ring + stage * STAGE;
+    if (b != cur_b) {
+      cur_b = b;
+      const uint8_t *qp = st + 32 * ROW + (w * G + lrow % G) * (D * 2) + lgrp * 16;
+      qf[0] = *reinterpret_cast<const bf16x8 *>(qp);
+      qf[1] = *reinterpret_cast<const bf16x8 *>(qp + 64);
+      m_run = kMaxFloor;
+      l_lane = 0.f;
+#pragma unroll
+      for (int mb = 0; mb < D / 16; ++mb) acc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    const int ctx = uniform(s_ctx[b]);
+    const bool ok = page_at(u, b, k) >= 0;
+    if (!ok) err_bits |= PA_DEVERR_BAD_PAGE;
+    const int nv = ok ? min(kPageTokens, ctx - kPageTokens * k) : 0;   // tokens that count
+    // S^T = K Q^T: lane holds tokens 4*lgrp + i of column lrow
+    f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const int chunk = (8 * w + 4 * p + lgrp) ^ lrow;
+      s = mfma16(*reinterpret_cast<const bf16x8 *>(st + lrow * ROW + chunk * 16), qf[p], s);
+    }
+    if (nv < kPageTokens) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) s[i] = (4 * lgrp + i) < nv ? s[i] : -INFINITY;
+      // rows of tokens that must not count (past the context, or a missing
+      // page) may hold anything, NaN included: zero this head's V of them
+      for (int j = lane; j < (kPageTokens - nv) * 8; j += 64) {
+        const int t = nv + j / 8;
+        const int chunk = (8 * w + j % 8) ^ ((t & 7) << 1);
+        *reinterpret_cast<u32x4 *>(const_cast<uint8_t *>(st) + VOFF + t * ROW + chunk * 16) =
+            u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+    float cmax = rows_max(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])));
+    const float mt = cmax * c;
+    if (__any(mt > m_run + kRescaleSlack)) {
+      const float m_new = fmaxf(m_run, mt);
+      const float corr = fast_exp2(m_run - m_new);
+      m_run = m_new;
+      l_lane *= corr;
+#pragma unroll
+      for (int mb = 0; mb < D / 16; ++mb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[mb][i] *= corr;
+    }
+    bf16x4 pb4;
+    float psum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float pr = fast_exp2(__builtin_fmaf(s[i], c, -m_run));
+      psum += pr;
+      pb4[i] = (__bf16)pr;
+    }
+    l_lane += psum;
+    // O^T += V^T P^T (16x16x16): lane lrow points at V[4*lgrp + lrow/4][16*mb +
+    // 4*(lrow%4)] and receives V[4*lgrp + k][16*mb + lrow], k = 0..3
+#pragma unroll
+    for (int mb = 0; mb < D / 16; ++mb) {
+      const int t = 4 * lgrp + (lrow >> 2);
+      const int d = 16 * mb + 4 * (lrow & 3);
+      const int chunk = (8 * w + d / 8) ^ ((t & 7) << 1);
+      const uint8_t *src = st + VOFF + t * ROW + chunk * 16 + (d % 8) * 2;
+      const i16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4 *)(src));
+      acc[mb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, __builtin_bit_cast(i16x4, pb4), acc[mb], 0, 0, 0);
+    }
+  };
+
+  if (n_my > 0) {
+    int fb = uniform(s_first), fk = lo - uniform(s_start[fb]);   // fetch cursor
+    int cb = fb, ck = fk;                                         // compute cursor
+    // Q goes with the first page of each sequence piece: the range's first
+    // page and every page that opens a sequence
+    int q_stages = 0;   // bit s: the page in stage s carries Q
+#pragma unroll
+    for (int u = 0; u < NS - 1; ++u) {
+      const bool wq = u < n_my && (u == 0 || fk == 0);
+      q_stages |= wq ? 1 << u : 0;
+      fetch(u, fb, fk, u < n_my, wq, u);
+      if (u < n_my) advance(fb, fk);
+    }
+    for (int u = 0; u < n_my; ++u) {
+      // this wave's transfers of page u have landed once only those of the
+      // NS-2 newer pages are left (4 each, 5 with Q); after the barrier every
+      // wave's have, and every wave is done with page u-1, whose stage the
+      // next fetch refills
+      int nq = 0;
+#pragma unroll
+      for (int j = 1; j <= NS - 2; ++j) nq += (q_stages >> ((u + j) % NS)) & 1;
+      if constexpr (NS == 2) {
+        wait_vm_lgkm0<0>();
+      } else if constexpr (NS == 3) {
+        if (nq) wait_vm_lgkm0<5>(); else wait_vm_lgkm0<4>();
+      } else {
+        if (nq == 2) wait_vm_lgkm0<10>(); else if (nq == 1) wait_vm_lgkm0<9>(); else wait_vm_lgkm0<8>();
+      }
+      __builtin_amdgcn_s_barrier();
+      // a piece that ends here is written before the next transfers are
+      // issued, so the wait above never has to wait for them
+      if (cur_b >= 0 && cb != cur_b) flush();
+      const int uf = u + NS - 1;
+      const bool wq = uf < n_my && fk == 0;
+      q_stages = (q_stages & ~(1 << (uf % NS))) | (wq ? 1 << (uf % NS) : 0);
+      fetch(uf, fb, fk, uf < n_my, wq, uf % NS);
+      if (uf < n_my) advance(fb, fk);
+      compute(u, cb, ck, u % NS);
+      advance(cb, ck);
+    }
+    if (cur_b >= 0) flush();
+    // no transfer may still be writing LDS when the workgroup ends
+    wait_vm_lgkm0<0>();
+  }
+  if (err_bits && lane == 0) raise_err(a.err, err_bits);
+}
+
+// Merge the partials of a sequence: O = sum_i w_i O_i / sum_i w_i, w_i =
+// exp(LSE_i - max LSE), LSE = max + ln(sum_i w_i) per q head; no partial (an
+// empty context): O = 0, LSE = -inf.  One workgroup per (sequence, 8 q heads):
+// thread t owns 8 dimensions of one head (lanes 8h..8h+7 of each wave) and
+// the partials i = t/64 mod 4, eight at a time with all their loads issued
+// together, merged online (rescaled to the larger maximum); the four groups
+// are merged through LDS.
+__global__ __launch_bounds__(256) void decode_rows_combine_kernel(DecodeArgs a, int Hq) {
+  constexpr int D = 64, NB = 8;
+  __shared__ float s_m[4][64], s_l[4][64];
+  __shared__ f32x4 s_o[4][64][2];
+  const int hgroups = Hq / 8;
+  const int b = blockIdx.x / hgroups;
+  const int tid = threadIdx.x, lane = tid & 63, grp = tid >> 6;
+  const int hq = (blockIdx.x % hgroups) * 8 + lane / 8;
+  const int d0 = (lane % 8) * 8;
+  const int s0 = a.ws_seg[2 * b], n = a.ws_seg[2 * b + 1];
+  float M = -INFINITY, L = 0.f;
+  f32x4 o0 = {0.f, 0.f, 0.f, 0.f}, o1 = {0.f, 0.f, 0.f, 0.f};
+  for (int i0 = grp; i0 < n; i0 += 4 * NB) {
+    float x[NB];
+    f32x4 y0[NB], y1[NB];
+#pragma unroll
+    for (int k = 0; k < NB; ++k) {
+      const int i = i0 + 4 * k;
+      const int64_t sidx = (int64_t)(s0 + min(i, n - 1)) * Hq + hq;
+      x[k] = a.ws_lse[sidx];
+      const f32x4 *op = reinterpret_cast<const f32x4 *>(a.ws_o + sidx * D + d0);
+      y0[k] = op[0];
+      y1[k] = op[1];
+    }
+    float mb = M;
+#pragma unroll
+    for (int k = 0; k < NB; ++k)
+      if (i0 + 4 * k < n) mb = fmaxf(mb, x[k]);
+    if (mb != -INFINITY) {
+      const float corr = fast_exp2((M - mb) * kLog2e);   // M = -inf: 0
+      L *= corr;
+      o0 *= corr;
+      o1 *= corr;
+#pragma unroll
+      for (int k = 0; k < NB; ++k) {
+        const float wgt = i0 + 4 * k < n ? fast_exp2((x[k] - mb) * kLog2e) : 0.f;
+        L += wgt;
+        o0 += wgt * y0[k];
+        o1 += wgt * y1[k];
+      }
+      M = mb;
+    }
+  }
+  s_m[grp][lane] = M;
+  s_l[grp][lane] = L;
+  s_o[grp][lane][0] = o0;
+  s_o[grp][lane][1] = o1;
+  __syncthreads();
+  if (grp == 0) {
+    const float Mt = fmaxf(fmaxf(s_m[0][lane], s_m[1][lane]), fmaxf(s_m[2][lane], s_m[3][lane]));
+    float Lt = 0.f;
+    f32x4 t0 = {0.f, 0.f, 0.f, 0.f}, t1 = {0.f, 0.f, 0.f, 0.f};
+    if (Mt != -INFINITY) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float wgt = fast_exp2((s_m[j][lane] - Mt) * kLog2e);
+        Lt += wgt * s_l[j][lane];
+        t0 += wgt * s_o[j][lane][0];
+        t1 += wgt * s_o[j][lane][1];
+      }
+    }
+    const float inv = Lt > 0.f ? 1.f / Lt : 0.f;
+    uint16_t *out = a.out + ((int64_t)b * Hq + hq) * D + d0;
+    u32x4 pk;
+    pk[0] = pack_bf16x2(t0[0] * inv, t0[1] * inv);
+    pk[1] = pack_bf16x2(t0[2] * inv, t0[3] * inv);
+    pk[2] = pack_bf16x2(t1[0] * inv, t1[1] * inv);
+    pk[3] = pack_bf16x2(t1[2] * inv, t1[3] * inv);
+    *reinterpret_cast<u32x4 *>(out) = pk;
+    if (d0 == 0) a.lse[(int64_t)b * Hq + hq] = Lt > 0.f ? Mt + fast_log2(Lt) * kLn2 : -INFINITY;
+  }
+}
+
 namespace {
 struct Split {
   int tokens, n;                // tokens per workgroup split, splits per context
@@ -606,9 +1031,50 @@ Split split_policy(int B, int Hq, int Hkv, int D, int max_ctx) {
 }
 }  // namespace
 
+// The whole-page path: 8 kv heads of head_dim 64, head groups up to 8, up to
+// kRowsMaxB sequences (its length scan holds one sequence per thread), not
+// the appending variant; except where the batch makes one to two (sequence,
+// kv head) units per CU, where decode_kernel's two rounds, longest context
+// first, pair the units of a CU well and measured faster on MI355X (64
+// sequences, ctx ~ U[1, 2048], 32/8/64: 36.1 against 37.3-37.7 us; at 16,
+// 32, 128, 256 sequences and 4 x 16384 the whole-page path is 2-14% faster).
+bool rows_path(int B, int Hq, int Hkv, int D, bool append) {
+#ifdef PA_ROWS_DISABLE
+  return false;
+#endif
+  if (append || D != 64 || Hkv != 8 || Hq % Hkv != 0 || Hq / Hkv > 8 || B < 1 || B > kRowsMaxB) return false;
+  const int64_t units = (int64_t)B * Hkv, n_cu = device_cu_count();
+  return !(units > n_cu && units <= 2 * n_cu);
+}
+
+// Workgroups of the whole-page path: one per CU, fewer when the batch cannot
+// have that many pages.
+int rows_groups(int B, int G, int max_ctx) {
+  const int64_t pages = (int64_t)B * ((max_ctx + kPageTokens - 1) / kPageTokens);
+  const int wgpc = G <= 4 ? PA_ROWS_WGPC : 1;
+  const int64_t n = std::min<int64_t>((int64_t)wgpc * device_cu_count(), pages);
+  return (int)std::max<int64_t>(1, n);
+}
+
+namespace {
+struct RowsWs {
+  int64_t o_bytes, lse_bytes, seg_bytes;   // partials [slot][Hq][64], LSE [slot][Hq], [B][2]
+};
+RowsWs rows_ws(int B, int Hq, int n_wg) {
+  auto up = [](int64_t x) { return (x + 255) / 256 * 256; };
+  const int64_t slots = (int64_t)n_wg + B;   // slot b + g, g < n_wg
+  return RowsWs{up(slots * Hq * 64 * 4), up(slots * Hq * 4), up((int64_t)B * 2 * 4)};
+}
+}  // namespace
+
 size_t decode_workspace_bytes(int B, int Hq, int Hkv, int D, int max_ctx) {
   const Split s = split_policy(B, Hq, Hkv, D, max_ctx);
-  return (size_t)(s.o_bytes + s.lse_bytes);
+  int64_t need = s.o_bytes + s.lse_bytes;   // decode_kernel (also attn_decode_append's)
+  if (rows_path(B, Hq, Hkv, D, false)) {
+    const RowsWs r = rows_ws(B, Hq, rows_groups(B, Hq / Hkv, max_ctx));
+    need = std::max<int64_t>(need, r.o_bytes + r.lse_bytes + r.seg_bytes);
+  }
+  return (size_t)need;
 }
 
 // ---- the workspace of attn_decode_noalloc: a static device array, one copy
@@ -653,6 +1119,16 @@ static int launch_decode_t(DecodeArgs a, int B, hipStream_t stream) {
   return PA_OK;
 }
 
+template <int G>
+static int launch_decode_rows(DecodeArgs a, int B, int max_ctx, hipStream_t stream) {
+  const int n_wg = rows_groups(B, G, max_ctx);
+  hipLaunchKernelGGL((decode_rows_kernel<G>), dim3((unsigned)n_wg), dim3(512), 0, stream, a, n_wg);
+  if (hipGetLastError() != hipSuccess) return PA_ERR_LAUNCH;
+  hipLaunchKernelGGL(decode_rows_combine_kernel, dim3((unsigned)(B * G)), dim3(256), 0, stream, a, 8 * G);
+  if (hipGetLastError() != hipSuccess) return PA_ERR_LAUNCH;
+  return PA_OK;
+}
+
 int launch_decode(const void *q, const void *kv_cache, int64_t n_pages, const int32_t *block_table,
                   int n_slots, int n_layers, int mbps, int layer, const int32_t *slot_ids,
                   const int32_t *ctx_lens, int B, int Hq, int Hkv, int D, float scale, int max_ctx,
@@ -686,6 +1162,16 @@ int launch_decode(const void *q, const void *kv_cache, int64_t n_pages, const in
   a.v_new = static_cast<const uint16_t *>(v_new);
   a.pool_w = k_new ? static_cast<uint8_t *>(const_cast<void *>(kv_cache)) : nullptr;
   const int G = Hq / Hkv;
+  if (rows_path(B, Hq, Hkv, D, k_new != nullptr)) {
+    const RowsWs r = rows_ws(B, Hq, rows_groups(B, G, max_ctx));
+    a.ws_o = reinterpret_cast<float *>(ws);
+    a.ws_lse = reinterpret_cast<float *>(ws + r.o_bytes);
+    a.ws_seg = reinterpret_cast<int32_t *>(ws + r.o_bytes + r.lse_bytes);
+    if (G == 1) return launch_decode_rows<1>(a, B, max_ctx, stream);
+    if (G == 2) return launch_decode_rows<2>(a, B, max_ctx, stream);
+    if (G == 4) return launch_decode_rows<4>(a, B, max_ctx, stream);
+    if (G == 8) return launch_decode_rows<8>(a, B, max_ctx, stream);
+  }
 #define PA_DECODE_CASE(DD, GG) \
   if (D == DD && G == GG) return launch_decode_t<DD, GG>(a, B, stream);
   PA_DECODE_CASE(64, 1)

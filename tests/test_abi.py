@@ -22,7 +22,7 @@ def declared_functions():
 def test_header_declares_the_path():
     names = declared_functions()
     for n in ["kv_scatter", "attn_prefill", "attn_decode", "attn_prefill_dense",
-              "attn_decode_workspace_size", "pa_status_string", "pa_page_bytes", "kv_append",
+              "attn_decode_workspace_size", "attn_decode_whole_pages", "pa_status_string", "pa_page_bytes", "kv_append",
               "kv_release", "attn_prefill_chunk", "attn_backward_dense",
               "attn_backward_workspace_size"]:
         assert n in names
@@ -44,24 +44,48 @@ def test_page_bytes_and_status_strings():
 
 
 def test_decode_workspace_size():
-    # a batch that fills the GPU needs no cross-workgroup partials
-    assert pa.decode_workspace_size(64, 32, 8, 64, 2048) == 0
-    # a few long contexts are split across workgroups: O and LSE partials
-    assert pa.decode_workspace_size(4, 32, 8, 64, 16384) >= 4 * 32 * 2 * (64 + 1) * 4
+    # head_dim 128 (per-head kernel): a batch that fills the GPU needs no
+    # cross-workgroup partials; a few long contexts are split across
+    # workgroups (O and LSE partials)
+    assert pa.decode_workspace_size(64, 32, 8, 128, 2048) == 0
+    assert pa.decode_workspace_size(4, 32, 8, 128, 16384) >= 4 * 32 * 2 * (128 + 1) * 4
     assert pa.decode_workspace_size(0, 32, 8, 64, 2048) == 0
-    assert pa.decode_splits(64, 32, 8, 64, 2048) == 1
-    assert pa.decode_splits(4, 32, 8, 64, 16384) >= 2
+    assert pa.decode_splits(64, 32, 8, 128, 2048) == 1
+    assert pa.decode_splits(4, 32, 8, 128, 16384) >= 2
+
+
+def test_decode_whole_page_workspace():
+    # 8 kv heads of head_dim 64 (group <= 8, B <= 512): one workgroup per CU
+    # (256 here, also the count assumed without a device), a partial per
+    # (sequence, workgroup) in slot b + g < 256 + B, plus [B][2] slot ranges
+    for B, Hq, max_ctx in ((4, 32, 16384), (32, 32, 2048), (128, 32, 2048), (512, 32, 2048), (3, 8, 100)):
+        assert pa.decode_whole_pages(B, Hq, 8, 64)
+        n_wg = min(256, B * ((max_ctx + 15) // 16))
+        assert pa.decode_workspace_size(B, Hq, 8, 64, max_ctx) >= (n_wg + B) * Hq * (64 + 1) * 4 + B * 8
+    # a short batch uses fewer workgroups than CUs: 3 sequences of up to 100
+    # tokens have at most 21 pages
+    assert pa.decode_workspace_size(3, 8, 8, 64, 100) < (256 + 3) * 8 * 65 * 4
+    # one to two (sequence, kv head) units per CU: the per-head kernel
+    assert not pa.decode_whole_pages(33, 32, 8, 64)
+    assert not pa.decode_whole_pages(64, 32, 8, 64)
+    assert pa.decode_whole_pages(65, 32, 8, 64)
+    assert not pa.decode_whole_pages(513, 32, 8, 64)       # the length scan holds 512
+    assert not pa.decode_whole_pages(16, 128, 8, 64)       # group 16
+    assert not pa.decode_whole_pages(16, 32, 8, 128)
+    assert not pa.decode_whole_pages(16, 16, 4, 64)
+    assert not pa.decode_whole_pages(0, 32, 8, 64)
 
 
 def test_decode_split_policy_one_workgroup_per_cu():
-    # splits give every CU (256 on this part, also the count assumed without a
-    # device) one workgroup: B * Hkv * splits = 256, never below 2 chunks of 32
-    # tokens per wavefront (512 tokens per split)
-    assert pa.decode_splits(4, 32, 8, 64, 16384) == 8      # 32 groups x 8
-    assert pa.decode_splits(16, 32, 8, 64, 2048) == 2      # 128 groups x 2
-    assert pa.decode_splits(1, 32, 8, 64, 3000) == 6       # 32 wanted, 3000 / 512 allowed
-    assert pa.decode_splits(1, 32, 8, 64, 100) == 1
-    assert pa.decode_splits(32, 32, 8, 64, 2048) == 1      # 256 groups already
+    # per-head kernel (here head_dim 128): splits give every CU (256 on this
+    # part, also the count assumed without a device) one workgroup: B * Hkv *
+    # splits = 256, never below 2 chunks of 32 tokens per wavefront (512 tokens
+    # per split)
+    assert pa.decode_splits(4, 32, 8, 128, 16384) == 8      # 32 groups x 8
+    assert pa.decode_splits(16, 32, 8, 128, 2048) == 2      # 128 groups x 2
+    assert pa.decode_splits(1, 32, 8, 128, 3000) == 6       # 32 wanted, 3000 / 512 allowed
+    assert pa.decode_splits(1, 32, 8, 128, 100) == 1
+    assert pa.decode_splits(32, 32, 8, 128, 2048) == 1      # 256 groups already
 
 
 P = ctypes.c_void_p
