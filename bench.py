@@ -191,7 +191,7 @@ def source_digest(*names: str) -> str:
 TRAFFIC = {
     # kernel: (source digest, fetched bytes, written bytes)
     "prefill": ("f6b15280df2341e4", 25386829, 17301504),
-    "decode": ("776cf067f4ba0de7", 152914968, 272864),
+    "decode": ("1e9fd69626998028", 152918124, 272691),
 }
 
 
