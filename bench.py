@@ -191,7 +191,7 @@ def source_digest(*names: str) -> str:
 TRAFFIC = {
     # kernel: (source digest, fetched bytes, written bytes)
     "prefill": ("f6b15280df2341e4", 25386829, 17301504),
-    "decode": ("1e9fd69626998028", 152918124, 272691),
+    "decode": ("8d098f650bae1593", 152917154, 272998),
 }
 
 
@@ -274,7 +274,7 @@ def sustained_clock() -> float:
 
 def decode_path_note(B: int, Hq: int, Hkv: int, d: int, max_ctx: int) -> str:
     """Which attn_decode kernel serves this shape, for the sweep's notes."""
-    if pa.decode_whole_pages(B, Hq, Hkv, d):
+    if pa.decode_whole_pages(B, Hq, Hkv, d, max_ctx):
         return "whole-page kernel (one workgroup per CU, equal page shares) + merge kernel"
     n = pa.decode_splits(B, Hq, Hkv, d, max_ctx)
     return "per-head kernel" + (f", {n} workgroup splits per context + combine kernel" if n > 1 else "")

@@ -326,11 +326,11 @@ size_t attn_decode_workspace_size(int B, int Hq, int Hkv, int head_dim, int max_
  * 1 when attn_decode (and attn_decode_noalloc) take the whole-page kernel for
  * this shape on the current device, 0 when they take the per-head kernel
  * (attn_decode_append always does).  Whole pages: head_dim 64, Hkv 8, Hq/Hkv
- * up to 8, 1 <= B <= 512, except B * Hkv between one and two times the CU
- * count (there the per-head kernel's schedule measured faster).  No device
- * work; 0 on bad sizes.
+ * up to 8, 1 <= B <= 512, B * ceil(max_ctx / 16) pages at most 1024 per CU,
+ * except B * Hkv between one and two times the CU count (there the per-head
+ * kernel's schedule measured faster).  No device work; 0 on bad sizes.
  */
-int attn_decode_whole_pages(int B, int Hq, int Hkv, int head_dim);
+int attn_decode_whole_pages(int B, int Hq, int Hkv, int head_dim, int max_ctx);
 
 /*
  * attn_decode_noalloc -- attn_decode for callers that cannot allocate device

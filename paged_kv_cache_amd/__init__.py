@@ -75,7 +75,7 @@ def load():
         lib.attn_decode_workspace_size.restype = _SZ
         lib.attn_decode_workspace_size.argtypes = [_I, _I, _I, _I, _I]
         lib.attn_decode_whole_pages.restype = _I
-        lib.attn_decode_whole_pages.argtypes = [_I, _I, _I, _I]
+        lib.attn_decode_whole_pages.argtypes = [_I, _I, _I, _I, _I]
         lib.kv_append.restype = _I
         lib.kv_append.argtypes = [_P, _P, _P, _P, _I, _I, _P, _P, _P, _P, _I, _P, _I64, _P, _I, _I,
                                   _I, _I, _P, _I, _P, _I, _I, _P, _P]
@@ -286,10 +286,10 @@ def decode_workspace_size(B: int, Hq: int, Hkv: int, head_dim: int, max_ctx: int
     return int(load().attn_decode_workspace_size(B, Hq, Hkv, head_dim, max_ctx))
 
 
-def decode_whole_pages(B: int, Hq: int, Hkv: int, head_dim: int) -> bool:
+def decode_whole_pages(B: int, Hq: int, Hkv: int, head_dim: int, max_ctx: int = 2048) -> bool:
     """Whether attn_decode (and attn_decode_noalloc) take the whole-page kernel
     for this shape on the current device (the library's own rule)."""
-    return bool(load().attn_decode_whole_pages(B, Hq, Hkv, head_dim))
+    return bool(load().attn_decode_whole_pages(B, Hq, Hkv, head_dim, max_ctx))
 
 
 def decode_splits(B: int, Hq: int, Hkv: int, head_dim: int, max_ctx: int) -> int:

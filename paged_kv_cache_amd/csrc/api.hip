@@ -213,8 +213,8 @@ int attn_prefill_packed(const void *q, const void *kv_cache, int64_t n_pages,
                                    n_part_slots, O, LSE, err, static_cast<hipStream_t>(stream));
 }
 
-int attn_decode_whole_pages(int B, int Hq, int Hkv, int head_dim) {
-  return pa::rows_path(B, Hq, Hkv, head_dim, false) ? 1 : 0;
+int attn_decode_whole_pages(int B, int Hq, int Hkv, int head_dim, int max_ctx) {
+  return pa::rows_path(B, Hq, Hkv, head_dim, max_ctx, false) ? 1 : 0;
 }
 
 size_t attn_decode_workspace_size(int B, int Hq, int Hkv, int head_dim, int max_ctx) {

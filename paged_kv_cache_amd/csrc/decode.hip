@@ -635,10 +635,10 @@ __global__ __launch_bounds__(512, rows_wgpc<G>()) void decode_rows_kernel(Decode
   __shared__ int s_ctx[kRowsMaxB], s_start[kRowsMaxB], s_slot[kRowsMaxB];
   __shared__ int s_wsum[8];
   __shared__ int s_first;
-  // physical page of each of the first kRowsList pages of the range (-1:
-  // missing), resolved in one parallel pass before the ring starts: a
-  // block-table read per page on the ring's path would stall the transfers
-  // behind it on every scalar-cache miss
+  // physical page of each page of the range (-1: missing; the host sends only
+  // batches whose ranges fit), resolved in one parallel pass before the ring
+  // starts: a block-table read per page on the ring's path would stall the
+  // transfers behind it on every scalar-cache miss
   __shared__ int s_page[kRowsList];
 
   const int tid = threadIdx.x;
@@ -729,11 +729,6 @@ __global__ __launch_bounds__(512, rows_wgpc<G>()) void decode_rows_kernel(Decode
   }
   __syncthreads();
 
-  const_i32_ptr table = as_const(a.block_table);
-  auto page_entry = [&](int b, int k) -> int32_t {
-    const int slot = uniform(s_slot[b]);
-    return table[((int64_t)slot * a.n_layers + a.layer) * a.mbps + k];
-  };
   auto pages_of = [&](int b) { return (uniform(s_ctx[b]) + kPageTokens - 1) / kPageTokens; };
   // next page of the list after (b, k); b == B past the last sequence
   auto advance = [&](int &b, int &k) {
@@ -745,11 +740,7 @@ __global__ __launch_bounds__(512, rows_wgpc<G>()) void decode_rows_kernel(Decode
   };
 
   // physical page u of the range, -1 when missing
-  auto page_at = [&](int u, int b, int k) -> int32_t {
-    if (u < kRowsList) return uniform(s_page[u]);
-    const int32_t e = page_entry(b, k);
-    return (e >= 0 && (int64_t)e < a.n_pages) ? e : -1;
-  };
+  auto page_at = [&](int u) -> int32_t { return uniform(s_page[u]); };
 
   // ---- transfers of page u of the range (sequence b, block k; and, with_q,
   // the sequence's Q) into a stage
@@ -758,7 +749,7 @@ __global__ __launch_bounds__(512, rows_wgpc<G>()) void decode_rows_kernel(Decode
     int64_t page = 0;   // a missing page, or a step past the end: pool page 0 (masked)
     int qs = 0;
     if (real) {
-      const int32_t e = page_at(u, b, k);
+      const int32_t e = page_at(u);
       if (e >= 0) page = e;
       qs = b;
     }
@@ -817,7 +808,7 @@ __global__ __launch_bounds__(512, rows_wgpc<G>()) void decode_rows_kernel(Decode
       for (int mb = 0; mb < D / 16; ++mb) acc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
     const int ctx = uniform(s_ctx[b]);
-    const bool ok = page_at(u, b, k) >= 0;
+    const bool ok = page_at(u) >= 0;
     if (!ok) err_bits |= PA_DEVERR_BAD_PAGE;
     const int nv = ok ? min(kPageTokens, ctx - kPageTokens * k) : 0;   // tokens that count
     // S^T = K Q^T: lane holds tokens 4*lgrp + i of column lrow
@@ -1038,17 +1029,20 @@ Split split_policy(int B, int Hq, int Hkv, int D, int max_ctx) {
 // first, pair the units of a CU well and measured faster on MI355X (64
 // sequences, ctx ~ U[1, 2048], 32/8/64: 36.1 against 37.3-37.7 us; at 16,
 // 32, 128, 256 sequences and 4 x 16384 the whole-page path is 2-14% faster).
-bool rows_path(int B, int Hq, int Hkv, int D, bool append) {
+bool rows_path(int B, int Hq, int Hkv, int D, int max_ctx, bool append) {
 #ifdef PA_ROWS_DISABLE
   return false;
 #endif
   if (append || D != 64 || Hkv != 8 || Hq % Hkv != 0 || Hq / Hkv > 8 || B < 1 || B > kRowsMaxB) return false;
   const int64_t units = (int64_t)B * Hkv, n_cu = device_cu_count();
+  // every workgroup's range fits the page list it resolves up front
+  const int64_t pages = (int64_t)B * ((std::max(max_ctx, 0) + kPageTokens - 1) / kPageTokens);
+  if (pages > (int64_t)kRowsList * n_cu) return false;
   return !(units > n_cu && units <= 2 * n_cu);
 }
 
 // Workgroups of the whole-page path: one per CU, fewer when the batch cannot
-// have that many pages.
+// have that many pages (so no range exceeds kRowsList pages: rows_path).
 int rows_groups(int B, int G, int max_ctx) {
   const int64_t pages = (int64_t)B * ((max_ctx + kPageTokens - 1) / kPageTokens);
   const int wgpc = G <= 4 ? PA_ROWS_WGPC : 1;
@@ -1070,7 +1064,7 @@ RowsWs rows_ws(int B, int Hq, int n_wg) {
 size_t decode_workspace_bytes(int B, int Hq, int Hkv, int D, int max_ctx) {
   const Split s = split_policy(B, Hq, Hkv, D, max_ctx);
   int64_t need = s.o_bytes + s.lse_bytes;   // decode_kernel (also attn_decode_append's)
-  if (rows_path(B, Hq, Hkv, D, false)) {
+  if (rows_path(B, Hq, Hkv, D, max_ctx, false)) {
     const RowsWs r = rows_ws(B, Hq, rows_groups(B, Hq / Hkv, max_ctx));
     need = std::max<int64_t>(need, r.o_bytes + r.lse_bytes + r.seg_bytes);
   }
@@ -1162,7 +1156,7 @@ int launch_decode(const void *q, const void *kv_cache, int64_t n_pages, const in
   a.v_new = static_cast<const uint16_t *>(v_new);
   a.pool_w = k_new ? static_cast<uint8_t *>(const_cast<void *>(kv_cache)) : nullptr;
   const int G = Hq / Hkv;
-  if (rows_path(B, Hq, Hkv, D, k_new != nullptr)) {
+  if (rows_path(B, Hq, Hkv, D, max_ctx, k_new != nullptr)) {
     const RowsWs r = rows_ws(B, Hq, rows_groups(B, G, max_ctx));
     a.ws_o = reinterpret_cast<float *>(ws);
     a.ws_lse = reinterpret_cast<float *>(ws + r.o_bytes);

@@ -47,7 +47,7 @@ int launch_prefill_store(const void *q, const void *k, const void *v, void *kv_c
 
 size_t decode_workspace_bytes(int B, int Hq, int Hkv, int D, int max_ctx);
 // whether attn_decode streams whole pages for this shape (decode_rows_kernel)
-bool rows_path(int B, int Hq, int Hkv, int D, bool append);
+bool rows_path(int B, int Hq, int Hkv, int D, int max_ctx, bool append);
 
 // attn_decode_noalloc's workspace: the capacity of the static device array and
 // the current device's address of it (looked up on the first call on each

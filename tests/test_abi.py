@@ -59,7 +59,7 @@ def test_decode_whole_page_workspace():
     # (256 here, also the count assumed without a device), a partial per
     # (sequence, workgroup) in slot b + g < 256 + B, plus [B][2] slot ranges
     for B, Hq, max_ctx in ((4, 32, 16384), (32, 32, 2048), (128, 32, 2048), (512, 32, 2048), (3, 8, 100)):
-        assert pa.decode_whole_pages(B, Hq, 8, 64)
+        assert pa.decode_whole_pages(B, Hq, 8, 64, max_ctx)
         n_wg = min(256, B * ((max_ctx + 15) // 16))
         assert pa.decode_workspace_size(B, Hq, 8, 64, max_ctx) >= (n_wg + B) * Hq * (64 + 1) * 4 + B * 8
     # a short batch uses fewer workgroups than CUs: 3 sequences of up to 100
@@ -74,6 +74,10 @@ def test_decode_whole_page_workspace():
     assert not pa.decode_whole_pages(16, 32, 8, 128)
     assert not pa.decode_whole_pages(16, 16, 4, 64)
     assert not pa.decode_whole_pages(0, 32, 8, 64)
+    # a workgroup resolves at most 1024 pages of its range up front: batches
+    # of more than 1024 pages per CU take the per-head kernel
+    assert pa.decode_whole_pages(512, 32, 8, 64, 512 * 16)
+    assert not pa.decode_whole_pages(512, 32, 8, 64, 512 * 16 + 16)
 
 
 def test_decode_split_policy_one_workgroup_per_cu():

@@ -187,3 +187,29 @@ def test_decode_workspace_reused_across_shapes():
                               case.scale, max(case.max_ctx, 1), slot_ids=i32(case.slot_ids), workspace=ws)
         Oref, Lref, _ = oracle.decode_case(case)
         assert_attn_close(O, L, Oref, Lref, what=case.name)
+
+
+def test_decode_whole_pages_missing_pages_at_piece_edges():
+    """The whole-page kernel: 5 sequences (1 to 5700 tokens, 805 pages over 256
+    workgroups: pieces of 3 or 4 pages, so most sequences are cut into many
+    pieces) with missing pages at the first page of a sequence, inside a piece,
+    at piece boundaries and on the last, partial page; O and LSE against the
+    oracle, the flag raised, the pieces merged."""
+    ctx = [3000, 17, 4100, 1, 5700]
+    case = W.make_decode("wp_bad", B=5, Hq=32, Hkv=8, d=64, n_pages=1024, ctx_lens=ctx, seed=21, mbps=512)
+    assert pa.decode_whole_pages(5, 32, 8, 64, 5700)
+    Oref0, Lref0, pool_h = oracle.decode_case(case)
+    O, L, pool = run_decode(case)
+    assert_attn_close(O, L, Oref0, Lref0, what="whole pages, all present")
+    bt = case.cache.block_table.copy()
+    for b, blk in ((0, 0), (0, 93), (0, 94), (2, 40), (2, 41), (2, 42), (2, 256), (4, 1), (4, 356)):
+        bt[b, 0, blk] = -1
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    O2, L2 = pa.attn_decode(case.q.to(DEV), pool, i32(bt), 0, i32(case.ctx_lens), 8, case.scale,
+                            5700, slot_ids=i32(case.slot_ids), err=err)
+    Oref, Lref, bad = oracle.attn_decode(case.q, pool_h, 1024, bt, 0, case.slot_ids, case.ctx_lens,
+                                         8, case.scale)
+    assert bad > 0
+    torch.cuda.synchronize()
+    assert int(err.item()) & pa.PA_DEVERR_BAD_PAGE
+    assert_attn_close(O2, L2, Oref, Lref, what="whole pages, missing pages")
